@@ -1,0 +1,117 @@
+"""Oracle: causal attention restricted to selected 64x64 blocks.  TEST INFRASTRUCTURE ONLY.
+
+Source passages:
+* Rebuttal "SeerAttention: Learning Intrinsic Sparse Attention in Your LLMs",
+  "Weakness 5 (Pseudo code of Inference Kernel)": every query block loops over
+  its selected KV blocks only, with K and V of a step taken from the same block
+  index, and an online softmax whose result is acc / l.  The online recurrence
+  is an evaluation order of an ordinary softmax; this oracle writes out that
+  ordinary softmax instead: skipped blocks contribute nothing (logit -inf), and
+  the output is softmax(s) . V over the allowed keys.
+* Reproducibility summary of "SeerAttention: Self-distilled Attention Gating for
+  Efficient Long-context Prefilling", Experiment Setup row: block size 64.
+* Rebuttal, "Weakness 4 (Rounding Issue when Seq not evenly divided by B)": a
+  sequence that is not a multiple of the block is padded; here the last block
+  is simply short (positions >= T do not exist).
+
+Readings (also in the design notes):
+* Causal alignment with Tq = Tk = T: query position r sees key position c iff
+  c <= r and block(c) is in the row's list.
+* Logits are sm_scale * <q_r, k_c>; sm_scale is an argument (1/sqrt(D) by default).
+* GQA (not on the pages): query head h reads KV head h // (Hq / Hkv).
+* List entries outside [0, i] are ignored; the list is read as a set.  A row
+  with no valid entry outputs zeros.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, List, Optional, Tuple
+
+import numpy as np
+
+BLOCK = 64
+
+
+def _f64(x) -> np.ndarray:
+    """Exact widening of the inputs (torch bf16/fp32 tensors or arrays) to float64."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float64)
+
+
+def block_probs(q_rows: np.ndarray, k_keys: np.ndarray, row_pos: np.ndarray,
+                key_pos: np.ndarray, sm_scale: float) -> np.ndarray:
+    """Softmax probabilities of some query rows over some keys, causally masked.
+
+    q_rows [R, D], k_keys [C, D] float64; row_pos [R], key_pos [C] are absolute
+    positions.  Key c is visible to row r iff key_pos[c] <= row_pos[r].  A row
+    that sees no key gets all-zero probabilities.
+    """
+    s = float(sm_scale) * (q_rows @ k_keys.T)
+    visible = key_pos[None, :] <= row_pos[:, None]
+    s = np.where(visible, s, -np.inf)
+    p = np.zeros_like(s)
+    has_key = visible.any(axis=1)
+    if has_key.any():
+        sv = s[has_key]
+        m = sv.max(axis=1, keepdims=True)
+        e = np.exp(sv - m)
+        p[has_key] = e / e.sum(axis=1, keepdims=True)
+    return p
+
+
+def allowed_blocks(idx_row, cnt: int, i: int) -> List[int]:
+    """Valid distinct entries of a row's list: those inside [0, i]."""
+    n = max(0, min(int(cnt), len(idx_row)))
+    return sorted({int(j) for j in idx_row[:n] if 0 <= int(j) <= i})
+
+
+def _key_positions(blocks: List[int], seq: int) -> np.ndarray:
+    if not blocks:
+        return np.zeros((0,), dtype=np.int64)
+    return np.concatenate([np.arange(BLOCK * j, min(BLOCK * j + BLOCK, seq)) for j in blocks])
+
+
+def sparse_attention_blocks_ref(q, k, v, idx, cnt, sm_scale: Optional[float],
+                                blocks: Iterable[Tuple[int, int, int]]
+                                ) -> Dict[Tuple[int, int, int], np.ndarray]:
+    """Output rows of selected query blocks: {(b, h, i): O_i [rows, D] float64}."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    idx = np.asarray(idx)
+    cnt = np.asarray(cnt)
+    bsz, hq, seq, d = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    out = {}
+    for (b, h, i) in blocks:
+        b, h, i = int(b), int(h), int(i)
+        g = h // group
+        r0, r1 = BLOCK * i, min(BLOCK * i + BLOCK, seq)
+        rows = np.arange(r0, r1)
+        sel = allowed_blocks(idx[b, h, i], cnt[b, h, i], i)
+        keys = _key_positions(sel, seq)
+        if keys.size == 0:
+            out[(b, h, i)] = np.zeros((r1 - r0, d))
+            continue
+        p = block_probs(q[b, h, r0:r1], k[b, g, keys], rows, keys, scale)
+        out[(b, h, i)] = p @ v[b, g, keys]
+    return out
+
+
+def sparse_attention_ref(q, k, v, idx, cnt, sm_scale: Optional[float] = None) -> np.ndarray:
+    """Full output O [B,Hq,T,D] float64 of block-sparse causal attention."""
+    qq = _f64(q)
+    bsz, hq, seq, d = qq.shape
+    nqb = (seq + BLOCK - 1) // BLOCK
+    blocks = [(b, h, i) for b in range(bsz) for h in range(hq) for i in range(nqb)]
+    res = sparse_attention_blocks_ref(qq, k, v, idx, cnt, sm_scale, blocks)
+    o = np.zeros((bsz, hq, seq, d))
+    for (b, h, i), oi in res.items():
+        o[b, h, BLOCK * i: BLOCK * i + oi.shape[0]] = oi
+    return o
