@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Throughput of the block-sparse prefill path on one MI355X.
+
+A step is one pass of the whole sparse path over one batch of synthetic input:
+seer_build_mask (TopK on the fp32 block scores) followed by seer_sparse_prefill
+(schedule + block-sparse flash attention), on the 32k-token Llama-3.1-8B
+attention shape at density 0.1 with inputs already resident in HBM.
+
+The headline value is computed-block TFLOP/s: every listed 64x64 tile counts
+4*64*64*D FLOP (a diagonal tile counts whole, since it is computed).  The JSON
+line also carries the roofline of the dominant call, the CPU oracle timed on a
+bounded sample of the same workload, the speedup over the same kernel at
+density 1.0, and the pooled-map pass on the Qwen2.5-32B shape.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PMC_FILE = os.path.join(ROOT, "profiles", "sparse_prefill_kernel_llama8b_t32768_d0.1_pmc.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_attention_prefill_amd", "csrc", "attention.hip")
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def tile_flops(d: int) -> int:
+    return 4 * 64 * 64 * d
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(launch_s: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    if absent or taken on a different kernel source."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    vals = {}
+    with open(PMC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                key, _, val = line.partition(":")
+                vals[key.strip()] = val.strip()
+    if vals.get("kernel_source_sha256_16") != source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_calls(fn, n: int, torch):
+    """Mean duration (ms) of fn() over n calls, bracketed by events on torch's
+    current stream -- the stream the library launches on."""
+    evs = []
+    for _ in range(n):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return statistics.mean(a.elapsed_time(b) for a, b in evs)
+
+
+def cpu_baseline(w, q, k, v, scores, max_k, blocks_per_head: int):
+    import numpy as np
+
+    import oracle
+    from block_sparse_attention_prefill_amd import workloads as wl
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    rows = wl.sample_qblocks(w, blocks_per_head)
+    t0 = time.perf_counter()
+    lists = oracle.mask_rows_ref(scores.numpy(), rows, w.mode, w.threshold, w.density,
+                                 w.keep_sink, max_k)
+    idx = np.full((w.batch, w.hq, w.nqb, max_k), -1, np.int32)
+    cnt = np.zeros((w.batch, w.hq, w.nqb), np.int32)
+    for (b, h, i), sel in lists.items():
+        idx[b, h, i, : len(sel)] = sel
+        cnt[b, h, i] = len(sel)
+    oracle.sparse_attention_blocks_ref(q, k, v, idx, cnt, None, rows)
+    dt = time.perf_counter() - t0
+    flops = int(cnt.sum()) * tile_flops(w.head_dim)
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{len(rows)} seeded query blocks ({blocks_per_head} per head incl. first and "
+                   f"last) of {w.name}: mask rows + fp64 attention, {dt:.1f} s"),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, help="workload id (default 3: 32k, density 0.1)")
+    ap.add_argument("--cpu-blocks-per-head", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the density-1.0 and pooled-map measurements")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by KV head with no exchange; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import block_sparse_attention_prefill_amd as seer
+    from block_sparse_attention_prefill_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    seer.load()
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS[args.workload]
+    assert w.kind == "sparse"
+    log(f"[bench] generating {w.name}")
+    q, k, v = wl.make_qkv(w)
+    scores = wl.make_scores(w)
+    qd, kd, vd, sd = (t.to(dev) for t in (q, k, v, scores))
+    max_k = seer.topk_budget(w.nqb, w.density, w.keep_sink) if w.mode == wl.MODE_TOPK else w.nqb
+    idx = torch.empty((w.batch, w.hq, w.nqb, max_k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((w.batch, w.hq, w.nqb), dtype=torch.int32, device=dev)
+    out = torch.empty_like(qd)
+    ws = torch.empty((seer.sparse_prefill_workspace_size(w.batch, w.hq, w.hkv, w.seq),),
+                     dtype=torch.uint8, device=dev)
+
+    def build_mask():
+        seer.seer_build_mask(sd, w.mode, w.threshold, w.density, w.keep_sink, max_k,
+                             kv_idx=idx, kv_cnt=cnt)
+
+    def prefill():
+        seer.seer_sparse_prefill(qd, kd, vd, idx, cnt, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        build_mask()
+        prefill()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    ev_mask, ev_pre = [], []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        build_mask()
+        e[1].record()
+        prefill()
+        e[2].record()
+        ev_mask.append((e[0], e[1]))
+        ev_pre.append((e[1], e[2]))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    mask_ms = statistics.mean(a.elapsed_time(b) for a, b in ev_mask)
+    pre_ms = statistics.mean(a.elapsed_time(b) for a, b in ev_pre)
+
+    blocks = int(cnt.sum().item())
+    flops = blocks * tile_flops(w.head_dim)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (pre_ms * 1e-3) / 1e12
+    causal_exact = (blocks - w.batch * w.hq * w.nqb * 0.5) * tile_flops(w.head_dim)
+    traffic = read_traffic(pre_ms * 1e-3)
+    algo_bytes = (qd.numel() * 2 * 2 + kd.numel() * 2 * 2 + idx.numel() * 4 + cnt.numel() * 4)
+
+    result = {
+        "metric": "sparse-prefill attention TFLOP/s (computed blocks) & % bf16 MFMA peak, 32k",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, local+stripe block scores)",
+        "config": {
+            "workload": w.name, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
+            "head_dim": w.head_dim, "seq_len": w.seq, "block": 64, "mask": "topk",
+            "density": w.density, "keep_sink": w.keep_sink, "computed_blocks": blocks,
+            "density_eff": round(blocks / (w.batch * w.hq * w.nqb * (w.nqb + 1) / 2), 5),
+        },
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "mask_build_ms": round(mask_ms, 4),
+        "sparse_prefill_ms": round(pre_ms, 4),
+        "causal_exact_tflops": round(causal_exact / (ms_per_step * 1e-3) / 1e12, 3),
+        "roofline": {
+            "kernel": "seer_sparse_prefill (schedule + sparse_prefill_kernel)",
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_hbm_bytes": algo_bytes,
+        },
+    }
+
+    if not args.no_extras:
+        # Same kernel at density 1.0 (every causal block listed).
+        log("[bench] density 1.0 reference")
+        idx1 = torch.empty((w.batch, w.hq, w.nqb, w.nqb), dtype=torch.int32, device=dev)
+        cnt1 = torch.empty((w.batch, w.hq, w.nqb), dtype=torch.int32, device=dev)
+        seer.seer_build_mask(sd, wl.MODE_TOPK, 0.0, 1.0, w.keep_sink, w.nqb, kv_idx=idx1,
+                             kv_cnt=cnt1)
+        seer.seer_sparse_prefill(qd, kd, vd, idx1, cnt1, out=out, workspace=ws)
+        n1 = max(2, args.steps // 5)
+        dense_ms = time_calls(lambda: seer.seer_sparse_prefill(qd, kd, vd, idx1, cnt1, out=out,
+                                                               workspace=ws), n1, torch)
+        blocks1 = int(cnt1.sum().item())
+        result["density1"] = {
+            "prefill_ms": round(dense_ms, 4),
+            "tflops": round(blocks1 * tile_flops(w.head_dim) / (dense_ms * 1e-3) / 1e12, 3),
+            "speedup": round(dense_ms / pre_ms, 3),
+            "ideal_speedup": round(blocks1 / blocks, 3),
+        }
+        del idx1, cnt1
+
+        # Pooled-map pass on the Qwen2.5-32B shape.
+        w5 = wl.C5
+        log(f"[bench] pooled map {w5.name}")
+        q5, k5, v5 = (t.to(dev) for t in wl.make_qkv(w5))
+        o5 = torch.empty_like(q5)
+        a5 = torch.empty((w5.batch, w5.hq, w5.nqb, w5.nqb), dtype=torch.float32, device=dev)
+        ws5 = torch.empty((seer.pooled_attn_map_workspace_size(w5.batch, w5.hq, w5.seq),),
+                          dtype=torch.uint8, device=dev)
+        call = lambda: seer.seer_pooled_attn_map(q5, k5, v5, out=o5, amap=a5, workspace=ws5)
+        call()
+        pm_ms = time_calls(call, max(2, args.steps // 5), torch)
+        tiles = w5.batch * w5.hq * w5.nqb * (w5.nqb + 1) // 2
+        result["pooled_map"] = {
+            "workload": w5.name,
+            "ms": round(pm_ms, 4),
+            "tflops": round(tiles * tile_flops(w5.head_dim) / (pm_ms * 1e-3) / 1e12, 3),
+            "pct_of_bf16_peak": round(100 * tiles * tile_flops(w5.head_dim) / (pm_ms * 1e-3)
+                                      / 1e12 / PEAK_BF16_TFLOPS, 2),
+        }
+        del q5, k5, v5, o5, a5, ws5
+
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, scores, max_k, args.cpu_blocks_per_head)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,196 @@
+"""ctypes binding of libseer.so: the C-ABI of include/seer.h with the same names.
+
+Argument marshalling only -- every step of the path runs in the HIP library.
+Torch tensors provide device memory and the current HIP stream.  If the
+library is missing the calls raise instead of falling back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libseer.so")
+
+SEER_OK = 0
+SEER_MASK_THRESHOLD = 0
+SEER_MASK_TOPK = 1
+BLOCK = 64
+
+EXPORTED = (
+    "seer_status_string", "seer_version", "seer_topk_budget", "seer_build_mask",
+    "seer_sparse_prefill_workspace_size", "seer_sparse_prefill",
+    "seer_pooled_attn_map_workspace_size", "seer_pooled_attn_map",
+)
+
+_lib = None
+
+
+class SeerError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} ({status})")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libseer.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m block_sparse_attention_prefill_amd.build`"
+            " (there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_int, c_float, c_double, c_size, c_void = (ctypes.c_int, ctypes.c_float, ctypes.c_double,
+                                                ctypes.c_size_t, ctypes.c_void_p)
+    lib.seer_status_string.restype = ctypes.c_char_p
+    lib.seer_status_string.argtypes = [c_int]
+    lib.seer_version.restype = c_int
+    lib.seer_version.argtypes = []
+    lib.seer_topk_budget.restype = c_int
+    lib.seer_topk_budget.argtypes = [c_int, c_double, c_int]
+    lib.seer_build_mask.restype = c_int
+    lib.seer_build_mask.argtypes = [c_void, c_int, c_int, c_int, c_int, c_int, c_float, c_double,
+                                    c_int, c_void, c_void, c_int, c_void]
+    lib.seer_sparse_prefill_workspace_size.restype = c_size
+    lib.seer_sparse_prefill_workspace_size.argtypes = [c_int, c_int, c_int, c_int]
+    lib.seer_sparse_prefill.restype = c_int
+    lib.seer_sparse_prefill.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int,
+                                        c_float, c_void, c_void, c_int, c_void, c_void, c_size,
+                                        c_void]
+    lib.seer_pooled_attn_map_workspace_size.restype = c_size
+    lib.seer_pooled_attn_map_workspace_size.argtypes = [c_int, c_int, c_int]
+    lib.seer_pooled_attn_map.restype = c_int
+    lib.seer_pooled_attn_map.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int,
+                                         c_float, c_void, c_void, c_void, c_size, c_void]
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != SEER_OK:
+        raise SeerError(fn, status, load().seer_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ...]) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def version() -> int:
+    return load().seer_version()
+
+
+def topk_budget(nqb: int, density: float, keep_sink: bool) -> int:
+    return load().seer_topk_budget(nqb, float(density), int(bool(keep_sink)))
+
+
+def seer_build_mask(scores: torch.Tensor, mode: int, threshold: float, density: float,
+                    keep_sink: bool, max_k: int, kv_idx: Optional[torch.Tensor] = None,
+                    kv_cnt: Optional[torch.Tensor] = None, stream=None):
+    """scores fp32 [B,H,nQB,nKB] -> (kv_idx int32 [B,H,nQB,max_k], kv_cnt int32 [B,H,nQB])."""
+    lib = load()
+    b, h, nqb, nkb = scores.shape
+    _need(scores, "scores", torch.float32, (b, h, nqb, nkb))
+    if kv_idx is None:
+        kv_idx = torch.empty((b, h, nqb, max_k), dtype=torch.int32, device=scores.device)
+    if kv_cnt is None:
+        kv_cnt = torch.empty((b, h, nqb), dtype=torch.int32, device=scores.device)
+    _need(kv_idx, "kv_idx", torch.int32, (b, h, nqb, max_k))
+    _need(kv_cnt, "kv_cnt", torch.int32, (b, h, nqb))
+    _check("seer_build_mask", lib.seer_build_mask(
+        _ptr(scores), b, h, nqb, nkb, int(mode), float(threshold), float(density),
+        int(bool(keep_sink)), _ptr(kv_idx), _ptr(kv_cnt), int(max_k), _stream(stream)))
+    return kv_idx, kv_cnt
+
+
+def sparse_prefill_workspace_size(b: int, hq: int, hkv: int, t: int) -> int:
+    return load().seer_sparse_prefill_workspace_size(b, hq, hkv, t)
+
+
+def pooled_attn_map_workspace_size(b: int, hq: int, t: int) -> int:
+    return load().seer_pooled_attn_map_workspace_size(b, hq, t)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator hands out 512-byte aligned blocks.
+    return torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=device)
+
+
+def _qkv_dims(q, k, v):
+    b, hq, t, d = q.shape
+    hkv = k.shape[1]
+    _need(q, "q", torch.bfloat16, (b, hq, t, d))
+    _need(k, "k", torch.bfloat16, (b, hkv, t, d))
+    _need(v, "v", torch.bfloat16, (b, hkv, t, d))
+    return b, hq, hkv, t, d
+
+
+def seer_sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_idx: torch.Tensor,
+                        kv_cnt: torch.Tensor, sm_scale: Optional[float] = None,
+                        out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Block-sparse causal prefill.  q [B,Hq,T,D], k/v [B,Hkv,T,D] bf16 -> O bf16."""
+    lib = load()
+    b, hq, hkv, t, d = _qkv_dims(q, k, v)
+    nqb = (t + BLOCK - 1) // BLOCK
+    max_k = kv_idx.shape[-1]
+    _need(kv_idx, "kv_idx", torch.int32, (b, hq, nqb, max_k))
+    _need(kv_cnt, "kv_cnt", torch.int32, (b, hq, nqb))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, (b, hq, t, d))
+    need = lib.seer_sparse_prefill_workspace_size(b, hq, hkv, t)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    scale = (1.0 / d ** 0.5) if sm_scale is None else float(sm_scale)
+    _check("seer_sparse_prefill", lib.seer_sparse_prefill(
+        _ptr(q), _ptr(k), _ptr(v), b, hq, hkv, t, d, scale, _ptr(kv_idx), _ptr(kv_cnt),
+        int(max_k), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out
+
+
+def seer_pooled_attn_map(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                         amap: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None):
+    """Dense causal pass -> (O bf16 [B,Hq,T,D], A fp32 [B,Hq,nQB,nQB])."""
+    lib = load()
+    b, hq, hkv, t, d = _qkv_dims(q, k, v)
+    nqb = (t + BLOCK - 1) // BLOCK
+    if out is None:
+        out = torch.empty_like(q)
+    if amap is None:
+        amap = torch.empty((b, hq, nqb, nqb), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16, (b, hq, t, d))
+    _need(amap, "amap", torch.float32, (b, hq, nqb, nqb))
+    need = lib.seer_pooled_attn_map_workspace_size(b, hq, t)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    scale = (1.0 / d ** 0.5) if sm_scale is None else float(sm_scale)
+    _check("seer_pooled_attn_map", lib.seer_pooled_attn_map(
+        _ptr(q), _ptr(k), _ptr(v), b, hq, hkv, t, d, scale, _ptr(out), _ptr(amap),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, amap

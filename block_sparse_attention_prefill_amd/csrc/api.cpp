@@ -1,0 +1,143 @@
+// Host side of the C-ABI declared in include/seer.h: argument checks, workspace
+// layout and kernel launches.  No allocation, no global mutable state.
+#include "seer.h"
+
+#include <math.h>
+#include <limits.h>
+
+#include "seer_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+int nqb_of(int T) { return (T + SEER_BLOCK - 1) / SEER_BLOCK; }
+
+// Sizes must keep every flattened index inside int32 / size_t arithmetic the
+// kernels use: item ids (B*H*nQB) are int, element offsets are size_t.
+bool items_fit(long long B, long long H, long long nqb) {
+  return B >= 0 && H >= 0 && nqb >= 0 && B * H * nqb <= (long long)INT_MAX;
+}
+
+int attention_args(const void* q, const void* k, const void* v, const void* o, int B, int Hq,
+                   int Hkv, int T, int D, float sm_scale) {
+  if (B < 0 || T < 0 || Hq <= 0 || Hkv <= 0) return SEER_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return SEER_ERR_INVALID_ARG;
+  if (!(isfinite(sm_scale) && sm_scale > 0.f)) return SEER_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return SEER_ERR_UNSUPPORTED;
+  if (!items_fit(B, Hq, nqb_of(T))) return SEER_ERR_UNSUPPORTED;
+  if ((long long)B * T == 0) return SEER_OK;
+  if (!q || !k || !v || !o) return SEER_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return SEER_ERR_INVALID_ARG;
+  return SEER_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* seer_status_string(int status) {
+  switch (status) {
+    case SEER_OK: return "SEER_OK";
+    case SEER_ERR_INVALID_ARG: return "SEER_ERR_INVALID_ARG";
+    case SEER_ERR_UNSUPPORTED: return "SEER_ERR_UNSUPPORTED";
+    case SEER_ERR_CAPACITY: return "SEER_ERR_CAPACITY";
+    case SEER_ERR_WORKSPACE: return "SEER_ERR_WORKSPACE";
+    case SEER_ERR_HIP: return "SEER_ERR_HIP";
+    default: return "SEER_ERR_UNKNOWN";
+  }
+}
+
+int seer_version(void) { return kVersion; }
+
+int seer_topk_budget(int nQB, double density, int keep_sink) {
+  if (nQB < 0 || !(density > 0.0 && density <= 1.0)) return -1;
+  if (nQB == 0) return 0;
+  const int i = nQB - 1;
+  const int forced = (i == 0) ? 1 : (keep_sink ? 2 : 1);
+  const double c = ceil(density * (double)(i + 1));
+  int k = (int)c;
+  if (k < forced) k = forced;
+  if (k > i + 1) k = i + 1;
+  return k;
+}
+
+int seer_build_mask(const float* scores, int B, int H, int nQB, int nKB, int mode,
+                    float threshold, double density, int keep_sink, int32_t* kv_idx,
+                    int32_t* kv_cnt, int max_k, void* stream) {
+  if (B < 0 || H < 0 || nQB < 0 || nKB < nQB) return SEER_ERR_INVALID_ARG;
+  if (mode != SEER_MASK_TOPK && mode != SEER_MASK_THRESHOLD) return SEER_ERR_INVALID_ARG;
+  if (!items_fit(B, H, nQB)) return SEER_ERR_UNSUPPORTED;
+  if (mode == SEER_MASK_TOPK && !(density > 0.0 && density <= 1.0)) return SEER_ERR_INVALID_ARG;
+  if (mode == SEER_MASK_THRESHOLD && !isfinite(threshold)) return SEER_ERR_INVALID_ARG;
+  if (max_k < 1) return SEER_ERR_CAPACITY;
+  if ((long long)B * H * nQB == 0) return SEER_OK;
+  if (!scores || !kv_idx || !kv_cnt) return SEER_ERR_INVALID_ARG;
+  if (mode == SEER_MASK_TOPK) {
+    if (max_k < seer_topk_budget(nQB, density, keep_sink)) return SEER_ERR_CAPACITY;
+  } else {
+    const int forced = (keep_sink && nQB > 1) ? 2 : 1;
+    if (max_k < forced) return SEER_ERR_CAPACITY;
+  }
+  const hipError_t err = seer::launch_build_mask(scores, B, H, nQB, nKB, mode, threshold,
+                                                 density, keep_sink ? 1 : 0, kv_idx, kv_cnt,
+                                                 max_k, (hipStream_t)stream);
+  return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
+}
+
+size_t seer_sparse_prefill_workspace_size(int B, int Hq, int Hkv, int T) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || T < 0 || Hq % Hkv != 0) return 0;
+  if (!items_fit(B, Hq, nqb_of(T))) return 0;
+  const size_t entries = seer::schedule_entries(B, Hq, nqb_of(T));
+  return ((entries * sizeof(int32_t) + 255) / 256) * 256 + 256;
+}
+
+int seer_sparse_prefill(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
+                        int T, int D, float sm_scale, const int32_t* kv_idx,
+                        const int32_t* kv_cnt, int max_k, void* o, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const int st = attention_args(q, k, v, o, B, Hq, Hkv, T, D, sm_scale);
+  if (st != SEER_OK) return st;
+  if (max_k < 1) return SEER_ERR_INVALID_ARG;
+  if ((long long)B * T == 0) return SEER_OK;
+  if (!kv_idx || !kv_cnt) return SEER_ERR_INVALID_ARG;
+  const size_t need = seer_sparse_prefill_workspace_size(B, Hq, Hkv, T);
+  if (!workspace || workspace_bytes < need || !aligned256(workspace)) return SEER_ERR_WORKSPACE;
+  const int nqb = nqb_of(T);
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* work = static_cast<int32_t*>(workspace);
+  hipError_t err = seer::launch_schedule(kv_cnt, B, Hq, Hkv, nqb, max_k, work, s);
+  if (err != hipSuccess) return SEER_ERR_HIP;
+  err = seer::launch_sparse_prefill(q, k, v, B, Hq, Hkv, T, D, sm_scale, kv_idx, kv_cnt, max_k,
+                                    work, o, s);
+  return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
+}
+
+size_t seer_pooled_attn_map_workspace_size(int B, int Hq, int T) {
+  if (B < 0 || Hq <= 0 || T < 0) return 0;
+  const int nqb = nqb_of(T);
+  if (!items_fit(B, Hq, nqb)) return 0;
+  const size_t tiles = (size_t)B * Hq * ((size_t)nqb * (nqb + 1) / 2);
+  return tiles * SEER_BLOCK * sizeof(float) + 256;
+}
+
+int seer_pooled_attn_map(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
+                         int T, int D, float sm_scale, void* o, float* amap, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const int st = attention_args(q, k, v, o, B, Hq, Hkv, T, D, sm_scale);
+  if (st != SEER_OK) return st;
+  if ((long long)B * T == 0) return SEER_OK;
+  if (!amap) return SEER_ERR_INVALID_ARG;
+  const size_t need = seer_pooled_attn_map_workspace_size(B, Hq, T);
+  if (!workspace || workspace_bytes < need || !aligned256(workspace)) return SEER_ERR_WORKSPACE;
+  const hipError_t err =
+      seer::launch_pooled_map(q, k, v, B, Hq, Hkv, T, D, sm_scale, o, amap,
+                              static_cast<float*>(workspace), (hipStream_t)stream);
+  return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
+}
+
+}  // extern "C"

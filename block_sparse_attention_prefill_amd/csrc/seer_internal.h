@@ -1,0 +1,40 @@
+// Internal declarations shared by the HIP translation units of libseer.
+// Not part of the public interface (that is include/seer.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace seer {
+
+constexpr int kBlk = 64;  // tokens per query / KV block
+
+// Vector types accepted by the gfx950 MFMA builtins.
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x8 __attribute__((__vector_size__(8 * sizeof(float))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+
+// Work-item order used by the attention kernels (one item = one query block of
+// one head).  Size of the list in int32 entries.
+inline size_t schedule_entries(int B, int Hq, int nqb) { return (size_t)B * Hq * nqb; }
+
+hipError_t launch_build_mask(const float* scores, int B, int H, int nqb, int nkb, int mode,
+                             float threshold, double density, int keep_sink, int32_t* idx,
+                             int32_t* cnt, int max_k, hipStream_t stream);
+
+hipError_t launch_schedule(const int32_t* cnt, int B, int Hq, int Hkv, int nqb, int max_k,
+                           int32_t* work, hipStream_t stream);
+
+hipError_t launch_sparse_prefill(const void* q, const void* k, const void* v, int B, int Hq,
+                                 int Hkv, int T, int D, float sm_scale, const int32_t* idx,
+                                 const int32_t* cnt, int max_k, const int32_t* work, void* o,
+                                 hipStream_t stream);
+
+hipError_t launch_pooled_map(const void* q, const void* k, const void* v, int B, int Hq,
+                             int Hkv, int T, int D, float sm_scale, void* o, float* amap,
+                             float* rowmax_ws, hipStream_t stream);
+
+}  // namespace seer

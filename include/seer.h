@@ -1,0 +1,159 @@
+/*
+ * seer.h -- C-ABI of the MI355X (gfx950) block-sparse attention prefill library.
+ *
+ * The calls follow the statement of the problem in the SeerAttention pages:
+ * soft block scores are turned into per-query-block KV-block lists by
+ * threshold or TopK (model card "SeerAttention-Llama-3.1-8B-AttnGates", method
+ * summary), a block-sparse flash-attention kernel then visits only the listed
+ * KV blocks (rebuttal "SeerAttention: Learning Intrinsic Sparse Attention in
+ * Your LLMs", "Weakness 5 (Pseudo code of Inference Kernel)"), and a dense
+ * flash-attention pass emits the 2D max-pooled attention map used as the gate's
+ * training target (reproducibility summary of "SeerAttention: Self-distilled
+ * Attention Gating for Efficient Long-context Prefilling", Pseudocode row,
+ * Figure 8).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Block size is 64 tokens (same summary, Experiment Setup row).
+ * - Tensors are dense, contiguous, row-major:
+ *     Q, O  : bf16 [B, Hq,  T, D]      K, V : bf16 [B, Hkv, T, D]
+ *   following the [Batch, Head, Seq, Dim] layout the rebuttal uses
+ *   ("Weakness 3 (The meaning of "max and min pooling on K matrix" is not clear)").
+ *   Q, K, V and O must be 16-byte aligned.
+ * - nQB = ceil(T / 64).  T need not be a multiple of 64: the last block is
+ *   short, as if padded (rebuttal, "Weakness 4 (Rounding Issue when Seq not
+ *   evenly divided by B)").
+ * - Attention is causal with Tq = Tk = T: query position r sees key c iff c <= r.
+ * - GQA: query head h reads KV head h / (Hq / Hkv).
+ * - Every pointer argument named "device" is device memory owned by the caller.
+ *   The library never allocates, frees or keeps any buffer, holds no global
+ *   mutable state and may be called from several host threads at once.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Every call only enqueues work on it and returns without synchronising.
+ * - Errors: argument errors are detected on the host before anything is
+ *   enqueued and return a non-zero seer_status_t; nothing is written then.
+ *   A failed kernel launch returns SEER_ERR_HIP.  No C++ exception crosses
+ *   this interface.
+ */
+#ifndef SEER_H_
+#define SEER_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SEER_BLOCK 64
+
+typedef enum {
+  SEER_OK = 0,
+  SEER_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned tensor, bad scalar */
+  SEER_ERR_UNSUPPORTED = 2, /* head dim other than 64 or 128, sizes beyond int range */
+  SEER_ERR_CAPACITY = 3,    /* max_k too small for the TopK budget or the forced blocks */
+  SEER_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the *_workspace_size() */
+  SEER_ERR_HIP = 5          /* the HIP runtime refused a launch */
+} seer_status_t;
+
+typedef enum { SEER_MASK_THRESHOLD = 0, SEER_MASK_TOPK = 1 } seer_mask_mode_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* seer_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int seer_version(void);
+
+/*
+ * Number of KV blocks the TopK rule keeps for the last (largest) query block,
+ * i.e. the smallest max_k seer_build_mask accepts in TopK mode:
+ *   k_i = min(i + 1, max(|F_i|, ceil(density * (i + 1)))) at i = nQB - 1,
+ * with the product and ceiling in IEEE double and F_i the forced blocks
+ * (diagonal, plus block 0 when keep_sink).  TopK is per row (rebuttal,
+ * "Weakness 2 (Memory complexity)") and its size is a user knob ("Weakness 1
+ * (How to choose sparsity?)").  Host only.  Returns -1 for nQB < 0 or a
+ * density outside (0, 1].
+ */
+int seer_topk_budget(int nQB, double density, int keep_sink);
+
+/*
+ * Block-mask construction: soft block scores -> compact per-row KV-block lists.
+ *
+ * scores  device fp32 [B, H, nQB, nKB]; row (b,h,i) reads only entries j <= i.
+ *         nKB >= nQB is the row stride.
+ * mode    SEER_MASK_TOPK: row i keeps its forced blocks plus the best-ranked
+ *         other causal blocks, k_i in total (see seer_topk_budget); `density`
+ *         must lie in (0, 1], `threshold` is ignored.
+ *         SEER_MASK_THRESHOLD: row i keeps its forced blocks plus every other
+ *         causal block whose fp32 score is >= (float)threshold (NaN never
+ *         passes); `threshold` must be finite, `density` is ignored.  When the
+ *         list would exceed max_k it keeps the forced blocks plus the
+ *         best-ranked passing blocks.
+ *         Forced blocks: the diagonal i, plus block 0 if keep_sink != 0.
+ *         Ranking: score descending, ties to the lower block index, NaN lowest.
+ * kv_idx  device int32 out [B, H, nQB, max_k]: row (b,h,i) holds its selected
+ *         blocks in strictly ascending order, then -1 up to max_k.
+ * kv_cnt  device int32 out [B, H, nQB]: list lengths (always <= max_k).
+ * max_k   TopK: >= seer_topk_budget(nQB, density, keep_sink);
+ *         threshold: >= 2 if keep_sink and nQB > 1, else >= 1.
+ *         Otherwise SEER_ERR_CAPACITY.
+ * The result is fully determined by the inputs (bit-reproducible).
+ */
+int seer_build_mask(const float* scores, int B, int H, int nQB, int nKB, int mode,
+                    float threshold, double density, int keep_sink, int32_t* kv_idx,
+                    int32_t* kv_cnt, int max_k, void* stream);
+
+/* Bytes of device workspace seer_sparse_prefill needs (work list of the
+ * load-balancing schedule).  Returns 0 for invalid sizes. */
+size_t seer_sparse_prefill_workspace_size(int B, int Hq, int Hkv, int T);
+
+/*
+ * Block-sparse causal flash-attention prefill (rebuttal, "Weakness 5 (Pseudo
+ * code of Inference Kernel)"): query block i of head h attends only to the KV
+ * blocks listed in kv_idx[b,h,i,0:min(kv_cnt,max_k)]; K and V of a step come
+ * from the same block.  Equivalent to logits sm_scale*<q_r,k_c> set to -inf on
+ * every unlisted block, then softmax and P.V.
+ *
+ * q, k, v  device bf16, layouts above; D in {64, 128}; Hq % Hkv == 0.
+ * sm_scale finite and > 0 (pass 1/sqrt(D) for the usual scaling).
+ * kv_idx   device int32 [B, Hq, nQB, max_k], kv_cnt device int32 [B, Hq, nQB]
+ *          (as written by seer_build_mask).  Entries outside [0, i] are
+ *          skipped, list order does not matter, a list must not repeat a block.
+ *          A row with no valid entry produces O = 0.
+ * o        device bf16 out [B, Hq, T, D], rounded to nearest even.
+ * workspace device, >= seer_sparse_prefill_workspace_size(B, Hq, Hkv, T) bytes,
+ *          256-byte aligned; overwritten.
+ */
+int seer_sparse_prefill(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
+                        int T, int D, float sm_scale, const int32_t* kv_idx,
+                        const int32_t* kv_cnt, int max_k, void* o, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace seer_pooled_attn_map needs: the stored per-row
+ * block maxima r_ij (fp32, 64 per causal (i, j) tile).  0 for invalid sizes. */
+size_t seer_pooled_attn_map_workspace_size(int B, int Hq, int T);
+
+/*
+ * Dense causal flash attention that also emits the 2D max-pooled attention
+ * map (reproducibility summary, Pseudocode row, Figure 8): a first pass stores
+ * the row maxima r_ij of every tile while it accumulates O, m_i and l_i; a
+ * second pass rescales them as exp(r_ij - m_i) / l_i and takes the max over
+ * the tile's rows.
+ *
+ * q, k, v, D, sm_scale as for seer_sparse_prefill.
+ * o     device bf16 out [B, Hq, T, D].
+ * amap  device fp32 out [B, Hq, nQB, nQB]: amap[b,h,i,j] = largest softmax
+ *       probability inside the (i, j) tile for j <= i, 0 for j > i.  Not
+ *       row-normalised.
+ * workspace device, >= seer_pooled_attn_map_workspace_size(B, Hq, T) bytes,
+ *       256-byte aligned; overwritten.
+ */
+int seer_pooled_attn_map(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
+                         int T, int D, float sm_scale, void* o, float* amap, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEER_H_ */

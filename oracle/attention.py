@@ -81,7 +81,6 @@ def sparse_attention_blocks_ref(q, k, v, idx, cnt, sm_scale: Optional[float],
                                 blocks: Iterable[Tuple[int, int, int]]
                                 ) -> Dict[Tuple[int, int, int], np.ndarray]:
     """Output rows of selected query blocks: {(b, h, i): O_i [rows, D] float64}."""
-    q, k, v = _f64(q), _f64(k), _f64(v)
     idx = np.asarray(idx)
     cnt = np.asarray(cnt)
     bsz, hq, seq, d = q.shape
@@ -99,18 +98,17 @@ def sparse_attention_blocks_ref(q, k, v, idx, cnt, sm_scale: Optional[float],
         if keys.size == 0:
             out[(b, h, i)] = np.zeros((r1 - r0, d))
             continue
-        p = block_probs(q[b, h, r0:r1], k[b, g, keys], rows, keys, scale)
-        out[(b, h, i)] = p @ v[b, g, keys]
+        p = block_probs(_f64(q[b, h, r0:r1]), _f64(k[b, g][keys]), rows, keys, scale)
+        out[(b, h, i)] = p @ _f64(v[b, g][keys])
     return out
 
 
 def sparse_attention_ref(q, k, v, idx, cnt, sm_scale: Optional[float] = None) -> np.ndarray:
     """Full output O [B,Hq,T,D] float64 of block-sparse causal attention."""
-    qq = _f64(q)
-    bsz, hq, seq, d = qq.shape
+    bsz, hq, seq, d = q.shape
     nqb = (seq + BLOCK - 1) // BLOCK
     blocks = [(b, h, i) for b in range(bsz) for h in range(hq) for i in range(nqb)]
-    res = sparse_attention_blocks_ref(qq, k, v, idx, cnt, sm_scale, blocks)
+    res = sparse_attention_blocks_ref(q, k, v, idx, cnt, sm_scale, blocks)
     o = np.zeros((bsz, hq, seq, d))
     for (b, h, i), oi in res.items():
         o[b, h, BLOCK * i: BLOCK * i + oi.shape[0]] = oi

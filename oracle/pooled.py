@@ -38,7 +38,6 @@ def pooled_map_blocks_ref(q, k, v, sm_scale: Optional[float],
                           blocks: Iterable[Tuple[int, int, int]]
                           ) -> Dict[Tuple[int, int, int], Tuple[np.ndarray, np.ndarray]]:
     """{(b, h, i): (O_i [rows, D], A_i [nQB])} for selected query blocks."""
-    q, k, v = _f64(q), _f64(k), _f64(v)
     bsz, hq, seq, d = q.shape
     hkv = k.shape[1]
     group = hq // hkv
@@ -51,8 +50,8 @@ def pooled_map_blocks_ref(q, k, v, sm_scale: Optional[float],
         r0, r1 = BLOCK * i, min(BLOCK * i + BLOCK, seq)
         rows = np.arange(r0, r1)
         keys = np.arange(0, r1)
-        p = block_probs(q[b, h, r0:r1], k[b, g, :r1], rows, keys, scale)
-        o = p @ v[b, g, :r1]
+        p = block_probs(_f64(q[b, h, r0:r1]), _f64(k[b, g, :r1]), rows, keys, scale)
+        o = p @ _f64(v[b, g, :r1])
         a = np.zeros((nqb,))
         for j in range(i + 1):
             a[j] = p[:, BLOCK * j: min(BLOCK * j + BLOCK, r1)].max()
@@ -62,11 +61,10 @@ def pooled_map_blocks_ref(q, k, v, sm_scale: Optional[float],
 
 def pooled_map_ref(q, k, v, sm_scale: Optional[float] = None):
     """O [B,Hq,T,D] and A [B,Hq,nQB,nQB] (float64) of the dense causal pass."""
-    qq = _f64(q)
-    bsz, hq, seq, d = qq.shape
+    bsz, hq, seq, d = q.shape
     nqb = (seq + BLOCK - 1) // BLOCK
     blocks = [(b, h, i) for b in range(bsz) for h in range(hq) for i in range(nqb)]
-    res = pooled_map_blocks_ref(qq, k, v, sm_scale, blocks)
+    res = pooled_map_blocks_ref(q, k, v, sm_scale, blocks)
     o = np.zeros((bsz, hq, seq, d))
     a = np.zeros((bsz, hq, nqb, nqb))
     for (b, h, i), (oi, ai) in res.items():

@@ -1,0 +1,112 @@
+"""CPU-side checks of the C-ABI: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_prefill_amd as seer
+from block_sparse_attention_prefill_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "seer.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(seer_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = seer.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_status_strings_and_version():
+    lib = seer.load()
+    assert lib.seer_status_string(0) == b"SEER_OK"
+    assert lib.seer_status_string(3) == b"SEER_ERR_CAPACITY"
+    assert lib.seer_status_string(99) == b"SEER_ERR_UNKNOWN"
+    assert seer.version() >= 100
+
+
+def test_topk_budget_host_helper():
+    assert seer.topk_budget(512, 0.1, True) == 52
+    assert seer.topk_budget(2048, 0.17, True) == 349
+    assert seer.topk_budget(8, 0.5, True) == 4
+    assert seer.topk_budget(1, 0.01, True) == 1
+    assert seer.topk_budget(8, 0.0, True) == -1
+    assert seer.topk_budget(8, 1.5, True) == -1
+
+
+def test_workspace_sizes():
+    assert seer.sparse_prefill_workspace_size(1, 32, 8, 32768) >= 32 * 512 * 4
+    assert seer.sparse_prefill_workspace_size(1, 32, 7, 32768) == 0  # Hq % Hkv != 0
+    # 64 fp32 per causal tile: 40 heads * 512*513/2 tiles at 32k tokens.
+    assert seer.pooled_attn_map_workspace_size(1, 40, 32768) >= 40 * (512 * 513 // 2) * 64 * 4
+    assert seer.pooled_attn_map_workspace_size(1, 0, 64) == 0
+
+
+FAKE = 1 << 20  # never dereferenced: every call below fails its host checks first
+
+
+@pytest.mark.parametrize("args,status", [
+    # mode
+    ((FAKE, 1, 1, 4, 4, 7, 0.0, 0.5, 1, FAKE, FAKE, 4, None), 1),
+    # nKB < nQB
+    ((FAKE, 1, 1, 4, 3, 1, 0.0, 0.5, 1, FAKE, FAKE, 4, None), 1),
+    # density out of range
+    ((FAKE, 1, 1, 4, 4, 1, 0.0, 0.0, 1, FAKE, FAKE, 4, None), 1),
+    # threshold not finite
+    ((FAKE, 1, 1, 4, 4, 0, float("nan"), 0.5, 1, FAKE, FAKE, 4, None), 1),
+    # max_k below the TopK budget (4 blocks at density 1 need 4)
+    ((FAKE, 1, 1, 4, 4, 1, 0.0, 1.0, 1, FAKE, FAKE, 3, None), 3),
+    # max_k cannot hold diagonal + sink
+    ((FAKE, 1, 1, 4, 4, 0, 0.1, 0.5, 1, FAKE, FAKE, 1, None), 3),
+    # null output
+    ((FAKE, 1, 1, 4, 4, 1, 0.0, 0.5, 1, None, FAKE, 4, None), 1),
+])
+def test_build_mask_rejects_on_host(args, status):
+    assert seer.load().seer_build_mask(*args) == status
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, Hq=4, Hkv=2, T=128, D=128, scale=0.1, idx=FAKE,
+             cnt=FAKE, max_k=2, o=FAKE, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return seer.load().seer_sparse_prefill(*a.values())
+
+
+def test_sparse_prefill_rejects_on_host():
+    assert _prefill(D=96) == 2
+    assert _prefill(Hkv=3) == 1
+    assert _prefill(scale=0.0) == 1
+    assert _prefill(scale=float("inf")) == 1
+    assert _prefill(q=None) == 1
+    assert _prefill(q=FAKE + 8) == 1          # misaligned
+    assert _prefill(max_k=0) == 1
+    assert _prefill(ws=None) == 4
+    assert _prefill(wsb=16) == 4
+    assert _prefill(ws=FAKE + 16) == 4        # workspace not 256-byte aligned
+    assert _prefill(T=0) == 0                 # nothing to do, nothing launched
+    assert _prefill(B=0) == 0
+
+
+def test_pooled_map_rejects_on_host():
+    lib = seer.load()
+    ok = (FAKE, FAKE, FAKE, 1, 4, 2, 128, 128, 0.1, FAKE, FAKE, FAKE, 1 << 20, None)
+    bad_d = ok[:7] + (80,) + ok[8:]
+    assert lib.seer_pooled_attn_map(*bad_d) == 2
+    no_map = ok[:10] + (None,) + ok[11:]
+    assert lib.seer_pooled_attn_map(*no_map) == 1
+    small_ws = ok[:12] + (64,) + ok[13:]
+    assert lib.seer_pooled_attn_map(*small_ws) == 4
