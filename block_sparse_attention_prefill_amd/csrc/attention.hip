@@ -24,13 +24,16 @@
 //   Lane l then holds column q = l % 32 and half h = l / 32 of the rows, so a
 //   row max or sum needs one cross-half exchange, and alpha and 1/l are
 //   per-lane scalars.
-// * The K tile sits in LDS row-major with a 16-byte row pad; V is stored
-//   transposed (d-major) with a kv permutation inside each 16-key group that
-//   makes every MFMA A-fragment one 16-byte LDS read and matches the register
-//   order of P^T.  The transpose happens in registers on the way into LDS.
-// * The next KV block's global loads are issued right after the current tile
-//   is in LDS, so they are in flight during the two contractions.
-// * exp2 with log2(e) folded into the softmax scale; fp32 row statistics.
+// * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
+//   register staging), in their natural [key][d] layout with XOR-swizzled
+//   16-byte chunks.  K fragments are plain 16-byte LDS reads; V^T fragments come
+//   from ds_read_b64_tr_b16, which transposes 4x16 bf16 blocks on the fly into
+//   the key order of P^T's registers.
+// * K and V of a tile are separate pipeline stages: K(j+1) streams in during
+//   softmax and PV of tile j, V(j+1) during QK of tile j+1.
+// * exp2 with log2(e) folded into the softmax scale; fp32 row statistics; the
+//   reference max is raised lazily (only when a tile exceeds it by 2^8), which
+//   leaves O = acc / l unchanged and skips most accumulator rescales.
 #include "seer_internal.h"
 
 #include <math.h>
@@ -40,131 +43,119 @@ namespace {
 
 constexpr int kThreads = 128;  // 2 waves
 constexpr int kXcds = 8;       // MI355X: workgroups are dealt round-robin to 8 XCDs
+// The running row max is only raised when a tile's max exceeds it by more than
+// this many powers of two; P values stay <= 2^8 and both O and l use the same
+// reference max, so the result is unchanged while most tiles skip the rescale.
+constexpr float kRescaleSlack = 8.0f;
 
 template <int D>
 struct Cfg {
-  static constexpr int kKPitch = D + 8;            // bf16 per K row in LDS
-  static constexpr int kVPitch = kBlk + 8;         // bf16 per V^T row in LDS
-  static constexpr int kKSteps = D / 16;           // k-steps of the S^T contraction
-  static constexpr int kDTiles = D / 32;           // 32-row tiles of O^T
-  static constexpr int kChunks = D / 8;            // 16-byte chunks per K/V row
-  static constexpr int kKLoads = kBlk * kChunks / kThreads;   // K chunks per thread
-  static constexpr int kVGroups = 16 * kChunks / kThreads;    // (4 rows x 16 B) V groups per thread
-  static constexpr int kLdsElems = kBlk * kKPitch + D * kVPitch;
+  static constexpr int kChunks = D / 8;                  // 16-byte chunks per K/V row
+  static constexpr int kRowsPerLoad = 64 / kChunks;      // rows per 1 KB wave-wide LDS load
+  static constexpr int kLoadsPerTile = kBlk / kRowsPerLoad;
+  static constexpr int kLoadsPerWave = kLoadsPerTile / 2;
+  static constexpr int kTileElems = kBlk * D;
+  static constexpr int kKSteps = D / 16;                 // k-steps of the S^T contraction
+  static constexpr int kDTiles = D / 32;                 // 32-row tiles of O^T
 };
 
-// Position of key kv (0..63) inside a V^T row.  Within each group of 16 keys,
-// key 8b + 4h + c goes to slot 8h + 4b + c, so the 8 keys a lane of half h
-// needs for one PV k-step (its P^T register order) are contiguous.
-__device__ __forceinline__ int vt_pos_of_quad(int kq) {
-  return 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1);
+#define SEER_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  compiler_fence();
 }
 
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
-  return (a & 0xFFFFu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xFFFF0000u);
+__device__ __forceinline__ void wg_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
 }
 
+// Barrier after which a tile may be overwritten: this wave's LDS reads of it
+// have returned (lgkmcnt(0)) before any wave passes.
+__device__ __forceinline__ void wg_barrier_reads_done() {
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));  // lgkmcnt(0), other counters free
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+// XOR swizzles of the 16-byte chunks of a tile row in LDS.  K rows are read 8
+// or 16 at a time at one logical chunk, so row r is rotated by r.  V rows are
+// read by ds_read_b64_tr_b16 four rows at a time over 2 (or 4) adjacent chunks;
+// the per-row masks {0,6,10,12} keep those reads on distinct banks.
 template <int D>
-struct KvStage {
-  uint4 k[Cfg<D>::kKLoads];
-  uint4 v[Cfg<D>::kVGroups][4];
+__device__ __forceinline__ int k_swz(int row) { return row & (Cfg<D>::kChunks - 1); }
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return D == 128 ? ((0xCA60 >> (4 * (row & 3))) & 15) : ((0x4260 >> (4 * (row & 3))) & 7);
+}
 
-  // Global -> registers for KV block starting at row `r0` of this head;
-  // rows >= nvalid (short last block) read as zero.
-  __device__ __forceinline__ void load(const __bf16* __restrict__ kh, const __bf16* __restrict__ vh,
-                                       int r0, int nvalid, int tid) {
-    const uint4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int m = 0; m < Cfg<D>::kKLoads; ++m) {
-      const int c = tid + kThreads * m;
-      const int row = c / Cfg<D>::kChunks;
-      const int col = c % Cfg<D>::kChunks;
-      k[m] = (row < nvalid)
-                 ? *reinterpret_cast<const uint4*>(kh + (size_t)(r0 + row) * D + col * 8)
-                 : zero;
-    }
-#pragma unroll
-    for (int m = 0; m < Cfg<D>::kVGroups; ++m) {
-      const int g = tid + kThreads * m;
-      const int kq = g & 15;
-      const int dc = g >> 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 4 * kq + e;
-        v[m][e] = (row < nvalid)
-                      ? *reinterpret_cast<const uint4*>(vh + (size_t)(r0 + row) * D + dc * 8)
-                      : zero;
-      }
-    }
-  }
+// One wave-wide HBM -> LDS copy: every lane moves 16 bytes from its own global
+// address to lds_base + 16 * lane (global_load_lds_dwordx4; M0 holds the LDS
+// base).  Written as inline asm so that the compiler does not add conservative
+// vmcnt(0) waits in front of unrelated LDS reads; every copy is instead waited
+// for explicitly with wait_vmcnt<> before a barrier, and each one is consumed
+// before the kernel ends.  The instruction writes no VGPR.
+__device__ __forceinline__ void dma16(const void* gaddr, const __bf16* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gaddr), "s"(m0)
+               : "memory");
+}
 
-  // Registers -> LDS: K row-major (padded), V transposed with the key permutation.
-  __device__ __forceinline__ void store(__bf16* ks, __bf16* vt, int tid) const {
+// Issue this wave's half of a 64-row tile load (1 KB per instruction), chunks
+// placed swizzled.  Rows past the end of the sequence re-read the last valid
+// row (those keys are always causally masked), so no LDS slot is left stale.
+template <int D, bool IS_V>
+__device__ __forceinline__ void issue_tile(const __bf16* __restrict__ g, int nvalid, __bf16* tile,
+                                           int wave, int lane) {
+  const int prow = lane / Cfg<D>::kChunks;
+  const int pch = lane % Cfg<D>::kChunks;
 #pragma unroll
-    for (int m = 0; m < Cfg<D>::kKLoads; ++m) {
-      const int c = tid + kThreads * m;
-      const int row = c / Cfg<D>::kChunks;
-      const int col = c % Cfg<D>::kChunks;
-      *reinterpret_cast<uint4*>(ks + row * Cfg<D>::kKPitch + col * 8) = k[m];
-    }
-#pragma unroll
-    for (int m = 0; m < Cfg<D>::kVGroups; ++m) {
-      const int g = tid + kThreads * m;
-      const int kq = g & 15;
-      const int dc = g >> 4;
-      const int pos = vt_pos_of_quad(kq);
-      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&v[m][0]);
-      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&v[m][1]);
-      const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&v[m][2]);
-      const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&v[m][3]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        uint2 out;
-        if (e & 1) {
-          out.x = hi_pair(r0[w], r1[w]);
-          out.y = hi_pair(r2[w], r3[w]);
-        } else {
-          out.x = lo_pair(r0[w], r1[w]);
-          out.y = lo_pair(r2[w], r3[w]);
-        }
-        *reinterpret_cast<uint2*>(vt + (dc * 8 + e) * Cfg<D>::kVPitch + pos) = out;
-      }
-    }
+  for (int n = 0; n < Cfg<D>::kLoadsPerWave; ++n) {
+    const int slab = wave * Cfg<D>::kLoadsPerWave + n;
+    const int row = slab * Cfg<D>::kRowsPerLoad + prow;
+    const int lch = pch ^ (IS_V ? v_swz<D>(row) : k_swz<D>(row));
+    const int grow = row < nvalid ? row : nvalid - 1;
+    dma16(g + (size_t)grow * D + lch * 8, tile + slab * 512);
   }
-};
+}
 
 // Per-wave state of one query block: Q fragments, O^T accumulators, row stats.
 template <int D>
 struct RowState {
   bf16x8 qf[Cfg<D>::kKSteps];
   f32x16 acc[Cfg<D>::kDTiles];
-  float m;  // running max of s * c (log2 domain)
+  float m;  // reference max of s * c (log2 domain)
   float l;  // this lane's partial row sum (its half of the keys)
 };
 
-struct BlockOut {
-  float rowmax_raw;  // max of raw logits of this lane's query row in the tile
-};
-
-// One KV tile: S^T = K Q^T, causal mask on the diagonal tile, online softmax,
-// O^T += V^T P^T.  Returns the raw row max (for the pooled map).
+// S^T = K Q^T for one 64-key tile (two 32-key MFMA tiles), causal mask on the
+// diagonal tile.  Reads the K tile from LDS.
 template <int D>
-__device__ __forceinline__ float attend_tile(RowState<D>& st, const __bf16* ks, const __bf16* vt,
-                                             int lane, int wave, bool diag, float c) {
+__device__ __forceinline__ void qk_tile(const RowState<D>& st, const __bf16* ks, int lane, int wave,
+                                        bool diag, f32x16 (&s)[2]) {
   const int col = lane & 31;
   const int half = lane >> 5;
-  f32x16 s[2];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     f32x16 a = {};
-    const __bf16* krow = ks + (32 * tt + col) * Cfg<D>::kKPitch + 8 * half;
+    const int kv = 32 * tt + col;
+    const __bf16* krow = ks + kv * D;
+    const int sw = k_swz<D>(kv);
 #pragma unroll
     for (int t = 0; t < Cfg<D>::kKSteps; ++t) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 16 * t);
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + (((2 * t + half) ^ sw) * 8));
       a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st.qf[t], a, 0, 0, 0);
     }
     s[tt] = a;
@@ -179,48 +170,78 @@ __device__ __forceinline__ float attend_tile(RowState<D>& st, const __bf16* ks, 
         if (kv > qrow) s[tt][r] = -INFINITY;
       }
   }
-  float mx = s[0][0];
+}
+
+// Online softmax update on S^T (in place -> P), returns the raw row max.
+template <int D>
+__device__ __forceinline__ float softmax_tile(RowState<D>& st, f32x16 (&s)[2], float c) {
+  float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+  for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[0][r], s[0][r + 1]));
 #pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+  for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[1][r], s[1][r + 1]));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
 
-  const float m_new = fmaxf(st.m, mx * c);
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-  st.m = m_new;
+  const float cand = mx * c;
+  const bool raise = cand > st.m + kRescaleSlack;
+  if (__any(raise)) {
+    const float m_new = raise ? cand : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.m = m_new;
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < Cfg<D>::kDTiles; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[dt][r] *= alpha;
+  }
+  const float nm = -st.m;
   float lsum = 0.f;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[tt][r], c, -m_new));
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[tt][r], c, nm));
       s[tt][r] = p;
       lsum += p;
     }
-  st.l = st.l * alpha + lsum;
-#pragma unroll
-  for (int dt = 0; dt < Cfg<D>::kDTiles; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st.acc[dt][r] *= alpha;
+  st.l += lsum;
+  return mx;
+}
 
-  // P^T fragments for the four 16-key steps: regs 8*(kk&1)..+7 of tile kk>>1.
+// O^T += V^T P^T.  The V tile sits in LDS in its natural [key][d] layout;
+// ds_read_b64_tr_b16 hands each lane four consecutive keys of one d, which is
+// exactly the A-fragment order matching P^T's registers.
+template <int D>
+__device__ __forceinline__ void pv_tile(RowState<D>& st, const f32x16 (&s)[2], const __bf16* vs,
+                                        int lane) {
+  const int g = lane >> 4;
+  const int i = lane & 15;
+  const int h = g >> 1;
+  const int r = i >> 2;
+  const int sub = 4 * (i & 1);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const f32x16& src = s[kk >> 1];
     const int o = 8 * (kk & 1);
-    f32x8 pv = {src[o + 0], src[o + 1], src[o + 2], src[o + 3],
-                src[o + 4], src[o + 5], src[o + 6], src[o + 7]};
+    const f32x8 pv = {src[o + 0], src[o + 1], src[o + 2], src[o + 3],
+                      src[o + 4], src[o + 5], src[o + 6], src[o + 7]};
     const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
-    const __bf16* vrow = vt + col * Cfg<D>::kVPitch + 16 * kk + 8 * half;
+    const int kv_a = 16 * kk + 4 * h + r;
+    const int kv_b = kv_a + 8;
 #pragma unroll
     for (int dt = 0; dt < Cfg<D>::kDTiles; ++dt) {
-      const bf16x8 vf =
-          *reinterpret_cast<const bf16x8*>(vrow + 32 * dt * Cfg<D>::kVPitch);
-      st.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, st.acc[dt], 0, 0, 0);
+      const int lc = 4 * dt + 2 * (g & 1) + ((i & 3) >> 1);
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vs + kv_a * D + ((lc ^ v_swz<D>(kv_a)) * 8) + sub));
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vs + kv_b * D + ((lc ^ v_swz<D>(kv_b)) * 8) + sub));
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x8 vv = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+      st.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb,
+                                                           st.acc[dt], 0, 0, 0);
     }
   }
-  return mx;
 }
 
 template <int D>
@@ -264,21 +285,67 @@ __device__ __forceinline__ float store_o(const RowState<D>& st, __bf16* __restri
   return l;
 }
 
+// The KV-block loop shared by both kernels.  Tile j's K and V are loaded in
+// separate stages so that K(j+1) streams in during softmax + PV of tile j and
+// V(j+1) during QK of tile j+1.  `next(e)` returns the next list position and
+// `block(e)` its KV block; `on_tile(j, rowmax)` observes every tile.
+// The query fragments are loaded after the first tile's copies are issued and
+// everything is drained once before the loop, so Q's latency overlaps the first
+// tile's and the loop body never waits on an older load.
+template <int D, typename Next, typename Block, typename OnTile>
+__device__ __forceinline__ void kv_loop(RowState<D>& st, const __bf16* __restrict__ qh, int q0,
+                                        const __bf16* __restrict__ kh,
+                                        const __bf16* __restrict__ vh, int T, int i, int n,
+                                        Next next, Block block, OnTile on_tile, __bf16* ks,
+                                        __bf16* vs, int lane, int wave, float c) {
+  constexpr int NL = Cfg<D>::kLoadsPerWave;
+  int e = next(0);
+  if (e >= n) {
+    load_q<D>(st, qh, q0, T, lane, wave);
+    return;
+  }
+  int j = block(e);
+  issue_tile<D, false>(kh + (size_t)kBlk * j * D, min(kBlk, T - kBlk * j), ks, wave, lane);
+  issue_tile<D, true>(vh + (size_t)kBlk * j * D, min(kBlk, T - kBlk * j), vs, wave, lane);
+  load_q<D>(st, qh, q0, T, lane, wave);
+  wait_vmcnt<0>();
+  while (true) {
+    const int cur = j;
+    e = next(e + 1);
+    const bool more = e < n;
+    if (more) j = block(e);
+
+    wait_vmcnt<NL>();  // K(cur) has landed; V(cur) may still be in flight
+    wg_barrier();
+    f32x16 s[2];
+    qk_tile<D>(st, ks, lane, wave, cur == i, s);
+    wg_barrier_reads_done();  // every wave is done reading K(cur)
+    if (more) issue_tile<D, false>(kh + (size_t)kBlk * j * D, min(kBlk, T - kBlk * j), ks, wave, lane);
+    const float mx = softmax_tile<D>(st, s, c);
+    on_tile(cur, mx);
+    if (more) wait_vmcnt<NL>(); else wait_vmcnt<0>();  // V(cur) has landed
+    wg_barrier();
+    pv_tile<D>(st, s, vs, lane);
+    wg_barrier_reads_done();  // every wave is done reading V(cur)
+    if (!more) break;
+    issue_tile<D, true>(vh + (size_t)kBlk * j * D, min(kBlk, T - kBlk * j), vs, wave, lane);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Sparse prefill: one workgroup per scheduled (b, h, i).
 template <int D>
-__global__ __launch_bounds__(kThreads) void sparse_prefill_kernel(
+__global__ __launch_bounds__(kThreads, 2) void sparse_prefill_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     int Hq, int Hkv, int T, int nqb, float c, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ cnt, int max_k, const int32_t* __restrict__ work,
     __bf16* __restrict__ o) {
-  __shared__ __attribute__((aligned(16))) __bf16 lds[Cfg<D>::kLdsElems];
-  __bf16* ks = lds;
-  __bf16* vt = lds + kBlk * Cfg<D>::kKPitch;
+  __shared__ __attribute__((aligned(1024))) __bf16 ks[Cfg<D>::kTileElems];
+  __shared__ __attribute__((aligned(1024))) __bf16 vs[Cfg<D>::kTileElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int item = work[blockIdx.x];
   const int i = item % nqb;
   const int bh = item / nqb;  // b * Hq + h
@@ -286,16 +353,12 @@ __global__ __launch_bounds__(kThreads) void sparse_prefill_kernel(
   const int b = bh / Hq;
   const int g = h / (Hq / Hkv);
   const size_t kv_off = ((size_t)b * Hkv + g) * (size_t)T * D;
-  const __bf16* kh = k + kv_off;
-  const __bf16* vh = v + kv_off;
   const size_t q_off = (size_t)bh * (size_t)T * D;
 
   RowState<D> st;
-  load_q<D>(st, q + q_off, kBlk * i, T, lane, wave);
-
   const int32_t* lst = idx + (size_t)item * max_k;
   const int n = min(max(cnt[item], 0), max_k);
-  auto next_valid = [&](int e) {
+  auto next = [&](int e) {
     while (e < n) {
       const int j = lst[e];
       if (j >= 0 && j <= i) break;
@@ -303,23 +366,10 @@ __global__ __launch_bounds__(kThreads) void sparse_prefill_kernel(
     }
     return e;
   };
-
-  KvStage<D> stage;
-  int e = next_valid(0);
-  int j = (e < n) ? lst[e] : -1;
-  if (e < n) stage.load(kh, vh, kBlk * j, min(kBlk, T - kBlk * j), tid);
-  while (e < n) {
-    __syncthreads();
-    stage.store(ks, vt, tid);
-    __syncthreads();
-    const int cur = j;
-    e = next_valid(e + 1);
-    if (e < n) {
-      j = lst[e];
-      stage.load(kh, vh, kBlk * j, min(kBlk, T - kBlk * j), tid);
-    }
-    (void)attend_tile<D>(st, ks, vt, lane, wave, cur == i, c);
-  }
+  auto block = [&](int e) { return lst[e]; };
+  auto on_tile = [](int, float) {};
+  kv_loop<D>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, n, next, block, on_tile, ks,
+             vs, lane, wave, c);
   (void)store_o<D>(st, o + q_off, kBlk * i, T, lane, wave);
 }
 
@@ -352,44 +402,36 @@ __device__ __forceinline__ void pooled_item(int L, int B, int Hq, int Hkv, int n
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void pooled_map_kernel(
+__global__ __launch_bounds__(kThreads, 2) void pooled_map_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     int B, int Hq, int Hkv, int T, int nqb, float c, __bf16* __restrict__ o,
     float* __restrict__ amap, float* __restrict__ rws) {
-  __shared__ __attribute__((aligned(16))) __bf16 lds[Cfg<D>::kLdsElems];
+  __shared__ __attribute__((aligned(1024))) __bf16 ks[Cfg<D>::kTileElems];
+  __shared__ __attribute__((aligned(1024))) __bf16 vs[Cfg<D>::kTileElems];
   __shared__ float ms[kBlk];
   __shared__ float ils[kBlk];
-  __bf16* ks = lds;
-  __bf16* vt = lds + kBlk * Cfg<D>::kKPitch;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int b, h, i;
   pooled_item(blockIdx.x, B, Hq, Hkv, nqb, &b, &h, &i);
   const int g = h / (Hq / Hkv);
   const size_t bh = (size_t)b * Hq + h;
   const size_t kv_off = ((size_t)b * Hkv + g) * (size_t)T * D;
-  const __bf16* kh = k + kv_off;
-  const __bf16* vh = v + kv_off;
   const size_t q_off = bh * (size_t)T * D;
   // r_ij of this row block: packed lower triangle, 64 floats per tile.
   const size_t tri = (size_t)nqb * (nqb + 1) / 2;
   float* rrow = rws + (bh * tri + (size_t)i * (i + 1) / 2) * kBlk;
 
   RowState<D> st;
-  load_q<D>(st, q + q_off, kBlk * i, T, lane, wave);
-
-  KvStage<D> stage;
-  stage.load(kh, vh, 0, min(kBlk, T), tid);
-  for (int j = 0; j <= i; ++j) {
-    __syncthreads();
-    stage.store(ks, vt, tid);
-    __syncthreads();
-    if (j < i) stage.load(kh, vh, kBlk * (j + 1), min(kBlk, T - kBlk * (j + 1)), tid);
-    const float mx = attend_tile<D>(st, ks, vt, lane, wave, j == i, c);
+  auto next = [](int e) { return e; };
+  auto block = [](int e) { return e; };
+  auto on_tile = [&](int j, float mx) {
     if (lane < 32) rrow[(size_t)j * kBlk + 32 * wave + lane] = mx;
-  }
+  };
+  kv_loop<D>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, i + 1, next, block, on_tile,
+             ks, vs, lane, wave, c);
   const float l = store_o<D>(st, o + q_off, kBlk * i, T, lane, wave);
   if (lane < 32) {
     const int r = 32 * wave + lane;
