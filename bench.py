@@ -126,7 +126,21 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the density-1.0 and pooled-map measurements")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run one plain device copy of this many MiB (to scale HBM "
+                         "byte counters) and exit")
     args = ap.parse_args(argv)
+
+    if args.copy_calibration_mib:
+        import torch
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -70,6 +70,7 @@ int seer_build_mask(const float* scores, int B, int H, int nQB, int nKB, int mod
                     float threshold, double density, int keep_sink, int32_t* kv_idx,
                     int32_t* kv_cnt, int max_k, void* stream) {
   if (B < 0 || H < 0 || nQB < 0 || nKB < nQB) return SEER_ERR_INVALID_ARG;
+  if (nQB > SEER_MAX_QUERY_BLOCKS) return SEER_ERR_UNSUPPORTED;
   if (mode != SEER_MASK_TOPK && mode != SEER_MASK_THRESHOLD) return SEER_ERR_INVALID_ARG;
   if (!items_fit(B, H, nQB)) return SEER_ERR_UNSUPPORTED;
   if (mode == SEER_MASK_TOPK && !(density > 0.0 && density <= 1.0)) return SEER_ERR_INVALID_ARG;

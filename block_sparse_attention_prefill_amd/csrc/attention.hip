@@ -98,38 +98,79 @@ __device__ __forceinline__ int v_swz(int row) {
   return D == 128 ? ((0xCA60 >> (4 * (row & 3))) & 15) : ((0x4260 >> (4 * (row & 3))) & 7);
 }
 
-// One wave-wide HBM -> LDS copy: every lane moves 16 bytes from its own global
-// address to lds_base + 16 * lane (global_load_lds_dwordx4; M0 holds the LDS
-// base).  Written as inline asm so that the compiler does not add conservative
-// vmcnt(0) waits in front of unrelated LDS reads; every copy is instead waited
-// for explicitly with wait_vmcnt<> before a barrier, and each one is consumed
-// before the kernel ends.  The instruction writes no VGPR.
-__device__ __forceinline__ void dma16(const void* gaddr, const __bf16* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)lds_base));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+// One wave-wide HBM -> LDS copy: every lane moves 16 bytes from sbase + voff
+// (its own byte offset) to lds_base + 16 * lane (global_load_lds_dwordx4 in
+// its SGPR-base form; M0 holds the LDS base).  Written as inline asm so that
+// the compiler does not add conservative vmcnt(0) waits in front of unrelated
+// LDS reads; every copy is instead waited for explicitly with wait_vmcnt<>
+// before a barrier, and each one is consumed before the kernel ends.  The
+// instruction writes no VGPR.
+__device__ __forceinline__ uint64_t uniform_u64(const void* p) {
+  const uint64_t x = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const __bf16* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p));
+}
+
+__device__ __forceinline__ void dma16(uint64_t sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(gaddr), "s"(m0)
+               : "v"(voff), "s"(sbase), "s"(m0)
                : "memory");
 }
 
-// Issue this wave's half of a 64-row tile load (1 KB per instruction), chunks
-// placed swizzled.  Rows past the end of the sequence re-read the last valid
-// row (those keys are always causally masked), so no LDS slot is left stale.
+// Per-lane byte offsets of this wave's share of one 64-row tile: slab n of
+// wave w covers rows (w * NL + n) * rowsPerLoad + lane / chunks, and the lane
+// fetches the logical chunk that lands, after the swizzle, in its LDS slot.
+// Rows at or past `nvalid` (short last block) re-read the last valid row; those
+// keys are always causally masked, and no LDS slot is left stale.
 template <int D, bool IS_V>
-__device__ __forceinline__ void issue_tile(const __bf16* __restrict__ g, int nvalid, __bf16* tile,
-                                           int wave, int lane) {
+__device__ __forceinline__ void tile_offsets(uint32_t (&off)[Cfg<D>::kLoadsPerWave], int nvalid,
+                                             int wave, int lane) {
   const int prow = lane / Cfg<D>::kChunks;
   const int pch = lane % Cfg<D>::kChunks;
 #pragma unroll
   for (int n = 0; n < Cfg<D>::kLoadsPerWave; ++n) {
-    const int slab = wave * Cfg<D>::kLoadsPerWave + n;
-    const int row = slab * Cfg<D>::kRowsPerLoad + prow;
+    const int row = (wave * Cfg<D>::kLoadsPerWave + n) * Cfg<D>::kRowsPerLoad + prow;
     const int lch = pch ^ (IS_V ? v_swz<D>(row) : k_swz<D>(row));
     const int grow = row < nvalid ? row : nvalid - 1;
-    dma16(g + (size_t)grow * D + lch * 8, tile + slab * 512);
+    off[n] = (uint32_t)((grow * D + lch * 8) * 2);
   }
 }
+
+template <int D>
+struct TileIssue {
+  uint32_t koff[Cfg<D>::kLoadsPerWave];
+  uint32_t voff[Cfg<D>::kLoadsPerWave];
+  uint32_t kbase_lds, vbase_lds;  // LDS byte address of this wave's first slab
+  __device__ __forceinline__ void init(const __bf16* ks, const __bf16* vs, int wave, int lane) {
+    tile_offsets<D, false>(koff, kBlk, wave, lane);
+    tile_offsets<D, true>(voff, kBlk, wave, lane);
+    kbase_lds = lds_u32(ks) + wave * Cfg<D>::kLoadsPerWave * 1024;
+    vbase_lds = lds_u32(vs) + wave * Cfg<D>::kLoadsPerWave * 1024;
+  }
+  // Issue this wave's half of a tile (K or V) whose first row is `g`.
+  template <bool IS_V>
+  __device__ __forceinline__ void issue(const __bf16* g, int nvalid, int wave, int lane) const {
+    const uint64_t sb = uniform_u64(g);
+    const uint32_t lb = IS_V ? vbase_lds : kbase_lds;
+    if (nvalid >= kBlk) {
+#pragma unroll
+      for (int n = 0; n < Cfg<D>::kLoadsPerWave; ++n)
+        dma16(sb, IS_V ? voff[n] : koff[n], lb + n * 1024);
+    } else {
+      uint32_t off[Cfg<D>::kLoadsPerWave];
+      tile_offsets<D, IS_V>(off, nvalid, wave, lane);
+#pragma unroll
+      for (int n = 0; n < Cfg<D>::kLoadsPerWave; ++n) dma16(sb, off[n], lb + n * 1024);
+    }
+  }
+};
 
 // Per-wave state of one query block: Q fragments, O^T accumulators, row stats.
 template <int D>
@@ -141,7 +182,8 @@ struct RowState {
 };
 
 // S^T = K Q^T for one 64-key tile (two 32-key MFMA tiles), causal mask on the
-// diagonal tile.  Reads the K tile from LDS.
+// diagonal tile.  Reads the K tile from LDS; all fragments of a 32-key tile
+// are requested before its MFMAs so the LDS latency is paid once.
 template <int D>
 __device__ __forceinline__ void qk_tile(const RowState<D>& st, const __bf16* ks, int lane, int wave,
                                         bool diag, f32x16 (&s)[2]) {
@@ -149,18 +191,21 @@ __device__ __forceinline__ void qk_tile(const RowState<D>& st, const __bf16* ks,
   const int half = lane >> 5;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    f32x16 a = {};
     const int kv = 32 * tt + col;
     const __bf16* krow = ks + kv * D;
     const int sw = k_swz<D>(kv);
+    bf16x8 kf[Cfg<D>::kKSteps];
 #pragma unroll
-    for (int t = 0; t < Cfg<D>::kKSteps; ++t) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + (((2 * t + half) ^ sw) * 8));
-      a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st.qf[t], a, 0, 0, 0);
-    }
+    for (int t = 0; t < Cfg<D>::kKSteps; ++t)
+      kf[t] = *reinterpret_cast<const bf16x8*>(krow + (((2 * t + half) ^ sw) * 8));
+    f32x16 a = {};
+#pragma unroll
+    for (int t = 0; t < Cfg<D>::kKSteps; ++t)
+      a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], st.qf[t], a, 0, 0, 0);
     s[tt] = a;
   }
-  if (diag) {
+  if (diag) {  // wave-uniform; the fence keeps it a branch instead of 32 selects per tile
+    compiler_fence();
     const int qrow = 32 * wave + col;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -172,15 +217,29 @@ __device__ __forceinline__ void qk_tile(const RowState<D>& st, const __bf16* ks,
   }
 }
 
+// v_max3_f32 directly: fmaxf chains on MFMA results otherwise get an extra
+// canonicalising v_max per element.  Inputs are finite or -inf (never NaN).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Online softmax update on S^T (in place -> P), returns the raw row max.
-template <int D>
+// EXACT_L: accumulate l from the fp32 probabilities here (the pooled map needs
+// l to fp32 accuracy); otherwise pv_tile sums the bf16 probabilities it feeds
+// to the MFMA, so numerator and denominator use the same weights.
+template <int D, bool EXACT_L>
 __device__ __forceinline__ float softmax_tile(RowState<D>& st, f32x16 (&s)[2], float c) {
-  float mx = fmaxf(s[0][0], s[0][1]);
+  float m0 = max3f(s[0][0], s[0][1], s[0][2]);
+  float m1 = max3f(s[1][0], s[1][1], s[1][2]);
 #pragma unroll
-  for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[0][r], s[0][r + 1]));
-#pragma unroll
-  for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[1][r], s[1][r + 1]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  for (int r = 3; r < 15; r += 2) {
+    m0 = max3f(m0, s[0][r], s[0][r + 1]);
+    m1 = max3f(m1, s[1][r], s[1][r + 1]);
+  }
+  float mx = max3f(m0, m1, max3f(s[0][15], s[1][15], -INFINITY));
+  mx = max3f(mx, __shfl_xor(mx, 32, 64), -INFINITY);
 
   const float cand = mx * c;
   const bool raise = cand > st.m + kRescaleSlack;
@@ -202,46 +261,62 @@ __device__ __forceinline__ float softmax_tile(RowState<D>& st, f32x16 (&s)[2], f
     for (int r = 0; r < 16; ++r) {
       const float p = __builtin_amdgcn_exp2f(fmaf(s[tt][r], c, nm));
       s[tt][r] = p;
-      lsum += p;
+      if (EXACT_L) lsum += p;
     }
-  st.l += lsum;
+  if (EXACT_L) st.l += lsum;
   return mx;
 }
 
 // O^T += V^T P^T.  The V tile sits in LDS in its natural [key][d] layout;
 // ds_read_b64_tr_b16 hands each lane four consecutive keys of one d, which is
 // exactly the A-fragment order matching P^T's registers.
-template <int D>
+template <int D, bool EXACT_L>
 __device__ __forceinline__ void pv_tile(RowState<D>& st, const f32x16 (&s)[2], const __bf16* vs,
                                         int lane) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
   const int g = lane >> 4;
   const int i = lane & 15;
   const int h = g >> 1;
   const int r = i >> 2;
   const int sub = 4 * (i & 1);
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float lsum = 0.f;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
+    const int kv_a = 16 * kk + 4 * h + r;
+    const int kv_b = kv_a + 8;
+    s16x4 va[Cfg<D>::kDTiles], vb[Cfg<D>::kDTiles];
+#pragma unroll
+    for (int dt = 0; dt < Cfg<D>::kDTiles; ++dt) {
+      const int lc = 4 * dt + 2 * (g & 1) + ((i & 3) >> 1);
+      va[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vs + kv_a * D + ((lc ^ v_swz<D>(kv_a)) * 8) + sub));
+      vb[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vs + kv_b * D + ((lc ^ v_swz<D>(kv_b)) * 8) + sub));
+    }
     const f32x16& src = s[kk >> 1];
     const int o = 8 * (kk & 1);
     const f32x8 pv = {src[o + 0], src[o + 1], src[o + 2], src[o + 3],
                       src[o + 4], src[o + 5], src[o + 6], src[o + 7]};
     const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
-    const int kv_a = 16 * kk + 4 * h + r;
-    const int kv_b = kv_a + 8;
+    if (!EXACT_L) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16x2 pair = {pb[2 * u], pb[2 * u + 1]};
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum, false);
+      }
+    }
 #pragma unroll
     for (int dt = 0; dt < Cfg<D>::kDTiles; ++dt) {
-      const int lc = 4 * dt + 2 * (g & 1) + ((i & 3) >> 1);
-      typedef short s16x4 __attribute__((ext_vector_type(4)));
-      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(vs + kv_a * D + ((lc ^ v_swz<D>(kv_a)) * 8) + sub));
-      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(vs + kv_b * D + ((lc ^ v_swz<D>(kv_b)) * 8) + sub));
-      typedef short s16x8 __attribute__((ext_vector_type(8)));
-      const s16x8 vv = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+      const s16x8 vv = {va[dt][0], va[dt][1], va[dt][2], va[dt][3],
+                        vb[dt][0], vb[dt][1], vb[dt][2], vb[dt][3]};
       st.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb,
                                                            st.acc[dt], 0, 0, 0);
     }
   }
+  if (!EXACT_L) st.l += lsum;
 }
 
 template <int D>
@@ -292,7 +367,7 @@ __device__ __forceinline__ float store_o(const RowState<D>& st, __bf16* __restri
 // The query fragments are loaded after the first tile's copies are issued and
 // everything is drained once before the loop, so Q's latency overlaps the first
 // tile's and the loop body never waits on an older load.
-template <int D, typename Next, typename Block, typename OnTile>
+template <int D, bool EXACT_L, typename Next, typename Block, typename OnTile>
 __device__ __forceinline__ void kv_loop(RowState<D>& st, const __bf16* __restrict__ qh, int q0,
                                         const __bf16* __restrict__ kh,
                                         const __bf16* __restrict__ vh, int T, int i, int n,
@@ -304,9 +379,11 @@ __device__ __forceinline__ void kv_loop(RowState<D>& st, const __bf16* __restric
     load_q<D>(st, qh, q0, T, lane, wave);
     return;
   }
+  TileIssue<D> io;
+  io.init(ks, vs, wave, lane);
   int j = block(e);
-  issue_tile<D, false>(kh + (size_t)kBlk * j * D, min(kBlk, T - kBlk * j), ks, wave, lane);
-  issue_tile<D, true>(vh + (size_t)kBlk * j * D, min(kBlk, T - kBlk * j), vs, wave, lane);
+  io.template issue<false>(kh + (size_t)kBlk * j * D, T - kBlk * j, wave, lane);
+  io.template issue<true>(vh + (size_t)kBlk * j * D, T - kBlk * j, wave, lane);
   load_q<D>(st, qh, q0, T, lane, wave);
   wait_vmcnt<0>();
   while (true) {
@@ -320,15 +397,15 @@ __device__ __forceinline__ void kv_loop(RowState<D>& st, const __bf16* __restric
     f32x16 s[2];
     qk_tile<D>(st, ks, lane, wave, cur == i, s);
     wg_barrier_reads_done();  // every wave is done reading K(cur)
-    if (more) issue_tile<D, false>(kh + (size_t)kBlk * j * D, min(kBlk, T - kBlk * j), ks, wave, lane);
-    const float mx = softmax_tile<D>(st, s, c);
+    if (more) io.template issue<false>(kh + (size_t)kBlk * j * D, T - kBlk * j, wave, lane);
+    const float mx = softmax_tile<D, EXACT_L>(st, s, c);
     on_tile(cur, mx);
     if (more) wait_vmcnt<NL>(); else wait_vmcnt<0>();  // V(cur) has landed
     wg_barrier();
-    pv_tile<D>(st, s, vs, lane);
+    pv_tile<D, EXACT_L>(st, s, vs, lane);
     wg_barrier_reads_done();  // every wave is done reading V(cur)
     if (!more) break;
-    issue_tile<D, true>(vh + (size_t)kBlk * j * D, min(kBlk, T - kBlk * j), vs, wave, lane);
+    io.template issue<true>(vh + (size_t)kBlk * j * D, T - kBlk * j, wave, lane);
   }
 }
 
@@ -368,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_prefill_kernel(
   };
   auto block = [&](int e) { return lst[e]; };
   auto on_tile = [](int, float) {};
-  kv_loop<D>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, n, next, block, on_tile, ks,
+  kv_loop<D, false>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, n, next, block, on_tile, ks,
              vs, lane, wave, c);
   (void)store_o<D>(st, o + q_off, kBlk * i, T, lane, wave);
 }
@@ -430,7 +507,7 @@ __global__ __launch_bounds__(kThreads, 2) void pooled_map_kernel(
   auto on_tile = [&](int j, float mx) {
     if (lane < 32) rrow[(size_t)j * kBlk + 32 * wave + lane] = mx;
   };
-  kv_loop<D>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, i + 1, next, block, on_tile,
+  kv_loop<D, true>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, i + 1, next, block, on_tile,
              ks, vs, lane, wave, c);
   const float l = store_o<D>(st, o + q_off, kBlk * i, T, lane, wave);
   if (lane < 32) {
@@ -460,56 +537,54 @@ __global__ __launch_bounds__(kThreads, 2) void pooled_map_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Schedule: order (b, h, i) items by descending block count (longest first),
-// optionally grouping each KV head's items onto one XCD.  Single workgroup.
+// Schedule (longest-processing-time first): one workgroup per KV group
+// (b, g) counting-sorts that group's G * nQB query-block items by descending
+// list length; the rank-r item of group q goes to position r * NG + q of the
+// work list.  Workgroups are dispatched in position order, so long rows start
+// first everywhere; and since the hardware deals workgroup L to XCD L % 8,
+// every item of a group lands on the same XCD whenever NG is a multiple of 8
+// (its K/V then stays in that XCD's L2).
 constexpr int kSchedThreads = 1024;
 constexpr int kCostBins = 1024;
 
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
-    const int32_t* __restrict__ cnt, int B, int Hq, int Hkv, int nqb, int max_k,
+    const int32_t* __restrict__ cnt, int Hq, int Hkv, int nqb, int max_k,
     int32_t* __restrict__ work) {
-  __shared__ int hist[kXcds][kCostBins];
+  __shared__ int hist[kCostBins];
   __shared__ int wsum[kSchedThreads / 64];
   const int tid = threadIdx.x;
+  const int ng = gridDim.x;
+  const int grp = blockIdx.x;
   const int G = Hq / Hkv;
-  const bool affinity = (B * Hkv) % kXcds == 0;
-  const int nb = affinity ? kXcds : 1;
-  const int n = B * Hq * nqb;
-  for (int x = tid; x < kXcds * kCostBins; x += kSchedThreads) (&hist[0][0])[x] = 0;
-  __syncthreads();
-  auto bucket_of = [&](int item) {
-    if (!affinity) return 0;
-    const int bh = item / nqb;
-    const int grp = (bh / Hq) * Hkv + (bh % Hq) / G;
-    return grp % kXcds;
+  const int b = grp / Hkv;
+  const int g = grp % Hkv;
+  const int base = (b * Hq + g * G) * nqb;  // the group's items are contiguous
+  const int count = G * nqb;
+  auto bin_of = [&](int it) {
+    const int c = min(max(cnt[base + it], 0), max_k);
+    return kCostBins - 1 - min(c, kCostBins - 1);  // bin 0 = longest list
   };
-  auto bin_of = [&](int item) {
-    const int c = min(max(cnt[item], 0), max_k);
-    return kCostBins - 1 - min(c, kCostBins - 1);  // bin 0 = most expensive
-  };
-  for (int it = tid; it < n; it += kSchedThreads) atomicAdd(&hist[bucket_of(it)][bin_of(it)], 1);
+  hist[tid] = 0;
   __syncthreads();
-  // Exclusive scan of each bucket's histogram (bin order = descending cost).
+  for (int it = tid; it < count; it += kSchedThreads) atomicAdd(&hist[bin_of(it)], 1);
+  __syncthreads();
   const int lane = tid & 63, wv = tid >> 6;
-  for (int bk = 0; bk < nb; ++bk) {
-    const int v = hist[bk][tid];
-    int incl = v;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
-    if (lane == 63) wsum[wv] = incl;
-    __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wv; ++w) before += wsum[w];
-    __syncthreads();
-    hist[bk][tid] = before + incl - v;
-    __syncthreads();
+  const int v = hist[tid];
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
   }
-  for (int it = tid; it < n; it += kSchedThreads) {
-    const int bk = bucket_of(it);
-    const int pos = atomicAdd(&hist[bk][bin_of(it)], 1);
-    work[affinity ? pos * kXcds + bk : pos] = it;
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wv; ++w) before += wsum[w];
+  hist[tid] = before + incl - v;  // exclusive offset of this bin
+  __syncthreads();
+  for (int it = tid; it < count; it += kSchedThreads) {
+    const int rank = atomicAdd(&hist[bin_of(it)], 1);
+    work[rank * ng + grp] = base + it;
   }
 }
 
@@ -518,8 +593,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
 hipError_t launch_schedule(const int32_t* cnt, int B, int Hq, int Hkv, int nqb, int max_k,
                            int32_t* work, hipStream_t stream) {
   if ((size_t)B * Hq * nqb == 0) return hipSuccess;
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, cnt, B, Hq, Hkv,
-                     nqb, max_k, work);
+  hipLaunchKernelGGL(schedule_kernel, dim3(B * Hkv), dim3(kSchedThreads), 0, stream, cnt, Hq,
+                     Hkv, nqb, max_k, work);
   return hipGetLastError();
 }
 

@@ -5,21 +5,26 @@
 // [Seq/Block, TopK] index layout from the rebuttal "SeerAttention: Learning
 // Intrinsic Sparse Attention in Your LLMs", "Weakness 2 (Memory complexity)").
 //
-// One 256-thread workgroup owns one row (b, h, i).  Every candidate j <= i gets
-// a 32-bit key that orders it exactly as the selection rule ranks it:
+// Every candidate j <= i gets a 32-bit key that orders it exactly as the
+// selection rule ranks it:
 //   forced blocks (diagonal, optional block 0)  -> 0xFFFFFFFF (always first)
 //   ranked candidates                           -> order-preserving image of the
 //                                                  fp32 score (NaN as -inf, -0 as +0)
 //   threshold mode, score below threshold       -> 0 (never selected)
-// A 4-pass, 8-bit radix select finds the k-th largest key t; ties on t are
-// broken toward lower block indices by a prefix count in index order, which is
-// also the output order, so the list comes out ascending without a sort.
+// An 8-bit-digit radix select finds the k-th largest key t; ties on t are broken
+// toward lower block indices by a running count in index order, which is also
+// the output order, so each list comes out ascending without a sort.
+//
+// One wave64 owns one row.  Row i's candidates sit in registers, candidate
+// j = 64 * c + lane in slot c, so the score row is read from HBM once and the
+// compaction is a ballot + popcount per 64 candidates.  The digit histograms
+// live in a per-wave 1 KB slice of LDS.
 #include "seer_internal.h"
 
 namespace seer {
 namespace {
 
-constexpr int kMaskThreads = 256;
+constexpr int kWavesPerGroup = 4;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -28,113 +33,136 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over the workgroup; *total receives the sum.
-__device__ __forceinline__ int block_excl_scan(int v, int* total, int* lds4) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  int incl = v;
+__device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) lds4[wave] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kMaskThreads / 64; ++w) {
-    int t = lds4[w];
-    before += (w < wave) ? t : 0;
-    all += t;
-  }
-  __syncthreads();
-  *total = all;
-  return before + incl - v;
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
 }
 
-__global__ __launch_bounds__(kMaskThreads) void build_mask_kernel(
-    const float* __restrict__ scores, int nqb, int nkb, int mode, float tau, double density,
-    int keep_sink, int32_t* __restrict__ idx, int32_t* __restrict__ cnt, int max_k) {
-  __shared__ int hist[256];
-  __shared__ int lds4[kMaskThreads / 64];
-  __shared__ int sel_bin, sel_above;
+// Inclusive prefix sum over the wave (lane order).
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
+  }
+  return v;
+}
 
-  const size_t row = blockIdx.x;
-  const int i = (int)(row % (size_t)nqb);
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int popc_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// NPL = key slots per lane (row length <= 64 * NPL).
+template <int NPL>
+__global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
+    const float* __restrict__ scores, long long rows, int nqb, int nkb, int mode, float tau,
+    double density, int keep_sink, int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
+    int max_k) {
+  __shared__ int hist_all[kWavesPerGroup][256];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * kWavesPerGroup + wv;
+  if (row >= rows) return;
+  int* hist = hist_all[wv];
+  const int i = (int)(row % nqb);
   const int n = i + 1;
-  const int tid = threadIdx.x;
-  const float* srow = scores + row * (size_t)nkb;
-  int32_t* out = idx + row * (size_t)max_k;
+  const float* srow = scores + row * (long long)nkb;
+  int32_t* out = idx + row * (long long)max_k;
 
-  auto key_of = [&](int j) -> uint32_t {
-    if (j == i || (keep_sink && j == 0)) return 0xFFFFFFFFu;
-    const float s = srow[j];
-    if (mode == 1) return order_key(s);
-    return (s >= tau) ? order_key(s) : 0u;
-  };
-
-  int npos_local = 0;
-  for (int j = tid; j < n; j += kMaskThreads) npos_local += key_of(j) != 0u;
-  int npos;
-  (void)block_excl_scan(npos_local, &npos, lds4);
+  uint32_t key[NPL];
+  int npos = 0;
+#pragma unroll
+  for (int c = 0; c < NPL; ++c) {
+    const int j = 64 * c + lane;
+    uint32_t kj = 0u;
+    if (j < n) {
+      if (j == i || (keep_sink && j == 0)) {
+        kj = 0xFFFFFFFFu;
+      } else {
+        const float s = srow[j];
+        kj = (mode == 1 || s >= tau) ? order_key(s) : 0u;
+      }
+    }
+    key[c] = kj;
+    npos += kj != 0u;
+  }
+  npos = wave_sum(npos);
 
   int k;
   if (mode == 1) {
     const int forced = (i == 0) ? 1 : (keep_sink ? 2 : 1);
-    const double c = ceil(density * (double)(i + 1));
-    k = min(i + 1, max(forced, (int)c));
+    const double cf = ceil(density * (double)(i + 1));
+    k = min(i + 1, max(forced, (int)cf));
   } else {
     k = min(npos, max_k);
   }
 
-  // Keys > t are kept, and the first `need` keys equal to t in index order.
+  // Keys > t are kept, plus the first `need` keys equal to t in index order.
   uint32_t t = 0u;
   int need = 0;
   if (k < npos) {
     uint32_t prefix = 0u, mask = 0u;
     int remaining = k;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
-      __syncthreads();
-      for (int j = tid; j < n; j += kMaskThreads) {
-        const uint32_t kj = key_of(j);
-        if ((kj & mask) == prefix) atomicAdd(&hist[(kj >> shift) & 255u], 1);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) hist[lane + 64 * b] = 0;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int c = 0; c < NPL; ++c)
+        if ((key[c] & mask) == prefix && key[c] != 0u)
+          atomicAdd(&hist[(key[c] >> shift) & 255u], 1);
+      __builtin_amdgcn_wave_barrier();
+      // Lane l owns bins 255-4l .. 252-4l (descending); running count from the top.
+      int hc[4], local = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        hc[b] = hist[255 - 4 * lane - b];
+        local += hc[b];
       }
-      __syncthreads();
-      // Thread tid looks at bin 255 - tid: running count from the top bin down.
-      const int c = hist[255 - tid];
-      int tot;
-      const int excl = block_excl_scan(c, &tot, lds4);
-      if (excl < remaining && remaining <= excl + c) {
-        sel_bin = 255 - tid;
-        sel_above = excl;
+      const int incl = wave_incl_scan(local, lane);
+      int above = incl - local;
+      int sel_bin = -1, sel_above = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (sel_bin < 0 && above < remaining && remaining <= above + hc[b]) {
+          sel_bin = 255 - 4 * lane - b;
+          sel_above = above;
+        }
+        above += hc[b];
       }
-      __syncthreads();
+      const uint64_t who = __ballot(sel_bin >= 0);
+      const int src = __builtin_ctzll(who);
+      sel_bin = __shfl(sel_bin, src, 64);
+      sel_above = __shfl(sel_above, src, 64);
       prefix |= (uint32_t)sel_bin << shift;
       mask |= 0xFFu << shift;
       remaining -= sel_above;
-      __syncthreads();
+      __builtin_amdgcn_wave_barrier();
     }
     t = prefix;
     need = remaining;
   }
 
   int base = 0, ties = 0;
-  for (int j0 = 0; j0 < n; j0 += kMaskThreads) {
-    const int j = j0 + tid;
-    const uint32_t kj = (j < n) ? key_of(j) : 0u;
-    const bool eq = (j < n) && (kj == t);
-    int eq_tot;
-    const int eq_rank = ties + block_excl_scan(eq ? 1 : 0, &eq_tot, lds4);
-    ties += eq_tot;
-    const bool keep = (j < n) && (kj > t || (eq && eq_rank < need));
-    int kept;
-    const int pos = base + block_excl_scan(keep ? 1 : 0, &kept, lds4);
-    if (keep) out[pos] = j;
-    base += kept;
+#pragma unroll
+  for (int c = 0; c < NPL; ++c) {
+    if (64 * c >= n) break;
+    const int j = 64 * c + lane;
+    const bool valid = j < n;
+    const bool eq = valid && key[c] == t;
+    const uint64_t eqm = __ballot(eq);
+    const int eq_rank = ties + popc_below(eqm);
+    ties += __popcll(eqm);
+    const bool keep = valid && (key[c] > t || (eq && eq_rank < need));
+    const uint64_t km = __ballot(keep);
+    if (keep) out[base + popc_below(km)] = j;
+    base += __popcll(km);
   }
-  for (int p = base + tid; p < max_k; p += kMaskThreads) out[p] = -1;
-  if (tid == 0) cnt[row] = base;
+  for (int p = base + lane; p < max_k; p += 64) out[p] = -1;
+  if (lane == 0) cnt[row] = base;
 }
 
 }  // namespace
@@ -142,10 +170,21 @@ __global__ __launch_bounds__(kMaskThreads) void build_mask_kernel(
 hipError_t launch_build_mask(const float* scores, int B, int H, int nqb, int nkb, int mode,
                              float threshold, double density, int keep_sink, int32_t* idx,
                              int32_t* cnt, int max_k, hipStream_t stream) {
-  const size_t rows = (size_t)B * H * nqb;
+  const long long rows = (long long)B * H * nqb;
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(build_mask_kernel, dim3((unsigned)rows), dim3(kMaskThreads), 0, stream,
-                     scores, nqb, nkb, mode, threshold, density, keep_sink, idx, cnt, max_k);
+  const dim3 grid((unsigned)((rows + kWavesPerGroup - 1) / kWavesPerGroup));
+  const dim3 block(64 * kWavesPerGroup);
+#define SEER_MASK_LAUNCH(NPL)                                                                  \
+  hipLaunchKernelGGL(build_mask_kernel<NPL>, grid, block, 0, stream, scores, rows, nqb, nkb,   \
+                     mode, threshold, density, keep_sink, idx, cnt, max_k)
+  if (nqb <= 64 * 1) SEER_MASK_LAUNCH(1);
+  else if (nqb <= 64 * 4) SEER_MASK_LAUNCH(4);
+  else if (nqb <= 64 * 8) SEER_MASK_LAUNCH(8);
+  else if (nqb <= 64 * 16) SEER_MASK_LAUNCH(16);
+  else if (nqb <= 64 * 32) SEER_MASK_LAUNCH(32);
+  else if (nqb <= 64 * 64) SEER_MASK_LAUNCH(64);
+  else return hipErrorInvalidValue;  // the host layer rejects nQB > 4096 first
+#undef SEER_MASK_LAUNCH
   return hipGetLastError();
 }
 

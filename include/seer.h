@@ -46,6 +46,8 @@ extern "C" {
 #endif
 
 #define SEER_BLOCK 64
+/* Longest row seer_build_mask accepts: 4096 blocks = 262144 tokens. */
+#define SEER_MAX_QUERY_BLOCKS 4096
 
 typedef enum {
   SEER_OK = 0,
@@ -94,6 +96,7 @@ int seer_topk_budget(int nQB, double density, int keep_sink);
  * kv_idx  device int32 out [B, H, nQB, max_k]: row (b,h,i) holds its selected
  *         blocks in strictly ascending order, then -1 up to max_k.
  * kv_cnt  device int32 out [B, H, nQB]: list lengths (always <= max_k).
+ * nQB     <= SEER_MAX_QUERY_BLOCKS, else SEER_ERR_UNSUPPORTED.
  * max_k   TopK: >= seer_topk_budget(nQB, density, keep_sink);
  *         threshold: >= 2 if keep_sink and nQB > 1, else >= 1.
  *         Otherwise SEER_ERR_CAPACITY.

@@ -74,6 +74,8 @@ FAKE = 1 << 20  # never dereferenced: every call below fails its host checks fir
     ((FAKE, 1, 1, 4, 4, 0, 0.1, 0.5, 1, FAKE, FAKE, 1, None), 3),
     # null output
     ((FAKE, 1, 1, 4, 4, 1, 0.0, 0.5, 1, None, FAKE, 4, None), 1),
+    # row longer than SEER_MAX_QUERY_BLOCKS
+    ((FAKE, 1, 1, 4097, 4097, 1, 0.0, 0.5, 1, FAKE, FAKE, 4097, None), 2),
 ])
 def test_build_mask_rejects_on_host(args, status):
     assert seer.load().seer_build_mask(*args) == status
