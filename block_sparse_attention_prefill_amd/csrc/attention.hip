@@ -54,10 +54,27 @@ struct Cfg {
   static constexpr int kRowsPerLoad = 64 / kChunks;      // rows per 1 KB wave-wide LDS load
   static constexpr int kLoadsPerTile = kBlk / kRowsPerLoad;
   static constexpr int kLoadsPerWave = kLoadsPerTile / 2;
-  static constexpr int kTileElems = kBlk * D;
   static constexpr int kKSteps = D / 16;                 // k-steps of the S^T contraction
   static constexpr int kDTiles = D / 32;                 // 32-row tiles of O^T
+  // LDS tile layout: slab n (one 1 KB wave-wide copy) holds rows n, n + S,
+  // n + 2S, ... (S = kLoadsPerTile slabs per tile), each row whole and in order,
+  // so every 16-lane group of a copy reads one contiguous row from HBM.  Slabs
+  // are spaced by a padded stride so that the rows read together land on
+  // distinct LDS banks: 16 rows at one 16-byte chunk for K (stride = 1 KB + 16 B,
+  // rows step by 4 banks), 4 rows x 4 chunks for the V transpose reads (stride =
+  // 1 KB + 64 B, rows step by 16 banks).
+  static constexpr int kKSlab = 1024 + 16;
+  static constexpr int kVSlab = 1024 + 64;
+  static constexpr int kKTileBytes = kLoadsPerTile * kKSlab;
+  static constexpr int kVTileBytes = kLoadsPerTile * kVSlab;
 };
+
+// Byte offset of (row, 16-byte chunk) inside a K or V tile in LDS.
+template <int D, bool IS_V>
+__device__ __forceinline__ int tile_byte(int row, int chunk) {
+  constexpr int S = Cfg<D>::kLoadsPerTile;
+  return (row % S) * (IS_V ? Cfg<D>::kVSlab : Cfg<D>::kKSlab) + (row / S) * (2 * D) + 16 * chunk;
+}
 
 #define SEER_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -87,17 +104,6 @@ __device__ __forceinline__ void wg_barrier_reads_done() {
   compiler_fence();
 }
 
-// XOR swizzles of the 16-byte chunks of a tile row in LDS.  K rows are read 8
-// or 16 at a time at one logical chunk, so row r is rotated by r.  V rows are
-// read by ds_read_b64_tr_b16 four rows at a time over 2 (or 4) adjacent chunks;
-// the per-row masks {0,6,10,12} keep those reads on distinct banks.
-template <int D>
-__device__ __forceinline__ int k_swz(int row) { return row & (Cfg<D>::kChunks - 1); }
-template <int D>
-__device__ __forceinline__ int v_swz(int row) {
-  return D == 128 ? ((0xCA60 >> (4 * (row & 3))) & 15) : ((0x4260 >> (4 * (row & 3))) & 7);
-}
-
 // One wave-wide HBM -> LDS copy: every lane moves 16 bytes from sbase + voff
 // (its own byte offset) to lds_base + 16 * lane (global_load_lds_dwordx4 in
 // its SGPR-base form; M0 holds the LDS base).  Written as inline asm so that
@@ -112,7 +118,7 @@ __device__ __forceinline__ uint64_t uniform_u64(const void* p) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ uint32_t lds_u32(const __bf16* p) {
+__device__ __forceinline__ uint32_t lds_u32(const char* p) {
   return __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p));
 }
@@ -124,50 +130,47 @@ __device__ __forceinline__ void dma16(uint64_t sbase, uint32_t voff, uint32_t m0
                : "memory");
 }
 
-// Per-lane byte offsets of this wave's share of one 64-row tile: slab n of
-// wave w covers rows (w * NL + n) * rowsPerLoad + lane / chunks, and the lane
-// fetches the logical chunk that lands, after the swizzle, in its LDS slot.
-// Rows at or past `nvalid` (short last block) re-read the last valid row; those
-// keys are always causally masked, and no LDS slot is left stale.
-template <int D, bool IS_V>
+// Per-lane HBM byte offsets of this wave's share of one 64-row tile: slab n of
+// wave w is slab w * NL + n; its lane L copies chunk L % chunks of row
+// slab + S * (L / chunks).  Rows at or past `nvalid` (short last block) re-read
+// the last valid row; those keys are always causally masked, and no LDS slot is
+// left stale.
+template <int D>
 __device__ __forceinline__ void tile_offsets(uint32_t (&off)[Cfg<D>::kLoadsPerWave], int nvalid,
                                              int wave, int lane) {
-  const int prow = lane / Cfg<D>::kChunks;
-  const int pch = lane % Cfg<D>::kChunks;
+  const int r = lane / Cfg<D>::kChunks;
+  const int ch = lane % Cfg<D>::kChunks;
 #pragma unroll
   for (int n = 0; n < Cfg<D>::kLoadsPerWave; ++n) {
-    const int row = (wave * Cfg<D>::kLoadsPerWave + n) * Cfg<D>::kRowsPerLoad + prow;
-    const int lch = pch ^ (IS_V ? v_swz<D>(row) : k_swz<D>(row));
+    const int row = (wave * Cfg<D>::kLoadsPerWave + n) + Cfg<D>::kLoadsPerTile * r;
     const int grow = row < nvalid ? row : nvalid - 1;
-    off[n] = (uint32_t)((grow * D + lch * 8) * 2);
+    off[n] = (uint32_t)((grow * D + ch * 8) * 2);
   }
 }
 
 template <int D>
 struct TileIssue {
-  uint32_t koff[Cfg<D>::kLoadsPerWave];
-  uint32_t voff[Cfg<D>::kLoadsPerWave];
+  uint32_t off[Cfg<D>::kLoadsPerWave];
   uint32_t kbase_lds, vbase_lds;  // LDS byte address of this wave's first slab
-  __device__ __forceinline__ void init(const __bf16* ks, const __bf16* vs, int wave, int lane) {
-    tile_offsets<D, false>(koff, kBlk, wave, lane);
-    tile_offsets<D, true>(voff, kBlk, wave, lane);
-    kbase_lds = lds_u32(ks) + wave * Cfg<D>::kLoadsPerWave * 1024;
-    vbase_lds = lds_u32(vs) + wave * Cfg<D>::kLoadsPerWave * 1024;
+  __device__ __forceinline__ void init(const char* ks, const char* vs, int wave, int lane) {
+    tile_offsets<D>(off, kBlk, wave, lane);
+    kbase_lds = lds_u32(ks) + wave * Cfg<D>::kLoadsPerWave * Cfg<D>::kKSlab;
+    vbase_lds = lds_u32(vs) + wave * Cfg<D>::kLoadsPerWave * Cfg<D>::kVSlab;
   }
-  // Issue this wave's half of a tile (K or V) whose first row is `g`.
+  // Issue this wave's share of a tile (K or V) whose first row is `g`.
   template <bool IS_V>
   __device__ __forceinline__ void issue(const __bf16* g, int nvalid, int wave, int lane) const {
     const uint64_t sb = uniform_u64(g);
     const uint32_t lb = IS_V ? vbase_lds : kbase_lds;
+    constexpr uint32_t stride = IS_V ? Cfg<D>::kVSlab : Cfg<D>::kKSlab;
     if (nvalid >= kBlk) {
 #pragma unroll
-      for (int n = 0; n < Cfg<D>::kLoadsPerWave; ++n)
-        dma16(sb, IS_V ? voff[n] : koff[n], lb + n * 1024);
+      for (int n = 0; n < Cfg<D>::kLoadsPerWave; ++n) dma16(sb, off[n], lb + n * stride);
     } else {
-      uint32_t off[Cfg<D>::kLoadsPerWave];
-      tile_offsets<D, IS_V>(off, nvalid, wave, lane);
+      uint32_t o[Cfg<D>::kLoadsPerWave];
+      tile_offsets<D>(o, nvalid, wave, lane);
 #pragma unroll
-      for (int n = 0; n < Cfg<D>::kLoadsPerWave; ++n) dma16(sb, off[n], lb + n * 1024);
+      for (int n = 0; n < Cfg<D>::kLoadsPerWave; ++n) dma16(sb, o[n], lb + n * stride);
     }
   }
 };
@@ -185,19 +188,17 @@ struct RowState {
 // diagonal tile.  Reads the K tile from LDS; all fragments of a 32-key tile
 // are requested before its MFMAs so the LDS latency is paid once.
 template <int D>
-__device__ __forceinline__ void qk_tile(const RowState<D>& st, const __bf16* ks, int lane, int wave,
+__device__ __forceinline__ void qk_tile(const RowState<D>& st, const char* ks, int lane, int wave,
                                         bool diag, f32x16 (&s)[2]) {
   const int col = lane & 31;
   const int half = lane >> 5;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    const int kv = 32 * tt + col;
-    const __bf16* krow = ks + kv * D;
-    const int sw = k_swz<D>(kv);
+    const char* krow = ks + tile_byte<D, false>(32 * tt + col, half);
     bf16x8 kf[Cfg<D>::kKSteps];
 #pragma unroll
     for (int t = 0; t < Cfg<D>::kKSteps; ++t)
-      kf[t] = *reinterpret_cast<const bf16x8*>(krow + (((2 * t + half) ^ sw) * 8));
+      kf[t] = *reinterpret_cast<const bf16x8*>(krow + 32 * t);
     f32x16 a = {};
 #pragma unroll
     for (int t = 0; t < Cfg<D>::kKSteps; ++t)
@@ -271,7 +272,7 @@ __device__ __forceinline__ float softmax_tile(RowState<D>& st, f32x16 (&s)[2], f
 // ds_read_b64_tr_b16 hands each lane four consecutive keys of one d, which is
 // exactly the A-fragment order matching P^T's registers.
 template <int D, bool EXACT_L>
-__device__ __forceinline__ void pv_tile(RowState<D>& st, const f32x16 (&s)[2], const __bf16* vs,
+__device__ __forceinline__ void pv_tile(RowState<D>& st, const f32x16 (&s)[2], const char* vs,
                                         int lane) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -287,14 +288,15 @@ __device__ __forceinline__ void pv_tile(RowState<D>& st, const f32x16 (&s)[2], c
   for (int kk = 0; kk < 4; ++kk) {
     const int kv_a = 16 * kk + 4 * h + r;
     const int kv_b = kv_a + 8;
+    const char* va_row = vs + tile_byte<D, true>(kv_a, 2 * (g & 1) + ((i & 3) >> 1)) + 2 * sub;
+    const char* vb_row = vs + tile_byte<D, true>(kv_b, 2 * (g & 1) + ((i & 3) >> 1)) + 2 * sub;
     s16x4 va[Cfg<D>::kDTiles], vb[Cfg<D>::kDTiles];
 #pragma unroll
     for (int dt = 0; dt < Cfg<D>::kDTiles; ++dt) {
-      const int lc = 4 * dt + 2 * (g & 1) + ((i & 3) >> 1);
       va[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(vs + kv_a * D + ((lc ^ v_swz<D>(kv_a)) * 8) + sub));
+          (__attribute__((address_space(3))) s16x4*)(va_row + 64 * dt));
       vb[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(vs + kv_b * D + ((lc ^ v_swz<D>(kv_b)) * 8) + sub));
+          (__attribute__((address_space(3))) s16x4*)(vb_row + 64 * dt));
     }
     const f32x16& src = s[kk >> 1];
     const int o = 8 * (kk & 1);
@@ -371,8 +373,8 @@ template <int D, bool EXACT_L, typename Next, typename Block, typename OnTile>
 __device__ __forceinline__ void kv_loop(RowState<D>& st, const __bf16* __restrict__ qh, int q0,
                                         const __bf16* __restrict__ kh,
                                         const __bf16* __restrict__ vh, int T, int i, int n,
-                                        Next next, Block block, OnTile on_tile, __bf16* ks,
-                                        __bf16* vs, int lane, int wave, float c) {
+                                        Next next, Block block, OnTile on_tile, char* ks,
+                                        char* vs, int lane, int wave, float c) {
   constexpr int NL = Cfg<D>::kLoadsPerWave;
   int e = next(0);
   if (e >= n) {
@@ -417,8 +419,8 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_prefill_kernel(
     int Hq, int Hkv, int T, int nqb, float c, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ cnt, int max_k, const int32_t* __restrict__ work,
     __bf16* __restrict__ o) {
-  __shared__ __attribute__((aligned(1024))) __bf16 ks[Cfg<D>::kTileElems];
-  __shared__ __attribute__((aligned(1024))) __bf16 vs[Cfg<D>::kTileElems];
+  __shared__ __attribute__((aligned(1024))) char ks[Cfg<D>::kKTileBytes];
+  __shared__ __attribute__((aligned(1024))) char vs[Cfg<D>::kVTileBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -483,8 +485,8 @@ __global__ __launch_bounds__(kThreads, 2) void pooled_map_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     int B, int Hq, int Hkv, int T, int nqb, float c, __bf16* __restrict__ o,
     float* __restrict__ amap, float* __restrict__ rws) {
-  __shared__ __attribute__((aligned(1024))) __bf16 ks[Cfg<D>::kTileElems];
-  __shared__ __attribute__((aligned(1024))) __bf16 vs[Cfg<D>::kTileElems];
+  __shared__ __attribute__((aligned(1024))) char ks[Cfg<D>::kKTileBytes];
+  __shared__ __attribute__((aligned(1024))) char vs[Cfg<D>::kVTileBytes];
   __shared__ float ms[kBlk];
   __shared__ float ils[kBlk];
 
