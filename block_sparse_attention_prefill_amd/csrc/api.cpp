@@ -93,7 +93,7 @@ int seer_build_mask(const float* scores, int B, int H, int nQB, int nKB, int mod
 size_t seer_sparse_prefill_workspace_size(int B, int Hq, int Hkv, int T) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || T < 0 || Hq % Hkv != 0) return 0;
   if (!items_fit(B, Hq, nqb_of(T))) return 0;
-  const size_t entries = seer::schedule_entries(B, Hq, nqb_of(T));
+  const size_t entries = seer::sparse_work_entries(B, Hq, Hkv, nqb_of(T));
   return ((entries * sizeof(int32_t) + 255) / 256) * 256 + 256;
 }
 
@@ -108,13 +108,9 @@ int seer_sparse_prefill(const void* q, const void* k, const void* v, int B, int 
   if (!kv_idx || !kv_cnt) return SEER_ERR_INVALID_ARG;
   const size_t need = seer_sparse_prefill_workspace_size(B, Hq, Hkv, T);
   if (!workspace || workspace_bytes < need || !aligned256(workspace)) return SEER_ERR_WORKSPACE;
-  const int nqb = nqb_of(T);
-  hipStream_t s = (hipStream_t)stream;
-  int32_t* work = static_cast<int32_t*>(workspace);
-  hipError_t err = seer::launch_schedule(kv_cnt, B, Hq, Hkv, nqb, max_k, work, s);
-  if (err != hipSuccess) return SEER_ERR_HIP;
-  err = seer::launch_sparse_prefill(q, k, v, B, Hq, Hkv, T, D, sm_scale, kv_idx, kv_cnt, max_k,
-                                    work, o, s);
+  const hipError_t err =
+      seer::launch_sparse_prefill(q, k, v, B, Hq, Hkv, T, D, sm_scale, kv_idx, kv_cnt, max_k,
+                                  static_cast<int32_t*>(workspace), o, (hipStream_t)stream);
   return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
 }
 

@@ -17,20 +17,16 @@ typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef float f32x8 __attribute__((__vector_size__(8 * sizeof(float))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
-// Work-item order used by the attention kernels (one item = one query block of
-// one head).  Size of the list in int32 entries.
-inline size_t schedule_entries(int B, int Hq, int nqb) { return (size_t)B * Hq * nqb; }
+// int32 entries of the sparse prefill's work lists (schedule output).
+size_t sparse_work_entries(int B, int Hq, int Hkv, int nqb);
 
 hipError_t launch_build_mask(const float* scores, int B, int H, int nqb, int nkb, int mode,
                              float threshold, double density, int keep_sink, int32_t* idx,
                              int32_t* cnt, int max_k, hipStream_t stream);
 
-hipError_t launch_schedule(const int32_t* cnt, int B, int Hq, int Hkv, int nqb, int max_k,
-                           int32_t* work, hipStream_t stream);
-
 hipError_t launch_sparse_prefill(const void* q, const void* k, const void* v, int B, int Hq,
                                  int Hkv, int T, int D, float sm_scale, const int32_t* idx,
-                                 const int32_t* cnt, int max_k, const int32_t* work, void* o,
+                                 const int32_t* cnt, int max_k, int32_t* work, void* o,
                                  hipStream_t stream);
 
 hipError_t launch_pooled_map(const void* q, const void* k, const void* v, int B, int Hq,

@@ -192,9 +192,13 @@ def _random_lists(seed, b, h, nqb, max_k, mode):
     for bb in range(b):
         for hh in range(h):
             for i in range(nqb):
-                m = int(rng.integers(0, min(i + 1, max_k) + 1))
+                hi = min(i + 1, max_k)
+                if mode == "dense":  # mostly heavy rows, so that head pairs share a workgroup
+                    m = int(rng.integers(max(0, (3 * hi) // 4), hi + 1))
+                else:
+                    m = int(rng.integers(0, hi + 1))
                 sel = list(rng.choice(i + 1, size=m, replace=False)) if m else []
-                if mode == "unsorted":
+                if mode in ("unsorted", "dense"):
                     rng.shuffle(sel)
                 else:
                     sel.sort()
@@ -214,6 +218,8 @@ def _random_lists(seed, b, h, nqb, max_k, mode):
     (1, 3, 3, 200, 128, "invalid"),     # MHA, invalid entries, cnt > max_k, empty rows
     (1, 8, 1, 64, 128, "sorted"),       # a single block
     (1, 2, 1, 33, 64, "sorted"),        # shorter than one block
+    (1, 8, 2, 900, 128, "dense"),       # GQA 4, heavy unsorted rows: paired and single items
+    (2, 4, 1, 450, 64, "invalid"),      # GQA 4, invalid entries in paired rows
 ])
 def test_sparse_prefill_shapes_and_lists(b, hq, hkv, t, d, mode):
     announce(f"sparse prefill custom b={b} hq={hq} hkv={hkv} t={t} d={d} lists={mode}")
@@ -222,7 +228,7 @@ def test_sparse_prefill_shapes_and_lists(b, hq, hkv, t, d, mode):
     k = torch.randn(b, hkv, t, d, generator=g).to(torch.bfloat16)
     v = torch.randn(b, hkv, t, d, generator=g).to(torch.bfloat16)
     nqb = (t + 63) // 64
-    max_k = max(1, min(nqb, 6))
+    max_k = nqb if mode == "dense" else max(1, min(nqb, 6))
     idx, cnt = _random_lists(t + d, b, hq, nqb, max_k, mode)
     scale = 0.2
     o = _run_sparse(q, k, v, torch.from_numpy(idx), torch.from_numpy(cnt), scale)
@@ -247,6 +253,36 @@ def test_sparse_density_one_matches_dense_causal():
     o = _run_sparse(q, k, v, torch.from_numpy(idx), torch.from_numpy(cnt))
     ref = oracle.sparse_attention_ref(q, k, v, idx, cnt, None)
     assert float(np.abs(o.double().numpy() - ref).max()) <= O_TOL
+
+
+@pytest.mark.parametrize("hq,hkv,t,mode", [(32, 8, 4096, "sorted"), (6, 2, 700, "dense"),
+                                           (3, 3, 1000, "invalid")])
+def test_sparse_schedule_work_list(hq, hkv, t, mode):
+    """The work list the schedule leaves in the workspace: column q = b * Hkv + g
+    holds every item of KV group (b, g) exactly once, longest list first."""
+    announce(f"schedule work list hq={hq} hkv={hkv} t={t} lists={mode}")
+    b, d = 1, 64
+    nqb = (t + 63) // 64
+    G = hq // hkv
+    max_k = nqb if mode == "dense" else max(1, min(nqb, 6))
+    idx, cnt = _random_lists(hq * t, b, hq, nqb, max_k, mode)
+    z = torch.zeros(b, hq, t, d, dtype=torch.bfloat16, device="cuda")
+    zk = torch.zeros(b, hkv, t, d, dtype=torch.bfloat16, device="cuda")
+    ws_bytes = seer.sparse_prefill_workspace_size(b, hq, hkv, t)
+    ws = torch.empty(ws_bytes // 4, dtype=torch.int32, device="cuda")
+    seer.seer_sparse_prefill(z, zk, zk, _dev(torch.from_numpy(idx)), _dev(torch.from_numpy(cnt)),
+                             workspace=ws.view(torch.uint8))
+    torch.cuda.synchronize()
+    ng = b * hkv
+    work = ws.cpu().numpy()[: b * hq * nqb].reshape(G * nqb, ng)
+    flat_cnt = np.minimum(np.maximum(cnt.reshape(-1), 0), max_k)
+    for grp in range(ng):
+        bb, gg = divmod(grp, hkv)
+        lo = (bb * hq + gg * G) * nqb
+        col = work[:, grp]
+        assert sorted(col.tolist()) == list(range(lo, lo + G * nqb))
+        costs = flat_cnt[col]
+        assert (np.diff(costs) <= 0).all(), "items must be longest first"
 
 
 # ------------------------------------------------------------------ pooled map
