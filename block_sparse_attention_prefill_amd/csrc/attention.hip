@@ -34,8 +34,12 @@
 //   free.  K fragments are plain 16-byte LDS reads; V^T fragments come from
 //   ds_read_b64_tr_b16, which transposes 4x16 bf16 blocks on the fly into the
 //   key order of P^T's registers.
-// * K and V of a tile are separate pipeline stages: K(j+1) streams in during
-//   softmax and PV of tile j, V(j+1) during QK of tile j+1.
+// * K and V of a tile are separate pipeline stages.  The sparse pass keeps one
+//   LDS slot per workgroup (K(j), then V(j), then K(j+1)): V(j) streams in during
+//   the softmax, and the small footprint lets a CU hold 6 workgroups whose
+//   copies cover each other's waits.  The pooled pass keeps a ring of two K
+//   slots and one V slot per (two-item) workgroup, so K(j+1) streams in during
+//   tile j and V(j+1) during QK of tile j+1.
 // * exp2 with log2(e) folded into the softmax scale; fp32 row statistics; the
 //   reference max is raised lazily (only when a tile exceeds it by 2^8), which
 //   leaves O = acc / l unchanged and skips most accumulator rescales.
@@ -157,6 +161,7 @@ __device__ __forceinline__ void tile_offsets(uint32_t (&off)[Cfg<D>::kLoadsPerTi
 // This wave's share (kLoadsPerTile / NW slabs) of every K or V tile copy.
 template <int D, int NW>
 struct TileIssue {
+  static_assert(Cfg<D>::kKTileBytes <= Cfg<D>::kVTileBytes, "K fits the V slot");
   static_assert(Cfg<D>::kLoadsPerTile % NW == 0, "slabs split evenly over the waves");
   static constexpr int NL = Cfg<D>::kLoadsPerTile / NW;
   uint32_t off[NL];
@@ -481,48 +486,48 @@ __device__ __forceinline__ void kv_loop(RowState<D>& st, const __bf16* __restric
 }
 
 // The sparse pass's loop: one item, its index list walked in list order
-// (entries outside [0, i] skipped), one K and one V slot.  It is the ring loop
-// above at KS = VS = 1 written for a list: the next entry is looked up at the
-// top of each tile, where its index load overlaps the first wait, and nothing
-// before QK depends on it (measured: the ring loop's form costs 1-3 % here).
+// (entries outside [0, i] skipped), and ONE LDS tile slot that holds K(t),
+// then V(t), then K(t+1).  V(t) streams in during the softmax of tile t; K(t+1)
+// is requested after PV(t) and its latency is covered by the other workgroups
+// of the CU: with one 17 KB slot a CU holds 6 workgroups (3 waves per SIMD,
+// the VGPR limit) instead of 4 with separate K and V slots, which measured
+// +5 % on the sparse workloads.  The next list entry is looked up at the top of
+// each tile, where its index load overlaps the first wait.
 template <int D, typename Next, typename Block>
 __device__ __forceinline__ void kv_loop_list(RowState<D>& st, const __bf16* __restrict__ qh,
                                              int q0, const __bf16* __restrict__ kh,
                                              const __bf16* __restrict__ vh, int T, int i, int n,
-                                             Next next, Block block, char* ks, char* vs, int lane,
-                                             int wave, float c) {
-  constexpr int NL = Cfg<D>::kLoadsPerTile / 2;
+                                             Next next, Block block, char* kvs, int lane, int wave,
+                                             float c) {
   int e = next(0);
   if (e >= n) {
     load_q<D>(st, qh, q0, T, lane, wave);
     return;
   }
   TileIssue<D, 2> io;
-  io.init(ks, vs, wave, lane);
+  io.init(kvs, kvs, wave, lane);
   int j = block(e);
   io.template issue<false>(kh + (size_t)kBlk * j * D, T - kBlk * j, wave, lane, 0);
-  io.template issue<true>(vh + (size_t)kBlk * j * D, T - kBlk * j, wave, lane, 0);
   load_q<D>(st, qh, q0, T, lane, wave);
-  wait_vmcnt<0>();
   while (true) {
     const int cur = j;
     e = next(e + 1);
     const bool more = e < n;
     if (more) j = block(e);
 
-    wait_vmcnt<NL>();  // K(cur) has landed; V(cur) may still be in flight
+    wait_vmcnt<0>();  // K(cur) has landed
     wg_barrier();
     f32x16 s[2];
-    qk_tile<D>(st, ks, lane, wave, cur == i, s);
+    qk_tile<D>(st, kvs, lane, wave, cur == i, s);
     wg_barrier_reads_done();  // every wave is done reading K(cur)
-    if (more) io.template issue<false>(kh + (size_t)kBlk * j * D, T - kBlk * j, wave, lane, 0);
+    io.template issue<true>(vh + (size_t)kBlk * cur * D, T - kBlk * cur, wave, lane, 0);
     (void)softmax_tile<D, false>(st, s, c);
-    if (more) wait_vmcnt<NL>(); else wait_vmcnt<0>();  // V(cur) has landed
+    wait_vmcnt<0>();  // V(cur) has landed
     wg_barrier();
-    pv_tile<D, false>(st, s, vs, lane);
+    pv_tile<D, false>(st, s, kvs, lane);
     wg_barrier_reads_done();  // every wave is done reading V(cur)
     if (!more) break;
-    io.template issue<true>(vh + (size_t)kBlk * j * D, T - kBlk * j, wave, lane, 0);
+    io.template issue<false>(kh + (size_t)kBlk * j * D, T - kBlk * j, wave, lane, 0);
   }
 }
 
@@ -537,13 +542,13 @@ __device__ __forceinline__ void kv_loop_list(RowState<D>& st, const __bf16* __re
 // dense lists (break-even near 0.62), while sparse rows of different heads
 // overlap far less.
 template <int D>
-__global__ __launch_bounds__(kPairThreads, 2) void sparse_prefill_kernel(
+__global__ __launch_bounds__(kPairThreads, 3) void sparse_prefill_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     int Hq, int Hkv, int T, int nqb, float c, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ cnt, int max_k, const int32_t* __restrict__ work,
     __bf16* __restrict__ o) {
-  __shared__ __attribute__((aligned(1024))) char ks[Cfg<D>::kKTileBytes];
-  __shared__ __attribute__((aligned(1024))) char vs[Cfg<D>::kVTileBytes];
+  // One slot for K and V in turn (K uses the first kKTileBytes of it).
+  __shared__ __attribute__((aligned(1024))) char kvs[Cfg<D>::kVTileBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -568,7 +573,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void sparse_prefill_kernel(
     return e;
   };
   auto block = [&](int e) { return lst[e]; };
-  kv_loop_list<D>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, n, next, block, ks, vs,
+  kv_loop_list<D>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, n, next, block, kvs,
                   lane, wave, c);
   (void)store_o<D>(st, o + q_off, kBlk * i, T, lane, wave);
 }
