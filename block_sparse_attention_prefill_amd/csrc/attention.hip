@@ -485,55 +485,32 @@ __device__ __forceinline__ void kv_loop(RowState<D>& st, const __bf16* __restric
   }
 }
 
-// The sparse pass's loop: one item, its index list walked in list order
-// (entries outside [0, i] skipped), and ONE LDS tile slot that holds K(t),
-// then V(t), then K(t+1).  V(t) streams in during the softmax of tile t; K(t+1)
-// is requested after PV(t) and its latency is covered by the other workgroups
-// of the CU: with one 17 KB slot a CU holds 6 workgroups (3 waves per SIMD,
-// the VGPR limit) instead of 4 with separate K and V slots, which measured
-// +5 % on the sparse workloads.  The next list entry is looked up at the top of
-// each tile, where its index load overlaps the first wait.
-template <int D, typename Next, typename Block>
-__device__ __forceinline__ void kv_loop_list(RowState<D>& st, const __bf16* __restrict__ qh,
-                                             int q0, const __bf16* __restrict__ kh,
-                                             const __bf16* __restrict__ vh, int T, int i, int n,
-                                             Next next, Block block, char* kvs, int lane, int wave,
-                                             float c) {
-  int e = next(0);
-  if (e >= n) {
-    load_q<D>(st, qh, q0, T, lane, wave);
-    return;
-  }
-  TileIssue<D, 2> io;
-  io.init(kvs, kvs, wave, lane);
-  int j = block(e);
-  io.template issue<false>(kh + (size_t)kBlk * j * D, T - kBlk * j, wave, lane, 0);
-  load_q<D>(st, qh, q0, T, lane, wave);
-  while (true) {
-    const int cur = j;
-    e = next(e + 1);
-    const bool more = e < n;
-    if (more) j = block(e);
-
-    wait_vmcnt<0>();  // K(cur) has landed
-    wg_barrier();
-    f32x16 s[2];
-    qk_tile<D>(st, kvs, lane, wave, cur == i, s);
-    wg_barrier_reads_done();  // every wave is done reading K(cur)
-    io.template issue<true>(vh + (size_t)kBlk * cur * D, T - kBlk * cur, wave, lane, 0);
-    (void)softmax_tile<D, false>(st, s, c);
-    wait_vmcnt<0>();  // V(cur) has landed
-    wg_barrier();
-    pv_tile<D, false>(st, s, kvs, lane);
-    wg_barrier_reads_done();  // every wave is done reading V(cur)
-    if (!more) break;
-    io.template issue<false>(kh + (size_t)kBlk * j * D, T - kBlk * j, wave, lane, 0);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Sparse prefill: one workgroup (one wave pair) per work-list entry, an entry
 // being an item (b, h, i).
+//
+// Copies move in "parts": part p of a tile is its 64 keys x head-dims
+// 64p..64p+63 of K or of V (8 KB; a D = 128 tile has two K parts and two V
+// parts, a D = 64 tile one of each).  A tile is consumed part by part in the
+// order K0 [K1] V0 [V1], and the parts of consecutive tiles form one stream
+// that cycles through a ring of three LDS part slots: in step u (consuming
+// stream part u) part u + 2 is requested into the slot part u - 1 vacated, so
+// up to two parts are in flight while one is computed on.  One barrier per
+// step serves both purposes: every wave has finished reading part u - 1 and
+// has seen its own copies of part u land.  Three 8.5 KB slots let a CU hold 6
+// workgroups (3 waves per SIMD, the VGPR limit).
+//
+// Within a step the copy is requested only after the step's LDS reads have
+// been issued.  Requesting it first (copy, then LDS reads of another slot,
+// with no s_waitcnt or barrier between them) returned corrupted K or V data
+// now and then on MI355X: a few outputs per million moved by up to 0.004 and
+// repeated runs differed.  With reads first, repeated runs are bit-identical
+// (the GPU tests check this), and every other copy in this file is likewise
+// separated from later LDS reads by a wait and a barrier.
+//
+// The contraction order is that of the whole-tile kernel (S^T accumulates
+// k-steps 0..D/16-1 in order, O^T accumulates key steps 0..3 in order), so
+// splitting a tile into parts does not change a single bit of the result.
 //
 // Pairing two heads of a KV group in one workgroup (as the pooled pass does)
 // does not pay here: a pair walks the union of its two lists and the wave pair
@@ -541,14 +518,275 @@ __device__ __forceinline__ void kv_loop_list(RowState<D>& st, const __bf16* __re
 // a union of 0.73 of the summed list lengths and wins 18 % only for identical
 // dense lists (break-even near 0.62), while sparse rows of different heads
 // overlap far less.
+constexpr int kPartD = 64;                  // head-dims per part
+constexpr int kPartRowBytes = 2 * kPartD;   // 128 B of one row in a part
+constexpr int kPartSlabs = 8;               // 1 KB wave-wide copies per part
+constexpr int kPartCopiesPerWave = kPartSlabs / 2;
+// Slab n of a part holds rows n, n + 8, ..., n + 56 (each 128-byte row segment
+// whole).  Slab strides keep the fragment reads conflict-free: K reads 16 rows
+// at one 16-byte chunk (stride = 1 KB + 16 B: rows step by one 16-byte bank
+// group), V transpose reads 4 rows x 64 B (stride = 1 KB + 64 B: rows step by
+// 16 banks).  A slot fits either kind.
+constexpr int kPartKSlab = 1024 + 16;
+constexpr int kPartVSlab = 1024 + 64;
+constexpr int kPartSlotBytes = kPartSlabs * kPartVSlab;
+constexpr int kPartSlots = 3;
+
+template <bool IS_V>
+__device__ __forceinline__ int part_byte(int row, int chunk) {
+  return (row % kPartSlabs) * (IS_V ? kPartVSlab : kPartKSlab) +
+         (row / kPartSlabs) * kPartRowBytes + 16 * chunk;
+}
+
+// This wave's four copies of a part: copy n of wave w fills slab 4w + n; its
+// lane L moves 16-byte chunk L % 8 of row (4w + n) + 8 (L / 8).  Rows at or
+// past `nvalid` (short last block) re-read the last valid row; those keys are
+// always causally masked.
+template <int D>
+struct PartIssue {
+  uint32_t off[kPartCopiesPerWave];  // per-lane byte offset of a full tile's part 0
+  uint32_t lds0;                     // LDS byte address of the ring
+  int wave, lane;
+  __device__ __forceinline__ void offsets(uint32_t (&o)[kPartCopiesPerWave], int nvalid) const {
+#pragma unroll
+    for (int n = 0; n < kPartCopiesPerWave; ++n) {
+      const int row = (kPartCopiesPerWave * wave + n) + kPartSlabs * (lane >> 3);
+      const int grow = row < nvalid ? row : nvalid - 1;
+      o[n] = (uint32_t)((grow * D + (lane & 7) * 8) * 2);
+    }
+  }
+  __device__ __forceinline__ void init(const char* ring, int w, int l) {
+    wave = w;
+    lane = l;
+    offsets(off, kBlk);
+    lds0 = lds_u32(ring);
+  }
+  // Copy part `p` of the K or V tile whose first row is `g` into ring slot `slot`.
+  template <bool IS_V>
+  __device__ __forceinline__ void issue(const __bf16* g, int nvalid, int p, int slot) const {
+    const uint64_t sb = uniform_u64(g + kPartD * p);
+    constexpr uint32_t stride = IS_V ? kPartVSlab : kPartKSlab;
+    const uint32_t lb = lds0 + slot * kPartSlotBytes + kPartCopiesPerWave * wave * stride;
+    if (nvalid >= kBlk) {
+#pragma unroll
+      for (int n = 0; n < kPartCopiesPerWave; ++n) dma16(sb, off[n], lb + n * stride);
+    } else {
+      uint32_t o[kPartCopiesPerWave];
+      offsets(o, nvalid);
+#pragma unroll
+      for (int n = 0; n < kPartCopiesPerWave; ++n) dma16(sb, o[n], lb + n * stride);
+    }
+  }
+};
+
+// Step barrier: this wave's copies other than the newest N have landed and
+// its LDS reads have returned; then every wave of the workgroup meets.
+template <int N>
+__device__ __forceinline__ void step_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+// S^T += K_p Q_p^T for K part p (k-steps 4p..4p+3) of the tile in `ks`.
+template <int D>
+__device__ __forceinline__ void qk_part(const RowState<D>& st, const char* ks, int lane, int p,
+                                        f32x16 (&s)[2]) {
+  const int col = lane & 31;
+  const int half = lane >> 5;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const char* krow = ks + part_byte<false>(32 * tt + col, half);
+    bf16x8 kf[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(krow + 32 * t);
+    f32x16 a = p == 0 ? f32x16{} : s[tt];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], st.qf[4 * p + t], a, 0, 0, 0);
+    s[tt] = a;
+  }
+}
+
+__device__ __forceinline__ void mask_diag(f32x16 (&s)[2], int lane, int wave) {
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int qrow = 32 * wave + col;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kv = 32 * tt + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (kv > qrow) s[tt][r] = -INFINITY;
+    }
+}
+
+// P^T as the bf16 B operands of the four 16-key steps, and its row sum (the
+// sum of exactly the bf16 weights the MFMA uses) added to l.
+template <int D>
+__device__ __forceinline__ void p_operands(RowState<D>& st, const f32x16 (&s)[2],
+                                           bf16x8 (&pb)[4]) {
+  typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float lsum = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const f32x16& src = s[kk >> 1];
+    const int o = 8 * (kk & 1);
+    const f32x8 pv = {src[o + 0], src[o + 1], src[o + 2], src[o + 3],
+                      src[o + 4], src[o + 5], src[o + 6], src[o + 7]};
+    pb[kk] = __builtin_convertvector(pv, bf16x8);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bf16x2 pair = {pb[kk][2 * u], pb[kk][2 * u + 1]};
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum, false);
+    }
+  }
+  st.l += lsum;
+}
+
+// O^T[d-tiles 2p, 2p+1] += V_p^T P^T for V part p of the tile in `vs`.
+template <int D>
+__device__ __forceinline__ void pv_part(RowState<D>& st, const bf16x8 (&pb)[4], const char* vs,
+                                        int lane, int p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const int g = lane >> 4;
+  const int i = lane & 15;
+  const int h = g >> 1;
+  const int r = i >> 2;
+  const int sub = 4 * (i & 1);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int kv_a = 16 * kk + 4 * h + r;
+    const int kv_b = kv_a + 8;
+    const char* va_row = vs + part_byte<true>(kv_a, 2 * (g & 1) + ((i & 3) >> 1)) + 2 * sub;
+    const char* vb_row = vs + part_byte<true>(kv_b, 2 * (g & 1) + ((i & 3) >> 1)) + 2 * sub;
+    s16x4 va[2], vb[2];
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      va[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(va_row + 64 * dt));
+      vb[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vb_row + 64 * dt));
+    }
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      const s16x8 vv = {va[dt][0], va[dt][1], va[dt][2], va[dt][3],
+                        vb[dt][0], vb[dt][1], vb[dt][2], vb[dt][3]};
+      st.acc[2 * p + dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, vv), pb[kk], st.acc[2 * p + dt], 0, 0, 0);
+    }
+  }
+}
+
+// The sparse pass's loop over one item's list (entries outside [0, i] are
+// skipped; `next(e)` is the first usable list position >= e, `block(e)` its
+// KV block).  The last step reads its slot after the final barrier, so the
+// ring must not be reused without another barrier (the kernel ends here).
+template <int D, typename Next, typename Block>
+__device__ __forceinline__ void kv_loop_parts(RowState<D>& st, const __bf16* __restrict__ qh,
+                                              int q0, const __bf16* __restrict__ kh,
+                                              const __bf16* __restrict__ vh, int T, int i, int n,
+                                              Next next, Block block, char* ring, int lane,
+                                              int wave, float c) {
+  constexpr int NP = D / kPartD;           // K (and V) parts per tile
+  constexpr int NL = kPartCopiesPerWave;   // this wave's copies per part
+  int e = next(0);
+  if (e >= n) {
+    load_q<D>(st, qh, q0, T, lane, wave);
+    return;
+  }
+  PartIssue<D> io;
+  io.init(ring, wave, lane);
+  int j = block(e);
+  // Stream parts 0 and 1: K0, K1 for D = 128; K, V for D = 64.
+  io.template issue<false>(kh + (size_t)kBlk * j * D, T - kBlk * j, 0, 0);
+  if (NP == 2)
+    io.template issue<false>(kh + (size_t)kBlk * j * D, T - kBlk * j, 1, 1);
+  else
+    io.template issue<true>(vh + (size_t)kBlk * j * D, T - kBlk * j, 0, 1);
+  load_q<D>(st, qh, q0, T, lane, wave);
+  wait_vmcnt<0>();
+  int slot0 = 0;  // ring slot of the current tile's first part
+  auto slot = [&](int p) {  // ring slot of stream part (current tile, p), p <= 5
+    return (slot0 + p) % kPartSlots;
+  };
+  while (true) {
+    const int cur = j;
+    const __bf16* kc = kh + (size_t)kBlk * cur * D;
+    const __bf16* vc = vh + (size_t)kBlk * cur * D;
+    const int nc = T - kBlk * cur;
+    bool more;
+    f32x16 s[2];
+    bf16x8 pb[4];
+    if constexpr (NP == 2) {
+      // Step K0: parts K0 (landing), K1 in flight; request V0.
+      step_barrier<NL>();
+      // The next list entry is needed from step V0 on: its scalar load
+      // overlaps the QK below instead of stalling a step barrier.
+      e = next(e + 1);
+      more = e < n;
+      if (more) j = block(e);
+      qk_part<D>(st, ring + slot(0) * kPartSlotBytes, lane, 0, s);
+      io.template issue<true>(vc, nc, 0, slot(2));
+      // Step K1: K1 landing, V0 in flight; request V1.
+      step_barrier<NL>();
+      qk_part<D>(st, ring + slot(1) * kPartSlotBytes, lane, 1, s);
+      io.template issue<true>(vc, nc, 1, slot(3));
+      if (cur == i) {  // wave-uniform; the fence keeps it a branch
+        compiler_fence();
+        mask_diag(s, lane, wave);
+      }
+      (void)softmax_tile<D, false>(st, s, c);
+      p_operands<D>(st, s, pb);
+      const __bf16* kn = kh + (size_t)kBlk * j * D;
+      const int nn = T - kBlk * j;
+      // Step V0: V0 landing, V1 in flight; request K0 of the next tile.
+      step_barrier<NL>();
+      pv_part<D>(st, pb, ring + slot(2) * kPartSlotBytes, lane, 0);
+      if (more) io.template issue<false>(kn, nn, 0, slot(4));
+      // Step V1: V1 landing, K0' in flight if any; request K1'.
+      if (more) step_barrier<NL>(); else step_barrier<0>();
+      pv_part<D>(st, pb, ring + slot(3) * kPartSlotBytes, lane, 1);
+      if (more) io.template issue<false>(kn, nn, 1, slot(5));
+      slot0 = slot(4);
+    } else {
+      e = next(e + 1);
+      more = e < n;
+      if (more) j = block(e);
+      const __bf16* kn = kh + (size_t)kBlk * j * D;
+      const __bf16* vn = vh + (size_t)kBlk * j * D;
+      const int nn = T - kBlk * j;
+      // Step K: K landing, V in flight; request K of the next tile.
+      step_barrier<NL>();
+      qk_part<D>(st, ring + slot(0) * kPartSlotBytes, lane, 0, s);
+      if (more) io.template issue<false>(kn, nn, 0, slot(2));
+      if (cur == i) {
+        compiler_fence();
+        mask_diag(s, lane, wave);
+      }
+      (void)softmax_tile<D, false>(st, s, c);
+      p_operands<D>(st, s, pb);
+      // Step V: V landing, K' in flight if any; request V'.
+      if (more) step_barrier<NL>(); else step_barrier<0>();
+      pv_part<D>(st, pb, ring + slot(1) * kPartSlotBytes, lane, 0);
+      if (more) io.template issue<true>(vn, nn, 0, slot(3));
+      slot0 = slot(2);
+    }
+    if (!more) break;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kPairThreads, 3) void sparse_prefill_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     int Hq, int Hkv, int T, int nqb, float c, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ cnt, int max_k, const int32_t* __restrict__ work,
     __bf16* __restrict__ o) {
-  // One slot for K and V in turn (K uses the first kKTileBytes of it).
-  __shared__ __attribute__((aligned(1024))) char kvs[Cfg<D>::kVTileBytes];
+  __shared__ __attribute__((aligned(1024))) char ring[kPartSlots * kPartSlotBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -573,8 +811,8 @@ __global__ __launch_bounds__(kPairThreads, 3) void sparse_prefill_kernel(
     return e;
   };
   auto block = [&](int e) { return lst[e]; };
-  kv_loop_list<D>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, n, next, block, kvs,
-                  lane, wave, c);
+  kv_loop_parts<D>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, n, next, block, ring,
+                   lane, wave, c);
   (void)store_o<D>(st, o + q_off, kBlk * i, T, lane, wave);
 }
 
