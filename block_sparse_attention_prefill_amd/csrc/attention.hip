@@ -182,6 +182,7 @@ struct TileIssue {
 #pragma unroll
       for (int n = 0; n < NL; ++n) dma16(sb, off[n], lb + n * stride);
     } else {
+      compiler_fence();  // a real branch: the short-tile offsets stay off the common path
       uint32_t o[NL];
       tile_offsets<D, NW>(o, nvalid, wave, lane);
 #pragma unroll
@@ -242,6 +243,17 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
+// This lane's value and that of lane ^ 32 (the other row half of the same
+// query row), via v_permlane32_swap: one VALU op instead of an LDS permute.
+struct HalfPair {
+  float mine, other;
+};
+__device__ __forceinline__ HalfPair half_pair(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 // Online softmax update on S^T (in place -> P), returns the raw row max.
 // EXACT_L: accumulate l from the fp32 probabilities here (the pooled map needs
 // l to fp32 accuracy); otherwise pv_tile sums the bf16 probabilities it feeds
@@ -256,7 +268,8 @@ __device__ __forceinline__ float softmax_tile(RowState<D>& st, f32x16 (&s)[2], f
     m1 = max3f(m1, s[1][r], s[1][r + 1]);
   }
   float mx = max3f(m0, m1, max3f(s[0][15], s[1][15], -INFINITY));
-  mx = max3f(mx, __shfl_xor(mx, 32, 64), -INFINITY);
+  const HalfPair hp = half_pair(mx);
+  mx = max3f(hp.mine, hp.other, -INFINITY);
 
   const float cand = mx * c;
   const bool raise = cand > st.m + kRescaleSlack;
@@ -360,7 +373,8 @@ __device__ __forceinline__ void load_q(RowState<D>& st, const __bf16* __restrict
 template <int D>
 __device__ __forceinline__ float store_o(const RowState<D>& st, __bf16* __restrict__ oh, int q0,
                                          int T, int lane, int rw) {
-  const float l = st.l + __shfl_xor(st.l, 32, 64);
+  const HalfPair hl = half_pair(st.l);
+  const float l = hl.mine + hl.other;
   const float inv = (l > 0.f) ? 1.0f / l : 0.f;
   const int row = q0 + 32 * rw + (lane & 31);
   const int half = lane >> 5;
@@ -571,6 +585,7 @@ struct PartIssue {
 #pragma unroll
       for (int n = 0; n < kPartCopiesPerWave; ++n) dma16(sb, off[n], lb + n * stride);
     } else {
+      compiler_fence();  // a real branch: the short-tile offsets stay off the common path
       uint32_t o[kPartCopiesPerWave];
       offsets(o, nvalid);
 #pragma unroll
