@@ -18,6 +18,11 @@ What it computes, each function citing the passage it follows:
                  (reproducibility summary of "SeerAttention: Self-distilled
                  Attention Gating for Efficient Long-context Prefilling",
                  Pseudocode row, Figure 8).
+* ``target``  -- the row-normalised map used as the gate's ground truth and the
+                 MSE against gate scores (rebuttal "SeerAttention: Learning
+                 Intrinsic Sparse Attention in Your LLMs", "Question 2:
+                 (Row-Normalization of Max-Pooled Attention Map)" and "Question
+                 2 (Currently use MSE loss, how about e2e LM loss?)").
 
 Everything is evaluated in float64 on the exact input values (bf16 inputs are
 widened exactly).  The pins that tie these definitions to something other than
@@ -29,10 +34,11 @@ from .mask import (MODE_THRESHOLD, MODE_TOPK, forced_blocks, topk_count, select_
 from .attention import (BLOCK, block_probs, allowed_blocks, sparse_attention_ref,
                         sparse_attention_blocks_ref)
 from .pooled import pooled_map_ref, pooled_map_blocks_ref
+from .target import pooled_target_ref
 
 __all__ = [
     "MODE_THRESHOLD", "MODE_TOPK", "BLOCK", "forced_blocks", "topk_count", "select_row",
     "build_mask_ref", "mask_rows_ref", "block_probs", "allowed_blocks",
     "sparse_attention_ref", "sparse_attention_blocks_ref", "pooled_map_ref",
-    "pooled_map_blocks_ref",
+    "pooled_map_blocks_ref", "pooled_target_ref",
 ]
