@@ -24,7 +24,7 @@ BLOCK = 64
 EXPORTED = (
     "seer_status_string", "seer_version", "seer_topk_budget", "seer_build_mask",
     "seer_sparse_prefill_workspace_size", "seer_sparse_prefill",
-    "seer_pooled_attn_map_workspace_size", "seer_pooled_attn_map",
+    "seer_pooled_attn_map_workspace_size", "seer_pooled_attn_map", "seer_pooled_target_mse",
 )
 
 _lib = None
@@ -68,6 +68,9 @@ def load() -> ctypes.CDLL:
     lib.seer_pooled_attn_map.restype = c_int
     lib.seer_pooled_attn_map.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int,
                                          c_float, c_void, c_void, c_void, c_size, c_void]
+    lib.seer_pooled_target_mse.restype = c_int
+    lib.seer_pooled_target_mse.argtypes = [c_void, c_void, c_int, c_int, c_int, c_void, c_void,
+                                           c_void, c_void]
     _lib = lib
     return lib
 
@@ -194,3 +197,32 @@ def seer_pooled_attn_map(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _ptr(q), _ptr(k), _ptr(v), b, hq, hkv, t, d, scale, _ptr(out), _ptr(amap),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, amap
+
+
+def seer_pooled_target_mse(amap: torch.Tensor, gate: Optional[torch.Tensor] = None,
+                           target: Optional[torch.Tensor] = None, row_sse: Optional[torch.Tensor] = None,
+                           loss: Optional[torch.Tensor] = None, stream=None):
+    """amap fp32 [B,H,nQB,nQB] -> (target, row_sse, loss); the last two are None without gate.
+
+    target may be amap itself (normalised in place)."""
+    lib = load()
+    b, h, nqb, nkb = amap.shape
+    _need(amap, "amap", torch.float32, (b, h, nqb, nqb))
+    if gate is not None:
+        _need(gate, "gate", torch.float32, (b, h, nqb, nqb))
+    if target is None:
+        target = torch.empty_like(amap)
+    _need(target, "target", torch.float32, (b, h, nqb, nqb))
+    if gate is not None:
+        if row_sse is None:
+            row_sse = torch.empty((b, h, nqb), dtype=torch.float32, device=amap.device)
+        if loss is None:
+            loss = torch.empty((1,), dtype=torch.float32, device=amap.device)
+        _need(row_sse, "row_sse", torch.float32, (b, h, nqb))
+        _need(loss, "loss", torch.float32, (1,))
+    else:
+        row_sse = loss = None
+    _check("seer_pooled_target_mse", lib.seer_pooled_target_mse(
+        _ptr(amap), _ptr(gate), b, h, nqb, _ptr(target), _ptr(row_sse), _ptr(loss),
+        _stream(stream)))
+    return target, row_sse, loss

@@ -137,4 +137,17 @@ int seer_pooled_attn_map(const void* q, const void* k, const void* v, int B, int
   return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
 }
 
+int seer_pooled_target_mse(const float* amap, const float* gate, int B, int H, int nQB,
+                           float* target, float* row_sse, float* loss, void* stream) {
+  if (B < 0 || H < 0 || nQB < 0) return SEER_ERR_INVALID_ARG;
+  if (!items_fit(B, H, nQB)) return SEER_ERR_UNSUPPORTED;
+  if ((long long)B * H * nQB == 0) return SEER_OK;
+  if (!amap || !target) return SEER_ERR_INVALID_ARG;
+  if (loss && (!gate || !row_sse)) return SEER_ERR_INVALID_ARG;
+  const hipError_t err = seer::launch_pooled_target(amap, gate, B, H, nQB, target,
+                                                    gate ? row_sse : nullptr, gate ? loss : nullptr,
+                                                    (hipStream_t)stream);
+  return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
+}
+
 }  // extern "C"

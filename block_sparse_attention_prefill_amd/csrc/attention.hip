@@ -182,7 +182,9 @@ struct TileIssue {
 #pragma unroll
       for (int n = 0; n < NL; ++n) dma16(sb, off[n], lb + n * stride);
     } else {
-      compiler_fence();  // a real branch: the short-tile offsets stay off the common path
+      // nvalid "redefined" here, so the clamped offsets cannot be computed
+      // ahead of the branch: they stay off the common (full-tile) path.
+      asm volatile("" : "+s"(nvalid));
       uint32_t o[NL];
       tile_offsets<D, NW>(o, nvalid, wave, lane);
 #pragma unroll
@@ -585,7 +587,9 @@ struct PartIssue {
 #pragma unroll
       for (int n = 0; n < kPartCopiesPerWave; ++n) dma16(sb, off[n], lb + n * stride);
     } else {
-      compiler_fence();  // a real branch: the short-tile offsets stay off the common path
+      // nvalid "redefined" here, so the clamped offsets cannot be computed
+      // ahead of the branch: they stay off the common (full-tile) path.
+      asm volatile("" : "+s"(nvalid));
       uint32_t o[kPartCopiesPerWave];
       offsets(o, nvalid);
 #pragma unroll

@@ -33,4 +33,7 @@ hipError_t launch_pooled_map(const void* q, const void* k, const void* v, int B,
                              int Hkv, int T, int D, float sm_scale, void* o, float* amap,
                              float* rowmax_ws, hipStream_t stream);
 
+hipError_t launch_pooled_target(const float* amap, const float* gate, int B, int H, int nqb,
+                                float* target, float* row_sse, float* loss, hipStream_t stream);
+
 }  // namespace seer

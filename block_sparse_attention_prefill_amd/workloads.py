@@ -18,7 +18,7 @@ dataset, prompt or trained weight is used: every value is drawn from a seeded
 NumPy PCG64 generator.
 
 Seeds: ``seed = 1000 * workload_id + stream`` with stream 0 = Q, 1 = K, 2 = V,
-3 = scores, 4 = stripe columns, 5 = sampled query blocks.
+3 = scores, 4 = stripe columns, 5 = sampled query blocks, 6 = block maps.
 """
 
 from __future__ import annotations
@@ -159,6 +159,18 @@ def make_scores(w: Workload) -> torch.Tensor:
     s = np.ascontiguousarray(s, dtype=np.float32)
     s = np.where(np.tril(np.ones((n, n), dtype=bool)), s, np.float32(0.0)).astype(np.float32)
     return torch.from_numpy(np.ascontiguousarray(s))
+
+
+def make_block_map(w: Workload, seed_stream: int = 6) -> torch.Tensor:
+    """A stand-in for a max-pooled block map [B,Hq,nQB,nQB] fp32: U(0,1) on the
+    causal entries j <= i (shifted away from 0) and large junk values above the
+    diagonal, which consumers of such a map must never read."""
+    n = w.nqb
+    rng = np.random.Generator(np.random.PCG64(w.seed(seed_stream)))
+    a = rng.random(size=(w.batch, w.hq, n, n), dtype=np.float32) + np.float32(1e-3)
+    junk = np.float32(1e6) * (np.float32(1.0) + rng.random(size=a.shape, dtype=np.float32))
+    causal = np.tril(np.ones((n, n), dtype=bool))
+    return torch.from_numpy(np.ascontiguousarray(np.where(causal, a, junk).astype(np.float32)))
 
 
 def sample_qblocks(w: Workload, count: Optional[int] = None) -> np.ndarray:

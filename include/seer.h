@@ -155,6 +155,31 @@ int seer_pooled_attn_map(const void* q, const void* k, const void* v, int B, int
                          int T, int D, float sm_scale, void* o, float* amap, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/*
+ * Row-normalised distillation target and its MSE against gate scores.  The
+ * max-pooled map is normalised per row so that, like the gate's softmax
+ * output, each row sums to 1 (rebuttal "SeerAttention: Learning Intrinsic
+ * Sparse Attention in Your LLMs", "Question 2: (Row-Normalization of
+ * Max-Pooled Attention Map)"); the gate learns it with an MSE loss (same
+ * rebuttal, "Question 2 (Currently use MSE loss, how about e2e LM loss?)").
+ *
+ * amap    device fp32 [B, H, nQB, nQB], e.g. from seer_pooled_attn_map; only
+ *         entries j <= i are read.
+ * gate    device fp32 [B, H, nQB, nQB] gate scores, or NULL (target only);
+ *         only entries j <= i are read.
+ * target  device fp32 out [B, H, nQB, nQB]: amap[b,h,i,j] / sum_{j'<=i}
+ *         amap[b,h,i,j'] for j <= i (0 if that sum is 0), 0 for j > i.  May be
+ *         the same buffer as amap (normalised in place).
+ * row_sse device fp32 out [B, H, nQB] or NULL: sum over j <= i of
+ *         (gate - target)^2.  Written only when gate is given.
+ * loss    device fp32 out [1] or NULL: the mean of (gate - target)^2 over all
+ *         B * H * nQB * (nQB + 1) / 2 causal entries, summed in a fixed order.
+ *         Requires gate and row_sse (else SEER_ERR_INVALID_ARG).
+ * Sums are fp32 per row (fixed order, bit-reproducible) and fp64 for the loss.
+ */
+int seer_pooled_target_mse(const float* amap, const float* gate, int B, int H, int nQB,
+                           float* target, float* row_sse, float* loss, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

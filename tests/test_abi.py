@@ -112,3 +112,15 @@ def test_pooled_map_rejects_on_host():
     assert lib.seer_pooled_attn_map(*no_map) == 1
     small_ws = ok[:12] + (64,) + ok[13:]
     assert lib.seer_pooled_attn_map(*small_ws) == 4
+
+
+def test_pooled_target_rejects_on_host():
+    lib = seer.load()
+    ok = (FAKE, FAKE, 1, 2, 8, FAKE, FAKE, FAKE, None)
+    assert lib.seer_pooled_target_mse(*((None,) + ok[1:])) == 1          # no map
+    assert lib.seer_pooled_target_mse(*(ok[:5] + (None,) + ok[6:])) == 1  # no target
+    assert lib.seer_pooled_target_mse(*(ok[:1] + (None,) + ok[2:])) == 1  # loss without gate
+    assert lib.seer_pooled_target_mse(*(ok[:6] + (None,) + ok[7:])) == 1  # loss without row_sse
+    assert lib.seer_pooled_target_mse(FAKE, FAKE, -1, 2, 8, FAKE, FAKE, FAKE, None) == 1
+    assert lib.seer_pooled_target_mse(FAKE, FAKE, 0, 2, 8, FAKE, FAKE, FAKE, None) == 0  # empty
+

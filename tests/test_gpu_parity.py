@@ -394,3 +394,62 @@ def test_pooled_map_qwen_32k_sampled():
     assert (an[..., tri] > 0).all() and (an[..., tri] <= 1 + 1e-6).all()
     assert (an[..., ~tri] == 0).all()
     assert np.abs(an[:, :, 0, 0] - 1).max() <= 1e-6
+
+
+# ------------------------------------------------------------------ distillation target
+
+T_TOL = 1e-5      # target: fp32 row sums of <= 4096 terms in [0, 1], relative error << 1e-5
+SSE_RTOL = 1e-4   # per-row squared error (fp32 sums of <= 4096 terms)
+LOSS_RTOL = 1e-5  # loss: fp64 sum of the row errors
+
+
+@pytest.mark.parametrize("b,h,nqb", [(1, 2, 8), (2, 3, 13), (1, 40, 512)])
+def test_pooled_target_random_maps(b, h, nqb):
+    announce(f"pooled target b={b} h={h} nqb={nqb}")
+    w = wl.custom(40 + nqb, b, h, 1, 64, 64 * nqb, scores="softmax_normal")
+    amap = wl.make_block_map(w)
+    gate = wl.make_scores(w)
+    t, r, l = seer.seer_pooled_target_mse(_dev(amap), _dev(gate))
+    torch.cuda.synchronize()
+    rt, rr, rl = oracle.pooled_target_ref(amap.numpy(), gate.numpy())
+    assert float(np.abs(t.cpu().double().numpy() - rt).max()) <= T_TOL
+    assert np.allclose(r.cpu().double().numpy(), rr, rtol=SSE_RTOL, atol=1e-12)
+    assert abs(float(l.cpu()) - rl) <= LOSS_RTOL * rl
+
+
+def test_pooled_target_in_place_and_without_gate():
+    w = wl.custom(60, 1, 4, 1, 64, 64 * 37, scores="softmax_normal")
+    amap = wl.make_block_map(w)
+    rt, _, _ = oracle.pooled_target_ref(amap.numpy())
+    a = _dev(amap)
+    t, r, l = seer.seer_pooled_target_mse(a, None, target=a)
+    torch.cuda.synchronize()
+    assert r is None and l is None and t.data_ptr() == a.data_ptr()
+    assert float(np.abs(a.cpu().double().numpy() - rt).max()) <= T_TOL
+
+
+def test_pooled_target_chain_from_pooled_map():
+    """GPU pooled map -> GPU target, against the oracle map -> oracle target."""
+    w = wl.C1
+    q, k, v = wl.make_qkv(w)
+    _, amap = seer.seer_pooled_attn_map(_dev(q), _dev(k), _dev(v))
+    gate = _dev(wl.make_scores(wl.custom(61, 1, w.hq, 1, 64, w.seq, scores="softmax_normal")))
+    t, r, l = seer.seer_pooled_target_mse(amap, gate)
+    torch.cuda.synchronize()
+    _, ref_map = oracle.pooled_map_ref(q, k, v)
+    rt, rr, rl = oracle.pooled_target_ref(ref_map, gate.cpu().numpy())
+    # the map is within A_TOL of the oracle's; row normalisation can at most
+    # double a relative error, and rows sum to 1, so 2 * A_TOL bounds the target
+    assert float(np.abs(t.cpu().double().numpy() - rt).max()) <= 2 * A_TOL
+    assert abs(float(l.cpu()) - rl) <= 4 * A_TOL
+
+
+def test_pooled_target_repeat_bitexact():
+    w = wl.custom(62, 1, 8, 1, 64, 64 * 300, scores="softmax_normal")
+    amap, gate = _dev(wl.make_block_map(w)), _dev(wl.make_scores(w))
+    t0, r0, l0 = (x.clone() for x in seer.seer_pooled_target_mse(amap, gate))
+    for _ in range(2):
+        t, r, l = seer.seer_pooled_target_mse(amap, gate)
+        torch.cuda.synchronize()
+        assert torch.equal(t, t0) and torch.equal(r, r0) and torch.equal(l, l0)
+
