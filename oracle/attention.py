@@ -1,4 +1,4 @@
-"""Oracle: causal attention restricted to selected 64x64 blocks.  TEST INFRASTRUCTURE ONLY.
+"""Oracle: causal attention restricted to selected blocks (64x64 by default).  TEST INFRASTRUCTURE ONLY.
 
 Source passages:
 * Rebuttal "SeerAttention: Learning Intrinsic Sparse Attention in Your LLMs",
@@ -13,6 +13,10 @@ Source passages:
 * Rebuttal, "Weakness 4 (Rounding Issue when Seq not evenly divided by B)": a
   sequence that is not a multiple of the block is padded; here the last block
   is simply short (positions >= T do not exist).
+* Rebuttal, "Question 3 (Block Size Experiments)": block sizes 32, 64 and 128
+  are evaluated, so the block size is a parameter of the method; the functions
+  take it as ``block`` (default 64), the index lists then counting blocks of
+  that many tokens in both dimensions.
 
 Readings (also in the design notes):
 * Causal alignment with Tq = Tk = T: query position r sees key position c iff
@@ -71,16 +75,18 @@ def allowed_blocks(idx_row, cnt: int, i: int) -> List[int]:
     return sorted({int(j) for j in idx_row[:n] if 0 <= int(j) <= i})
 
 
-def _key_positions(blocks: List[int], seq: int) -> np.ndarray:
+def _key_positions(blocks: List[int], seq: int, block: int = BLOCK) -> np.ndarray:
     if not blocks:
         return np.zeros((0,), dtype=np.int64)
-    return np.concatenate([np.arange(BLOCK * j, min(BLOCK * j + BLOCK, seq)) for j in blocks])
+    return np.concatenate([np.arange(block * j, min(block * j + block, seq)) for j in blocks])
 
 
 def sparse_attention_blocks_ref(q, k, v, idx, cnt, sm_scale: Optional[float],
-                                blocks: Iterable[Tuple[int, int, int]]
+                                blocks: Iterable[Tuple[int, int, int]], block: int = BLOCK
                                 ) -> Dict[Tuple[int, int, int], np.ndarray]:
-    """Output rows of selected query blocks: {(b, h, i): O_i [rows, D] float64}."""
+    """Output rows of selected query blocks: {(b, h, i): O_i [rows, D] float64}.
+
+    i counts blocks of ``block`` tokens, as do the list entries."""
     idx = np.asarray(idx)
     cnt = np.asarray(cnt)
     bsz, hq, seq, d = q.shape
@@ -91,10 +97,10 @@ def sparse_attention_blocks_ref(q, k, v, idx, cnt, sm_scale: Optional[float],
     for (b, h, i) in blocks:
         b, h, i = int(b), int(h), int(i)
         g = h // group
-        r0, r1 = BLOCK * i, min(BLOCK * i + BLOCK, seq)
+        r0, r1 = block * i, min(block * i + block, seq)
         rows = np.arange(r0, r1)
         sel = allowed_blocks(idx[b, h, i], cnt[b, h, i], i)
-        keys = _key_positions(sel, seq)
+        keys = _key_positions(sel, seq, block)
         if keys.size == 0:
             out[(b, h, i)] = np.zeros((r1 - r0, d))
             continue
@@ -103,13 +109,15 @@ def sparse_attention_blocks_ref(q, k, v, idx, cnt, sm_scale: Optional[float],
     return out
 
 
-def sparse_attention_ref(q, k, v, idx, cnt, sm_scale: Optional[float] = None) -> np.ndarray:
-    """Full output O [B,Hq,T,D] float64 of block-sparse causal attention."""
+def sparse_attention_ref(q, k, v, idx, cnt, sm_scale: Optional[float] = None,
+                         block: int = BLOCK) -> np.ndarray:
+    """Full output O [B,Hq,T,D] float64 of block-sparse causal attention with
+    lists of ``block``-token blocks."""
     bsz, hq, seq, d = q.shape
-    nqb = (seq + BLOCK - 1) // BLOCK
+    nqb = (seq + block - 1) // block
     blocks = [(b, h, i) for b in range(bsz) for h in range(hq) for i in range(nqb)]
-    res = sparse_attention_blocks_ref(q, k, v, idx, cnt, sm_scale, blocks)
+    res = sparse_attention_blocks_ref(q, k, v, idx, cnt, sm_scale, blocks, block)
     o = np.zeros((bsz, hq, seq, d))
     for (b, h, i), oi in res.items():
-        o[b, h, BLOCK * i: BLOCK * i + oi.shape[0]] = oi
+        o[b, h, block * i: block * i + oi.shape[0]] = oi
     return o

@@ -42,14 +42,14 @@ def _random_lists(seed, b, h, nqb, max_k, keep_diag=True):
     return idx, cnt
 
 
-def _sdpa_with_blocks(q, k, v, idx, cnt, scale):
+def _sdpa_with_blocks(q, k, v, idx, cnt, scale, block=BLOCK):
     """Library reference: SDPA (float64, CPU) with the block list expanded to a
     boolean mask and intersected with causality; GQA by repeating KV heads."""
     b, hq, t, d = q.shape
     grp = hq // k.shape[1]
     kk = k.double().repeat_interleave(grp, dim=1)
     vv = v.double().repeat_interleave(grp, dim=1)
-    nqb = (t + BLOCK - 1) // BLOCK
+    nqb = (t + block - 1) // block
     allow = torch.zeros(b, hq, t, t, dtype=torch.bool)
     pos = torch.arange(t)
     causal = pos[None, :] <= pos[:, None]
@@ -60,36 +60,36 @@ def _sdpa_with_blocks(q, k, v, idx, cnt, scale):
                 for j in idx[bb, hh, i, : cnt[bb, hh, i]]:
                     if 0 <= j <= i:
                         bm[i, j] = True
-            allow[bb, hh] = bm.repeat_interleave(BLOCK, 0).repeat_interleave(BLOCK, 1)[:t, :t] & causal
+            allow[bb, hh] = bm.repeat_interleave(block, 0).repeat_interleave(block, 1)[:t, :t] & causal
     out = F.scaled_dot_product_attention(q.double(), kk, vv, attn_mask=allow, scale=scale)
     empty = ~allow.any(dim=-1)
     out[empty] = 0.0
     return out.numpy()
 
 
-@pytest.mark.parametrize("t", [200, 256])
-def test_density_one_equals_dense_causal_sdpa(t):
+@pytest.mark.parametrize("t,block", [(200, 64), (256, 64), (300, 128), (256, 128)])
+def test_density_one_equals_dense_causal_sdpa(t, block):
     b, hq, hkv, d = 1, 4, 2, 64
     q, k, v = _inputs(1, b, hq, hkv, t, d)
-    nqb = (t + BLOCK - 1) // BLOCK
+    nqb = (t + block - 1) // block
     idx = np.tile(np.arange(nqb, dtype=np.int32), (b, hq, nqb, 1))
     cnt = np.tile(np.arange(1, nqb + 1, dtype=np.int32), (b, hq, 1))
-    o = oracle.sparse_attention_ref(q, k, v, idx, cnt, None)
+    o = oracle.sparse_attention_ref(q, k, v, idx, cnt, None, block)
     kk = k.double().repeat_interleave(hq // hkv, dim=1)
     vv = v.double().repeat_interleave(hq // hkv, dim=1)
     ref = F.scaled_dot_product_attention(q.double(), kk, vv, is_causal=True).numpy()
     np.testing.assert_allclose(o, ref, atol=1e-12, rtol=0)
 
 
-@pytest.mark.parametrize("seed", [2, 3])
-def test_block_mask_equals_sdpa_with_expanded_mask(seed):
-    b, hq, hkv, t, d = 2, 4, 2, 300, 32
+@pytest.mark.parametrize("seed,block", [(2, 64), (3, 64), (4, 128), (5, 128)])
+def test_block_mask_equals_sdpa_with_expanded_mask(seed, block):
+    b, hq, hkv, t, d = 2, 4, 2, 300 if block == 64 else 700, 32
     q, k, v = _inputs(seed, b, hq, hkv, t, d)
-    nqb = (t + BLOCK - 1) // BLOCK
+    nqb = (t + block - 1) // block
     idx, cnt = _random_lists(seed, b, hq, nqb, nqb)
     scale = 0.3
-    o = oracle.sparse_attention_ref(q, k, v, idx, cnt, scale)
-    ref = _sdpa_with_blocks(q, k, v, idx, cnt, scale)
+    o = oracle.sparse_attention_ref(q, k, v, idx, cnt, scale, block)
+    ref = _sdpa_with_blocks(q, k, v, idx, cnt, scale, block)
     np.testing.assert_allclose(o, ref, atol=1e-12, rtol=0)
 
 
