@@ -23,7 +23,7 @@ BLOCK = 64
 
 EXPORTED = (
     "seer_status_string", "seer_version", "seer_topk_budget", "seer_build_mask",
-    "seer_sparse_prefill_workspace_size", "seer_sparse_prefill",
+    "seer_sparse_prefill_workspace_size", "seer_sparse_prefill", "seer_sparse_prefill_block",
     "seer_pooled_attn_map_workspace_size", "seer_pooled_attn_map", "seer_pooled_target_mse",
 )
 
@@ -63,6 +63,10 @@ def load() -> ctypes.CDLL:
     lib.seer_sparse_prefill.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int,
                                         c_float, c_void, c_void, c_int, c_void, c_void, c_size,
                                         c_void]
+    lib.seer_sparse_prefill_block.restype = c_int
+    lib.seer_sparse_prefill_block.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int,
+                                              c_int, c_float, c_int, c_void, c_void, c_int,
+                                              c_void, c_void, c_size, c_void]
     lib.seer_pooled_attn_map_workspace_size.restype = c_size
     lib.seer_pooled_attn_map_workspace_size.argtypes = [c_int, c_int, c_int]
     lib.seer_pooled_attn_map.restype = c_int
@@ -150,17 +154,13 @@ def _qkv_dims(q, k, v):
     return b, hq, hkv, t, d
 
 
-def seer_sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_idx: torch.Tensor,
-                        kv_cnt: torch.Tensor, sm_scale: Optional[float] = None,
-                        out: Optional[torch.Tensor] = None,
-                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Block-sparse causal prefill.  q [B,Hq,T,D], k/v [B,Hkv,T,D] bf16 -> O bf16."""
+def _sparse_args(q, k, v, kv_idx, kv_cnt, block, sm_scale, out, workspace):
     lib = load()
     b, hq, hkv, t, d = _qkv_dims(q, k, v)
-    nqb = (t + BLOCK - 1) // BLOCK
+    nb = (t + block - 1) // block
     max_k = kv_idx.shape[-1]
-    _need(kv_idx, "kv_idx", torch.int32, (b, hq, nqb, max_k))
-    _need(kv_cnt, "kv_cnt", torch.int32, (b, hq, nqb))
+    _need(kv_idx, "kv_idx", torch.int32, (b, hq, nb, max_k))
+    _need(kv_cnt, "kv_cnt", torch.int32, (b, hq, nb))
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", torch.bfloat16, (b, hq, t, d))
@@ -168,9 +168,33 @@ def seer_sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_id
     if workspace is None:
         workspace = _workspace(need, q.device)
     scale = (1.0 / d ** 0.5) if sm_scale is None else float(sm_scale)
+    return lib, (b, hq, hkv, t, d, scale), int(max_k), out, workspace
+
+
+def seer_sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_idx: torch.Tensor,
+                        kv_cnt: torch.Tensor, sm_scale: Optional[float] = None,
+                        out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Block-sparse causal prefill.  q [B,Hq,T,D], k/v [B,Hkv,T,D] bf16 -> O bf16."""
+    lib, dims, max_k, out, workspace = _sparse_args(q, k, v, kv_idx, kv_cnt, BLOCK, sm_scale, out,
+                                                    workspace)
     _check("seer_sparse_prefill", lib.seer_sparse_prefill(
-        _ptr(q), _ptr(k), _ptr(v), b, hq, hkv, t, d, scale, _ptr(kv_idx), _ptr(kv_cnt),
-        int(max_k), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(q), _ptr(k), _ptr(v), *dims, _ptr(kv_idx), _ptr(kv_cnt), max_k, _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def seer_sparse_prefill_block(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                              kv_idx: torch.Tensor, kv_cnt: torch.Tensor, block: int,
+                              sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """seer_sparse_prefill with lists of `block`-token blocks (64 or 128):
+    kv_idx [B,Hq,ceil(T/block),max_k], kv_cnt [B,Hq,ceil(T/block)]."""
+    lib, dims, max_k, out, workspace = _sparse_args(q, k, v, kv_idx, kv_cnt, int(block), sm_scale,
+                                                    out, workspace)
+    _check("seer_sparse_prefill_block", lib.seer_sparse_prefill_block(
+        _ptr(q), _ptr(k), _ptr(v), *dims, int(block), _ptr(kv_idx), _ptr(kv_cnt), max_k,
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return out
 

@@ -97,10 +97,11 @@ size_t seer_sparse_prefill_workspace_size(int B, int Hq, int Hkv, int T) {
   return ((entries * sizeof(int32_t) + 255) / 256) * 256 + 256;
 }
 
-int seer_sparse_prefill(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
-                        int T, int D, float sm_scale, const int32_t* kv_idx,
-                        const int32_t* kv_cnt, int max_k, void* o, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+int seer_sparse_prefill_block(const void* q, const void* k, const void* v, int B, int Hq,
+                              int Hkv, int T, int D, float sm_scale, int block,
+                              const int32_t* kv_idx, const int32_t* kv_cnt, int max_k, void* o,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (block != 64 && block != 128) return SEER_ERR_UNSUPPORTED;
   const int st = attention_args(q, k, v, o, B, Hq, Hkv, T, D, sm_scale);
   if (st != SEER_OK) return st;
   if (max_k < 1) return SEER_ERR_INVALID_ARG;
@@ -109,9 +110,17 @@ int seer_sparse_prefill(const void* q, const void* k, const void* v, int B, int 
   const size_t need = seer_sparse_prefill_workspace_size(B, Hq, Hkv, T);
   if (!workspace || workspace_bytes < need || !aligned256(workspace)) return SEER_ERR_WORKSPACE;
   const hipError_t err =
-      seer::launch_sparse_prefill(q, k, v, B, Hq, Hkv, T, D, sm_scale, kv_idx, kv_cnt, max_k,
-                                  static_cast<int32_t*>(workspace), o, (hipStream_t)stream);
+      seer::launch_sparse_prefill(q, k, v, B, Hq, Hkv, T, D, sm_scale, block, kv_idx, kv_cnt,
+                                  max_k, static_cast<int32_t*>(workspace), o, (hipStream_t)stream);
   return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
+}
+
+int seer_sparse_prefill(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
+                        int T, int D, float sm_scale, const int32_t* kv_idx,
+                        const int32_t* kv_cnt, int max_k, void* o, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return seer_sparse_prefill_block(q, k, v, B, Hq, Hkv, T, D, sm_scale, SEER_BLOCK, kv_idx,
+                                   kv_cnt, max_k, o, workspace, workspace_bytes, stream);
 }
 
 size_t seer_pooled_attn_map_workspace_size(int B, int Hq, int T) {

@@ -799,7 +799,13 @@ __device__ __forceinline__ void kv_loop_parts(RowState<D>& st, const __bf16* __r
   }
 }
 
-template <int D>
+// BS = list block size in 64-token tiles (1: 64-token blocks, 2: 128-token
+// blocks).  Work items are always 64-row query blocks: item (b, h, i) reads
+// list row i / BS, and each listed block j stands for the tiles BS j .. BS j +
+// BS - 1, of which those past the diagonal tile i are skipped (a 128-token
+// diagonal block is one full tile plus the masked diagonal tile for the second
+// half of its rows, and the masked diagonal tile alone for the first half).
+template <int D, int BS>
 __global__ __launch_bounds__(kPairThreads, 3) void sparse_prefill_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     int Hq, int Hkv, int T, int nqb, float c, const int32_t* __restrict__ idx,
@@ -811,7 +817,7 @@ __global__ __launch_bounds__(kPairThreads, 3) void sparse_prefill_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int item = work[blockIdx.x];
-  const int i = item % nqb;
+  const int i = item % nqb;   // 64-row query block
   const int bh = item / nqb;  // b * Hq + h
   const int b = bh / Hq;
   const int g = (bh % Hq) / (Hq / Hkv);
@@ -819,19 +825,23 @@ __global__ __launch_bounds__(kPairThreads, 3) void sparse_prefill_kernel(
   const size_t q_off = (size_t)bh * (size_t)T * D;
 
   RowState<D> st;
-  const int32_t* lst = idx + (size_t)item * max_k;
-  const int n = min(max(cnt[item], 0), max_k);
-  auto next = [&](int e) {  // first list position >= e holding a block in [0, i]
-    while (e < n) {
-      const int j = lst[e];
-      if (j >= 0 && j <= i) break;
-      ++e;
+  const int rows = (nqb + BS - 1) / BS;  // list rows per head
+  const int ib = i / BS;                 // this item's list row (and its own block)
+  const size_t lrow = (size_t)bh * rows + ib;
+  const int32_t* lst = idx + lrow * max_k;
+  const int n = min(max(cnt[lrow], 0), max_k);
+  // Walk positions x = BS * entry + sub-tile; tile BS * lst[entry] + sub.
+  auto next = [&](int x) {  // first position >= x holding a tile in [0, i]
+    while (x < BS * n) {
+      const int j = lst[x / BS];
+      if (j >= 0 && j <= ib && BS * j + x % BS <= i) break;
+      ++x;
     }
-    return e;
+    return x;
   };
-  auto block = [&](int e) { return lst[e]; };
-  kv_loop_parts<D>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, n, next, block, ring,
-                   lane, wave, c);
+  auto block = [&](int x) { return BS * lst[x / BS] + x % BS; };
+  kv_loop_parts<D>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, BS * n, next, block,
+                   ring, lane, wave, c);
   (void)store_o<D>(st, o + q_off, kBlk * i, T, lane, wave);
 }
 
@@ -975,16 +985,21 @@ __device__ void lpt_column(int n, Keep keep, Cost cost, Id id, int32_t* __restri
 }
 
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
-    const int32_t* __restrict__ cnt, int Hq, int Hkv, int nqb, int max_k,
+    const int32_t* __restrict__ cnt, int Hq, int Hkv, int nqb, int bs, int max_k,
     int32_t* __restrict__ work) {
   __shared__ int hist[kCostBins];
   __shared__ int wsum[kSchedThreads / 64];
   const int G = Hq / Hkv;
   const int grp = blockIdx.x;
-  const int base = ((grp / Hkv) * Hq + (grp % Hkv) * G) * nqb;  // the group's items
+  const int bh0 = (grp / Hkv) * Hq + (grp % Hkv) * G;  // first head of the group
+  const int base = bh0 * nqb;                          // the group's items
+  const int rows = (nqb + bs - 1) / bs;                // list rows per head
   lpt_column(
       G * nqb, [](int) { return true; },
-      [&](int it) { return min(max(cnt[base + it], 0), max_k); },
+      [&](int it) {
+        const int c = cnt[(bh0 + it / nqb) * rows + (it % nqb) / bs];
+        return bs * min(max(c, 0), max_k);
+      },
       [&](int it) { return base + it; }, work, gridDim.x, grp, G * nqb, hist, wsum);
 }
 
@@ -995,11 +1010,11 @@ constexpr int kPairKSlots = 2;
 constexpr int kPairVSlots = 1;
 
 
-template <int D>
+template <int D, int BS>
 hipError_t sparse_launch(const void* q, const void* k, const void* v, size_t items, int Hq,
                          int Hkv, int T, int nqb, float c, const int32_t* idx, const int32_t* cnt,
                          int max_k, const int32_t* work, void* o, hipStream_t stream) {
-  hipLaunchKernelGGL((sparse_prefill_kernel<D>), dim3((unsigned)items), dim3(kPairThreads), 0,
+  hipLaunchKernelGGL((sparse_prefill_kernel<D, BS>), dim3((unsigned)items), dim3(kPairThreads), 0,
                      stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, Hq, Hkv, T,
                      nqb, c, idx, cnt, max_k, work, (__bf16*)o);
   return hipGetLastError();
@@ -1023,21 +1038,27 @@ hipError_t pooled_launch(const void* q, const void* k, const void* v, int B, int
 size_t sparse_work_entries(int B, int Hq, int, int nqb) { return (size_t)B * Hq * nqb; }
 
 hipError_t launch_sparse_prefill(const void* q, const void* k, const void* v, int B, int Hq,
-                                 int Hkv, int T, int D, float sm_scale, const int32_t* idx,
-                                 const int32_t* cnt, int max_k, int32_t* work, void* o,
-                                 hipStream_t stream) {
+                                 int Hkv, int T, int D, float sm_scale, int block,
+                                 const int32_t* idx, const int32_t* cnt, int max_k, int32_t* work,
+                                 void* o, hipStream_t stream) {
   const int nqb = (T + kBlk - 1) / kBlk;
   const size_t items = (size_t)B * Hq * nqb;
   if (items == 0) return hipSuccess;
   const float c = sm_scale * kLog2e;
+  const int bs = block / kBlk;
   hipLaunchKernelGGL(schedule_kernel, dim3(B * Hkv), dim3(kSchedThreads), 0, stream, cnt, Hq, Hkv,
-                     nqb, max_k, work);
+                     nqb, bs, max_k, work);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return D == 128 ? sparse_launch<128>(q, k, v, items, Hq, Hkv, T, nqb, c, idx, cnt, max_k, work,
-                                       o, stream)
-                  : sparse_launch<64>(q, k, v, items, Hq, Hkv, T, nqb, c, idx, cnt, max_k, work,
-                                      o, stream);
+  if (bs == 2)
+    return D == 128 ? sparse_launch<128, 2>(q, k, v, items, Hq, Hkv, T, nqb, c, idx, cnt, max_k,
+                                            work, o, stream)
+                    : sparse_launch<64, 2>(q, k, v, items, Hq, Hkv, T, nqb, c, idx, cnt, max_k,
+                                           work, o, stream);
+  return D == 128 ? sparse_launch<128, 1>(q, k, v, items, Hq, Hkv, T, nqb, c, idx, cnt, max_k,
+                                          work, o, stream)
+                  : sparse_launch<64, 1>(q, k, v, items, Hq, Hkv, T, nqb, c, idx, cnt, max_k, work,
+                                         o, stream);
 }
 
 hipError_t launch_pooled_map(const void* q, const void* k, const void* v, int B, int Hq,

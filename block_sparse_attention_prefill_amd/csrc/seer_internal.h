@@ -24,10 +24,11 @@ hipError_t launch_build_mask(const float* scores, int B, int H, int nqb, int nkb
                              float threshold, double density, int keep_sink, int32_t* idx,
                              int32_t* cnt, int max_k, hipStream_t stream);
 
+// block: list block size in tokens, 64 or 128 (checked by the caller).
 hipError_t launch_sparse_prefill(const void* q, const void* k, const void* v, int B, int Hq,
-                                 int Hkv, int T, int D, float sm_scale, const int32_t* idx,
-                                 const int32_t* cnt, int max_k, int32_t* work, void* o,
-                                 hipStream_t stream);
+                                 int Hkv, int T, int D, float sm_scale, int block,
+                                 const int32_t* idx, const int32_t* cnt, int max_k, int32_t* work,
+                                 void* o, hipStream_t stream);
 
 hipError_t launch_pooled_map(const void* q, const void* k, const void* v, int B, int Hq,
                              int Hkv, int T, int D, float sm_scale, void* o, float* amap,

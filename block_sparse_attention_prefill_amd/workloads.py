@@ -55,10 +55,11 @@ class Workload:
     scores: str = "uniform"  # "uniform" | "softmax_normal" | "local_stripe" | "none"
     qkv_scale: float = 1.0
     sample_qblocks: Optional[int] = None  # per head, for oracle checks at full size
+    block: int = BLOCK  # tokens per block of the score grid and the index lists
 
     @property
     def nqb(self) -> int:
-        return (self.seq + BLOCK - 1) // BLOCK
+        return (self.seq + self.block - 1) // self.block
 
     @property
     def groups(self) -> int:

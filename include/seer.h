@@ -132,6 +132,21 @@ int seer_sparse_prefill(const void* q, const void* k, const void* v, int B, int 
                         const int32_t* kv_cnt, int max_k, void* o, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/*
+ * seer_sparse_prefill with lists of `block`-token blocks, block in {64, 128}
+ * (else SEER_ERR_UNSUPPORTED); the rebuttal's "Question 3 (Block Size
+ * Experiments)" evaluates block sizes 32, 64 and 128.  kv_idx is
+ * [B, Hq, nB, max_k] and kv_cnt [B, Hq, nB] with nB = ceil(T / block), both
+ * counting blocks of `block` tokens (e.g. seer_build_mask run on
+ * [B, Hq, nB, nB] block scores); query block i of `block` rows attends to the
+ * keys of its listed blocks, causally.  Everything else, the workspace
+ * included, is as for seer_sparse_prefill, which is this call with block 64.
+ */
+int seer_sparse_prefill_block(const void* q, const void* k, const void* v, int B, int Hq,
+                              int Hkv, int T, int D, float sm_scale, int block,
+                              const int32_t* kv_idx, const int32_t* kv_cnt, int max_k, void* o,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace seer_pooled_attn_map needs: the stored per-row
  * block maxima r_ij (fp32, 64 per causal (i, j) tile).  0 for invalid sizes. */
 size_t seer_pooled_attn_map_workspace_size(int B, int Hq, int T);

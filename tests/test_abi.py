@@ -124,3 +124,18 @@ def test_pooled_target_rejects_on_host():
     assert lib.seer_pooled_target_mse(FAKE, FAKE, -1, 2, 8, FAKE, FAKE, FAKE, None) == 1
     assert lib.seer_pooled_target_mse(FAKE, FAKE, 0, 2, 8, FAKE, FAKE, FAKE, None) == 0  # empty
 
+
+def test_sparse_prefill_block_rejects_on_host():
+    lib = seer.load()
+    a = [FAKE, FAKE, FAKE, 1, 4, 2, 128, 128, 0.1, 128, FAKE, FAKE, 2, FAKE, FAKE, 1 << 20, None]
+    for bad_block in (32, 96, 256, 0):
+        a2 = list(a)
+        a2[9] = bad_block
+        assert lib.seer_sparse_prefill_block(*a2) == 2
+    a2 = list(a)
+    a2[7] = 80          # head dim
+    assert lib.seer_sparse_prefill_block(*a2) == 2
+    a2 = list(a)
+    a2[14] = None       # workspace
+    assert lib.seer_sparse_prefill_block(*a2) == 4
+

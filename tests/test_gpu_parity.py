@@ -134,10 +134,10 @@ def _run_sparse(q, k, v, idx, cnt, scale=None):
     return o.cpu()
 
 
-def _check_blocks(o_gpu, ref, tol, label):
+def _check_blocks(o_gpu, ref, tol, label, block=64):
     worst = 0.0
     for (b, h, i), oi in ref.items():
-        got = o_gpu[b, h, 64 * i: 64 * i + oi.shape[0]].double().numpy()
+        got = o_gpu[b, h, block * i: block * i + oi.shape[0]].double().numpy()
         err = float(np.abs(got - oi).max()) if oi.size else 0.0
         worst = max(worst, err)
         assert err <= tol, f"{label}: block {(b, h, i)} max-abs error {err}"
@@ -320,6 +320,85 @@ def test_pooled_map_repeat_bitexact():
         torch.cuda.synchronize()
         assert int((o.view(torch.int16) != o0).sum()) == 0
         assert int((a != a0).sum()) == 0
+
+
+# ------------------------------------------------------------------ 128-token blocks
+
+
+def _run_sparse_block(q, k, v, idx, cnt, block, scale=None):
+    o = seer.seer_sparse_prefill_block(_dev(q), _dev(k), _dev(v), _dev(idx), _dev(cnt), block,
+                                       scale)
+    torch.cuda.synchronize()
+    return o.cpu()
+
+
+@pytest.mark.parametrize("case", ["tiny", "llama8k"])
+def test_sparse_prefill_block128_topk(case):
+    """128-token blocks: mask built on the GPU from [B,H,T/128,T/128] scores
+    (checked bit for bit against the oracle's lists), O against the oracle."""
+    if case == "tiny":
+        w = wl.custom(70, 1, 2, 1, 64, 512, mode=wl.MODE_TOPK, density=0.5, keep_sink=True,
+                      scores="uniform", block=128)
+    else:
+        w = wl.custom(71, 1, 32, 8, 128, 8192, mode=wl.MODE_TOPK, density=0.1, keep_sink=True,
+                      scores="local_stripe", block=128)
+    announce(f"sparse prefill block 128 {w.name}")
+    q, k, v = wl.make_qkv(w)
+    s = wl.make_scores(w)
+    max_k = seer.topk_budget(w.nqb, w.density, w.keep_sink)
+    idx, cnt = seer.seer_build_mask(_dev(s), w.mode, w.threshold, w.density, w.keep_sink, max_k)
+    o = seer.seer_sparse_prefill_block(_dev(q), _dev(k), _dev(v), idx, cnt, 128)
+    torch.cuda.synchronize()
+    o, idx, cnt = o.cpu(), idx.cpu().numpy(), cnt.cpu().numpy()
+    ref_idx, ref_cnt = oracle.build_mask_ref(s.numpy(), w.mode, w.threshold, w.density,
+                                             w.keep_sink, max_k)
+    assert (idx == ref_idx).all() and (cnt == ref_cnt).all()
+    if case == "tiny":
+        blocks = [(0, h, i) for h in range(w.hq) for i in range(w.nqb)]
+    else:
+        blocks = wl.sample_qblocks(w, 4)
+    ref = oracle.sparse_attention_blocks_ref(q, k, v, idx, cnt, None, blocks, 128)
+    _check_blocks(o, ref, O_TOL, w.name, 128)
+
+
+@pytest.mark.parametrize("b,hq,hkv,t,d,mode", [
+    (1, 4, 2, 1000, 128, "unsorted"),   # ragged: the last 128-block holds one short tile
+    (2, 6, 3, 700, 64, "invalid"),      # invalid entries, cnt > max_k, empty rows
+    (1, 2, 1, 100, 128, "sorted"),      # one 128-block, two tiles
+    (1, 4, 1, 777, 64, "dense"),        # heavy rows
+])
+def test_sparse_prefill_block128_lists(b, hq, hkv, t, d, mode):
+    announce(f"sparse prefill block 128 custom b={b} hq={hq} hkv={hkv} t={t} d={d} lists={mode}")
+    g = torch.Generator().manual_seed(t * 11 + d)
+    q = torch.randn(b, hq, t, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(b, hkv, t, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(b, hkv, t, d, generator=g).to(torch.bfloat16)
+    nb = (t + 127) // 128
+    max_k = nb if mode == "dense" else max(1, min(nb, 4))
+    idx, cnt = _random_lists(t + 3 * d, b, hq, nb, max_k, mode)
+    o = _run_sparse_block(q, k, v, torch.from_numpy(idx), torch.from_numpy(cnt), 128, 0.2)
+    ref = oracle.sparse_attention_ref(q, k, v, idx, cnt, 0.2, 128)
+    err = float(np.abs(o.double().numpy() - ref).max())
+    announce(f"max-abs error {err:.3e}")
+    assert err <= O_TOL
+
+
+def test_sparse_prefill_block128_density_one_and_repeat():
+    """Every causal 128-block listed: dense causal attention (the oracle at
+    density 1 is pinned to SDPA); repeated runs are bit-identical."""
+    b, hq, hkv, t, d = 1, 4, 2, 1100, 128
+    g = torch.Generator().manual_seed(9)
+    q = torch.randn(b, hq, t, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(b, hkv, t, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(b, hkv, t, d, generator=g).to(torch.bfloat16)
+    nb = (t + 127) // 128
+    idx = np.tile(np.arange(nb, dtype=np.int32), (b, hq, nb, 1))
+    cnt = np.tile(np.arange(1, nb + 1, dtype=np.int32), (b, hq, 1))
+    o = _run_sparse_block(q, k, v, torch.from_numpy(idx), torch.from_numpy(cnt), 128)
+    ref = oracle.sparse_attention_ref(q, k, v, idx, cnt, None, 128)
+    assert float(np.abs(o.double().numpy() - ref).max()) <= O_TOL
+    o2 = _run_sparse_block(q, k, v, torch.from_numpy(idx), torch.from_numpy(cnt), 128)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
 
 
 # ------------------------------------------------------------------ pooled map
