@@ -282,7 +282,53 @@ def main(argv=None) -> int:
             "pct_of_bf16_peak": round(100 * tiles * tile_flops(w5.head_dim) / (pm_ms * 1e-3)
                                       / 1e12 / PEAK_BF16_TFLOPS, 2),
         }
-        del q5, k5, v5, o5, a5, ws5
+
+        # Row-normalised target + MSE on that map against gate-like scores
+        # (HBM-bound: causal halves of map and gate read, full target written).
+        log("[bench] distillation target + MSE on the pooled map")
+        gate = wl.make_scores(wl.custom(105, w5.batch, w5.hq, 1, 64, w5.seq,
+                                        scores="softmax_normal")).to(dev)
+        tgt = torch.empty_like(a5)
+        rsse = torch.empty((w5.batch, w5.hq, w5.nqb), dtype=torch.float32, device=dev)
+        lossd = torch.empty((1,), dtype=torch.float32, device=dev)
+        tcall = lambda: seer.seer_pooled_target_mse(a5, gate, target=tgt, row_sse=rsse,
+                                                    loss=lossd)
+        tcall()
+        tg_ms = time_calls(tcall, max(3, args.steps // 2), torch)
+        rows = w5.batch * w5.hq * w5.nqb
+        tg_bytes = 4 * (2 * tiles + rows * w5.nqb + rows + 1)
+        result["pooled_target_mse"] = {
+            "ms": round(tg_ms, 4),
+            "gbps": round(tg_bytes / (tg_ms * 1e-3) / 1e9, 1),
+            "hbm_peak_gbps": 8000.0,
+            "algorithmic_bytes": tg_bytes,
+        }
+        del q5, k5, v5, o5, a5, ws5, gate, tgt, rsse, lossd
+
+        # The bench workload's shape with 128-token blocks (TopK at the same density).
+        w128 = wl.custom(103, w.batch, w.hq, w.hkv, w.head_dim, w.seq, mode=w.mode,
+                         name=w.name + "_block128",
+                         density=w.density, keep_sink=w.keep_sink, scores=w.scores, block=128)
+        log(f"[bench] 128-token blocks on {w.name}")
+        s128 = wl.make_scores(w128).to(dev)
+        mk128 = seer.topk_budget(w128.nqb, w128.density, w128.keep_sink)
+        idx128, cnt128 = seer.seer_build_mask(s128, w128.mode, w128.threshold, w128.density,
+                                              w128.keep_sink, mk128)
+        call128 = lambda: seer.seer_sparse_prefill_block(qd, kd, vd, idx128, cnt128, 128, out=out,
+                                                         workspace=ws)
+        call128()
+        b128_ms = time_calls(call128, max(3, args.steps // 2), torch)
+        # 64-token tiles computed: a listed 128-block gives both of its tiles to each
+        # 64-row half, except the diagonal block, whose upper tile the first half skips.
+        c = cnt128.to(torch.int64)
+        tiles128 = int((4 * c - 1).clamp(min=0).sum().item())
+        result["block128"] = {
+            "workload": w128.name,
+            "prefill_ms": round(b128_ms, 4),
+            "computed_tiles64": tiles128,
+            "tflops": round(tiles128 * tile_flops(w.head_dim) / (b128_ms * 1e-3) / 1e12, 3),
+        }
+        del s128, idx128, cnt128
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
