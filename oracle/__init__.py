@@ -18,6 +18,10 @@ What it computes, each function citing the passage it follows:
                  (reproducibility summary of "SeerAttention: Self-distilled
                  Attention Gating for Efficient Long-context Prefilling",
                  Pseudocode row, Figure 8).
+* ``gate``    -- the AttnGate's soft block scores: pooled Q and K, linear layers,
+                 block RoPE and a causal softmax (rebuttal "SeerAttention:
+                 Learning Intrinsic Sparse Attention in Your LLMs", Weakness 3
+                 and the pooling and RoPE answers).
 * ``target``  -- the row-normalised map used as the gate's ground truth and the
                  MSE against gate scores (rebuttal "SeerAttention: Learning
                  Intrinsic Sparse Attention in Your LLMs", "Question 2:
@@ -35,10 +39,12 @@ from .attention import (BLOCK, block_probs, allowed_blocks, sparse_attention_ref
                         sparse_attention_blocks_ref)
 from .pooled import pooled_map_ref, pooled_map_blocks_ref
 from .target import pooled_target_ref
+from .gate import pool_qk, block_rope, gate_qk_ref, gate_scores_ref
 
 __all__ = [
     "MODE_THRESHOLD", "MODE_TOPK", "BLOCK", "forced_blocks", "topk_count", "select_row",
     "build_mask_ref", "mask_rows_ref", "block_probs", "allowed_blocks",
     "sparse_attention_ref", "sparse_attention_blocks_ref", "pooled_map_ref",
-    "pooled_map_blocks_ref", "pooled_target_ref",
+    "pooled_map_blocks_ref", "pooled_target_ref", "pool_qk", "block_rope", "gate_qk_ref",
+    "gate_scores_ref",
 ]
