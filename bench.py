@@ -305,6 +305,26 @@ def main(argv=None) -> int:
         }
         del q5, k5, v5, o5, a5, ws5, gate, tgt, rsse, lossd
 
+        # AttnGate soft scores on the bench shape (Dg 128, random-init weights): pool +
+        # project + RoPE, then the causal Q~K~^T softmax (read Q and K once: HBM-bound).
+        log(f"[bench] AttnGate scores on {w.name}")
+        dg = 128
+        wq, wk = (t.to(dev) for t in wl.make_gate_weights(w, dg))
+        gs = torch.empty((w.batch, w.hq, w.nqb, w.nqb), dtype=torch.float32, device=dev)
+        gws = torch.empty((seer.load().seer_attn_gate_workspace_size(
+            w.batch, w.hq, w.hkv, w.seq, dg),), dtype=torch.uint8, device=dev)
+        gcall = lambda: seer.seer_attn_gate_scores(qd, kd, wq, wk, scores=gs, workspace=gws)
+        gcall()
+        g_ms = time_calls(gcall, max(3, args.steps // 2), torch)
+        g_bytes = 2 * (qd.numel() + kd.numel()) + 4 * gs.numel()
+        result["attn_gate"] = {
+            "ms": round(g_ms, 4),
+            "gate_dim": dg,
+            "gbps": round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
+            "algorithmic_bytes": g_bytes,
+        }
+        del wq, wk, gs, gws
+
         # The bench workload's shape with 128-token blocks (TopK at the same density).
         w128 = wl.custom(103, w.batch, w.hq, w.hkv, w.head_dim, w.seq, mode=w.mode,
                          name=w.name + "_block128",

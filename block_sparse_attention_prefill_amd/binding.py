@@ -25,6 +25,7 @@ EXPORTED = (
     "seer_status_string", "seer_version", "seer_topk_budget", "seer_build_mask",
     "seer_sparse_prefill_workspace_size", "seer_sparse_prefill", "seer_sparse_prefill_block",
     "seer_pooled_attn_map_workspace_size", "seer_pooled_attn_map", "seer_pooled_target_mse",
+    "seer_attn_gate_workspace_size", "seer_attn_gate_scores",
 )
 
 _lib = None
@@ -72,6 +73,12 @@ def load() -> ctypes.CDLL:
     lib.seer_pooled_attn_map.restype = c_int
     lib.seer_pooled_attn_map.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int,
                                          c_float, c_void, c_void, c_void, c_size, c_void]
+    lib.seer_attn_gate_workspace_size.restype = c_size
+    lib.seer_attn_gate_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int]
+    lib.seer_attn_gate_scores.restype = c_int
+    lib.seer_attn_gate_scores.argtypes = [c_void, c_void, c_int, c_int, c_int, c_int, c_int,
+                                          c_void, c_void, c_int, c_float, c_float, c_void,
+                                          c_void, c_size, c_void]
     lib.seer_pooled_target_mse.restype = c_int
     lib.seer_pooled_target_mse.argtypes = [c_void, c_void, c_int, c_int, c_int, c_void, c_void,
                                            c_void, c_void]
@@ -250,3 +257,30 @@ def seer_pooled_target_mse(amap: torch.Tensor, gate: Optional[torch.Tensor] = No
         _ptr(amap), _ptr(gate), b, h, nqb, _ptr(target), _ptr(row_sse), _ptr(loss),
         _stream(stream)))
     return target, row_sse, loss
+
+
+def seer_attn_gate_scores(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor, wk: torch.Tensor,
+                          scale: Optional[float] = None, rope_base: float = 10000.0,
+                          scores: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """AttnGate soft block scores [B,Hq,nQB,nQB] fp32 from q [B,Hq,T,D], k [B,Hkv,T,D]
+    (bf16, before RoPE) and weights wq [Hq,D,Dg], wk [Hkv,2D,Dg] (fp32)."""
+    lib = load()
+    b, hq, hkv, t, d = _qkv_dims(q, k, k)
+    dg = wq.shape[-1]
+    nqb = (t + BLOCK - 1) // BLOCK
+    _need(wq, "wq", torch.float32, (hq, d, dg))
+    _need(wk, "wk", torch.float32, (hkv, 2 * d, dg))
+    if scores is None:
+        scores = torch.empty((b, hq, nqb, nqb), dtype=torch.float32, device=q.device)
+    _need(scores, "scores", torch.float32, (b, hq, nqb, nqb))
+    need = lib.seer_attn_gate_workspace_size(b, hq, hkv, t, dg)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    sc = (1.0 / dg ** 0.5) if scale is None else float(scale)
+    _check("seer_attn_gate_scores", lib.seer_attn_gate_scores(
+        _ptr(q), _ptr(k), b, hq, hkv, t, d, _ptr(wq), _ptr(wk), int(dg), sc, float(rope_base),
+        _ptr(scores), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return scores
+

@@ -159,4 +159,31 @@ int seer_pooled_target_mse(const float* amap, const float* gate, int B, int H, i
   return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
 }
 
+size_t seer_attn_gate_workspace_size(int B, int Hq, int Hkv, int T, int Dg) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || T < 0 || Dg <= 0 || Hq % Hkv != 0) return 0;
+  if (!items_fit(B, Hq + Hkv, nqb_of(T))) return 0;
+  return seer::attn_gate_workspace_floats(B, Hq, Hkv, nqb_of(T), Dg) * sizeof(float) + 256;
+}
+
+int seer_attn_gate_scores(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
+                          const float* wq, const float* wk, int Dg, float scale, float rope_base,
+                          float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return SEER_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return SEER_ERR_UNSUPPORTED;
+  if (Dg != 32 && Dg != 64 && Dg != 128) return SEER_ERR_UNSUPPORTED;
+  if (!(isfinite(scale) && scale > 0.f)) return SEER_ERR_INVALID_ARG;
+  if (!(isfinite(rope_base) && rope_base > 1.f)) return SEER_ERR_INVALID_ARG;
+  if (!items_fit(B, Hq + Hkv, nqb_of(T))) return SEER_ERR_UNSUPPORTED;
+  if ((long long)B * T == 0) return SEER_OK;
+  if (!q || !k || !wq || !wk || !scores) return SEER_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(wq) || !aligned16(wk))
+    return SEER_ERR_INVALID_ARG;
+  const size_t need = seer_attn_gate_workspace_size(B, Hq, Hkv, T, Dg);
+  if (!workspace || workspace_bytes < need || !aligned256(workspace)) return SEER_ERR_WORKSPACE;
+  const hipError_t err =
+      seer::launch_attn_gate(q, k, B, Hq, Hkv, T, D, wq, wk, Dg, scale, rope_base, scores,
+                             static_cast<float*>(workspace), (hipStream_t)stream);
+  return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
+}
+
 }  // extern "C"

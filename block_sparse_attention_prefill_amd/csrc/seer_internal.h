@@ -37,4 +37,11 @@ hipError_t launch_pooled_map(const void* q, const void* k, const void* v, int B,
 hipError_t launch_pooled_target(const float* amap, const float* gate, int B, int H, int nqb,
                                 float* target, float* row_sse, float* loss, hipStream_t stream);
 
+// fp32 elements of the gate's workspace (projected Q~ and K~).
+size_t attn_gate_workspace_floats(int B, int Hq, int Hkv, int nqb, int dg);
+
+hipError_t launch_attn_gate(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
+                            const float* wq, const float* wk, int dg, float scale,
+                            float rope_base, float* scores, float* ws, hipStream_t stream);
+
 }  // namespace seer

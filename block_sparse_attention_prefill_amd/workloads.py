@@ -18,7 +18,8 @@ dataset, prompt or trained weight is used: every value is drawn from a seeded
 NumPy PCG64 generator.
 
 Seeds: ``seed = 1000 * workload_id + stream`` with stream 0 = Q, 1 = K, 2 = V,
-3 = scores, 4 = stripe columns, 5 = sampled query blocks, 6 = block maps.
+3 = scores, 4 = stripe columns, 5 = sampled query blocks, 6 = block maps,
+7 = gate weights.
 """
 
 from __future__ import annotations
@@ -172,6 +173,18 @@ def make_block_map(w: Workload, seed_stream: int = 6) -> torch.Tensor:
     junk = np.float32(1e6) * (np.float32(1.0) + rng.random(size=a.shape, dtype=np.float32))
     causal = np.tril(np.ones((n, n), dtype=bool))
     return torch.from_numpy(np.ascontiguousarray(np.where(causal, a, junk).astype(np.float32)))
+
+
+def make_gate_weights(w: Workload, dg: int, gain: float = 1.0, seed_stream: int = 7):
+    """Random-init AttnGate linear weights: Wq [Hq, D, Dg] and Wk [Hkv, 2D, Dg],
+    fp32, N(0, gain^2 / fan_in) (no trained gate weights are used anywhere)."""
+    rng = np.random.Generator(np.random.PCG64(w.seed(seed_stream)))
+    d = w.head_dim
+    wq = (rng.standard_normal(size=(w.hq, d, dg), dtype=np.float32)
+          * np.float32(gain / math.sqrt(d)))
+    wk = (rng.standard_normal(size=(w.hkv, 2 * d, dg), dtype=np.float32)
+          * np.float32(gain / math.sqrt(2 * d)))
+    return torch.from_numpy(np.ascontiguousarray(wq)), torch.from_numpy(np.ascontiguousarray(wk))
 
 
 def sample_qblocks(w: Workload, count: Optional[int] = None) -> np.ndarray:

@@ -170,6 +170,43 @@ int seer_pooled_attn_map(const void* q, const void* k, const void* v, int B, int
                          int T, int D, float sm_scale, void* o, float* amap, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace seer_attn_gate_scores needs (the projected,
+ * rotated Q~ [B,Hq,nQB,Dg] and K~ [B,Hkv,nQB,Dg], fp32).  0 for invalid sizes. */
+size_t seer_attn_gate_workspace_size(int B, int Hq, int Hkv, int T, int Dg);
+
+/*
+ * AttnGate soft block scores, the input of seer_build_mask.  The gate pools
+ * along the sequence per 64-token block -- Q by average, K by max and by min,
+ * the two K poolings concatenated along the hidden dimension -- before its
+ * linear layers (rebuttal "SeerAttention: Learning Intrinsic Sparse Attention
+ * in Your LLMs", Weakness 3 and "Question 1 (Theoretical or Intuitive
+ * Explanation for Pooling Selection)"), pools the Q and K from before the
+ * model's RoPE and applies its own block RoPE ("Q1 More about in AttnGate's
+ * RoPE"), and outputs a softmax per row ("Question 2: (Row-Normalization of
+ * Max-Pooled Attention Map)").  With Qp_i = mean of Q's rows in block i and
+ * Kp_j = [max | min] of K's rows in block j:
+ *   Q~_i = rope(Qp_i Wq[h], i),  K~_j = rope(Kp_j Wk[g], j),  g = h / (Hq / Hkv)
+ *   scores[b,h,i,j] = softmax over j' <= i of scale <Q~_i, K~_j'>   (j <= i), 0 (j > i)
+ * rope is the rotate-half rotary embedding over Dg dims, frequencies
+ * rope_base^(-2t/Dg), at the block index.  A short last block pools the rows
+ * it has (torch pooling with ceil_mode, "Weakness 4 (Rounding Issue ...)").
+ *
+ * q, k     device bf16 [B,Hq,T,D] and [B,Hkv,T,D] (before the model's RoPE),
+ *          16-byte aligned; D in {64, 128}; Hq % Hkv == 0.
+ * wq, wk   device fp32 [Hq, D, Dg] and [Hkv, 2D, Dg] (row-major, no bias),
+ *          16-byte aligned.
+ * Dg       32, 64 or 128.
+ * scale    finite and > 0 (1/sqrt(Dg) is the usual choice); rope_base finite
+ *          and > 1 (10000 is the usual choice).
+ * scores   device fp32 out [B, Hq, nQB, nQB].
+ * workspace device, >= seer_attn_gate_workspace_size(B, Hq, Hkv, T, Dg) bytes,
+ *          256-byte aligned; overwritten.
+ * Arithmetic is fp32 (RoPE angles in fp64); results are bit-reproducible.
+ */
+int seer_attn_gate_scores(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
+                          const float* wq, const float* wk, int Dg, float scale, float rope_base,
+                          float* scores, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Row-normalised distillation target and its MSE against gate scores.  The
  * max-pooled map is normalised per row so that, like the gate's softmax

@@ -139,3 +139,22 @@ def test_sparse_prefill_block_rejects_on_host():
     a2[14] = None       # workspace
     assert lib.seer_sparse_prefill_block(*a2) == 4
 
+
+def test_attn_gate_rejects_on_host():
+    lib = seer.load()
+    a = [FAKE, FAKE, 1, 4, 2, 256, 128, FAKE, FAKE, 64, 0.125, 10000.0, FAKE, FAKE, 1 << 20, None]
+    def call(**kw):
+        b = list(a)
+        for i, v in kw.items():
+            b[int(i[1:])] = v
+        return lib.seer_attn_gate_scores(*b)
+    assert call(p6=96) == 2            # head dim
+    assert call(p9=48) == 2            # gate dim
+    assert call(p4=3) == 1             # Hq % Hkv
+    assert call(p10=0.0) == 1          # scale
+    assert call(p11=1.0) == 1          # rope base
+    assert call(p7=None) == 1          # weights
+    assert call(p13=None) == 4         # workspace
+    assert call(p2=0) == 0             # empty
+    assert seer.load().seer_attn_gate_workspace_size(1, 4, 2, 256, 64) >= (4 + 2) * 4 * 64 * 4
+
