@@ -170,8 +170,11 @@ int seer_pooled_attn_map(const void* q, const void* k, const void* v, int B, int
                          int T, int D, float sm_scale, void* o, float* amap, void* workspace,
                          size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace seer_attn_gate_scores needs (the projected,
- * rotated Q~ [B,Hq,nQB,Dg] and K~ [B,Hkv,nQB,Dg], fp32).  0 for invalid sizes. */
+/* Bytes of device workspace seer_attn_gate_scores needs: the pooled Q and K
+ * (fp32 [B,Hq,nQB,D] and [B,Hkv,nQB,2D], sized for D = 128), the projected,
+ * rotated Q~ [B,Hq,nQB,Dg] and K~ [B,Hkv,nQB,Dg] (fp32), and each row's
+ * (max, sum of exponentials) per 64-block tile of keys (fp32 pairs).  0 for
+ * invalid sizes. */
 size_t seer_attn_gate_workspace_size(int B, int Hq, int Hkv, int T, int Dg);
 
 /*
