@@ -22,6 +22,9 @@ What it computes, each function citing the passage it follows:
                  block RoPE and a causal softmax (rebuttal "SeerAttention:
                  Learning Intrinsic Sparse Attention in Your LLMs", Weakness 3
                  and the pooling and RoPE answers).
+* ``decode``  -- block-sparse attention of one new token over a KV cache and its
+                 block selection with a token budget (abstract of "SeerAttention-R:
+                 Sparse Attention Adaptation for Long Reasoning").
 * ``target``  -- the row-normalised map used as the gate's ground truth and the
                  MSE against gate scores (rebuttal "SeerAttention: Learning
                  Intrinsic Sparse Attention in Your LLMs", "Question 2:
@@ -40,11 +43,13 @@ from .attention import (BLOCK, block_probs, allowed_blocks, sparse_attention_ref
 from .pooled import pooled_map_ref, pooled_map_blocks_ref
 from .target import pooled_target_ref
 from .gate import pool_qk, block_rope, gate_qk_ref, gate_scores_ref
+from .decode import decode_blocks, select_decode_row, build_mask_decode_ref, sparse_decode_ref
 
 __all__ = [
     "MODE_THRESHOLD", "MODE_TOPK", "BLOCK", "forced_blocks", "topk_count", "select_row",
     "build_mask_ref", "mask_rows_ref", "block_probs", "allowed_blocks",
     "sparse_attention_ref", "sparse_attention_blocks_ref", "pooled_map_ref",
     "pooled_map_blocks_ref", "pooled_target_ref", "pool_qk", "block_rope", "gate_qk_ref",
-    "gate_scores_ref",
+    "gate_scores_ref", "decode_blocks", "select_decode_row", "build_mask_decode_ref",
+    "sparse_decode_ref",
 ]
