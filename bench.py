@@ -68,11 +68,16 @@ def read_traffic(launch_s: float):
         return None
 
 
-def time_calls(fn, n: int, torch):
+def time_calls(fn, n: int, torch, flush=None):
     """Mean duration (ms) of fn() over n calls, bracketed by events on torch's
-    current stream -- the stream the library launches on."""
+    current stream -- the stream the library launches on.  With `flush` (a 1 GiB
+    fp32 device buffer) it is read before each call, outside the events, so that
+    the call starts with L2 and MALL holding other, clean data (a write would
+    leave dirty lines whose write-back the call would pay for)."""
     evs = []
     for _ in range(n):
+        if flush is not None:
+            flush.sum()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -114,6 +119,69 @@ def cpu_baseline(w, q, k, v, scores, max_k, blocks_per_head: int):
         "sample": (f"{len(rows)} seeded query blocks ({blocks_per_head} per head incl. first and "
                    f"last) of {w.name}: mask rows + fp64 attention, {dt:.1f} s"),
     }
+
+
+def decode_bench(seer, wl, torch, dev, args):
+    import dataclasses
+    import numpy as np
+    dw = wl.DEC1
+    log(f"[bench] decode {dw.name}")
+    q, k, v, kv_len = wl.make_decode_inputs(dw)
+    qd, kd, vd, ld = (t.to(dev) for t in (q, k, v, kv_len))
+    del q, k, v
+    od = torch.empty_like(qd)
+    out = {"workload": dw.name, "batch": dw.batch, "kv_len": dw.kv_lens[0], "block": dw.block,
+           "budget_tokens": dw.budget_tokens, "hbm_peak_gbps": 8000.0}
+    d, g = dw.head_dim, dw.hq // dw.hkv
+    flush = torch.ones((1 << 28,), dtype=torch.float32, device=dev)  # 1 GiB > L2 + 256 MB MALL
+    for var in (dw, wl.DEC2):
+        sc = wl.make_decode_scores(var).to(dev)
+        max_k = min(var.nkb, max(var.k_blocks, 2))
+        idx, cnt = seer.seer_build_mask_decode(sc, ld, var.block, wl.MODE_TOPK, 0.0, var.k_blocks,
+                                               var.keep_sink, max_k)
+        mcall = lambda: seer.seer_build_mask_decode(sc, ld, var.block, wl.MODE_TOPK, 0.0,
+                                                    var.k_blocks, var.keep_sink, max_k,
+                                                    kv_idx=idx, kv_cnt=cnt)
+        wsd = torch.empty((seer.sparse_decode_workspace_size(
+            dw.batch, dw.hq, dw.hkv, dw.tmax, d, var.lh, max_k, var.block),),
+            dtype=torch.uint8, device=dev)
+        call = lambda: seer.seer_sparse_decode(qd, kd, vd, ld, idx, cnt, var.block, out=od,
+                                               workspace=wsd)
+        call()
+        m_ms = time_calls(mcall, max(5, args.steps), torch, flush)
+        d_ms = time_calls(call, max(5, args.steps), torch, flush)
+        # Blocks each KV group reads: the union of its heads' lists.
+        ii, cc = idx.cpu().numpy(), cnt.cpu().numpy()
+        tokens = 0
+        for b in range(dw.batch):
+            for grp in range(dw.hkv):
+                heads = range(grp * g, grp * g + g) if var.lh == dw.hq else [grp]
+                blocks = {int(j) for h in heads for j in ii[b, h, : cc[b, h]]}
+                tokens += sum(min(var.block, dw.kv_lens[b] - j * var.block) for j in blocks)
+        nbytes = tokens * d * 2 * 2 + 2 * 2 * qd.numel() + 4 * (idx.numel() + cnt.numel())
+        key = "lists_per_kv_head" if var.lh == dw.hkv else "lists_per_q_head"
+        out[key] = {"mask_ms": round(m_ms, 4), "decode_ms": round(d_ms, 4),
+                    "algorithmic_bytes": nbytes,
+                    "gbps": round(nbytes / (d_ms * 1e-3) / 1e9, 1)}
+        del sc, idx, cnt, wsd
+    # The same kernel with every block listed (dense decode) for the speedup.
+    dense = dataclasses.replace(dw, wid=13)
+    nkb = dense.nkb
+    idx = torch.arange(nkb, dtype=torch.int32, device=dev).repeat(dw.batch, dw.hkv, 1).contiguous()
+    cnt = torch.full((dw.batch, dw.hkv), nkb, dtype=torch.int32, device=dev)
+    wsd = torch.empty((seer.sparse_decode_workspace_size(dw.batch, dw.hq, dw.hkv, dw.tmax, d,
+                                                         dw.hkv, nkb, dw.block),),
+                      dtype=torch.uint8, device=dev)
+    call = lambda: seer.seer_sparse_decode(qd, kd, vd, ld, idx, cnt, dw.block, out=od,
+                                           workspace=wsd)
+    call()
+    dn_ms = time_calls(call, max(3, args.steps // 2), torch, flush)
+    dn_bytes = sum(dw.kv_lens) * dw.hkv * d * 2 * 2 + 2 * 2 * qd.numel()
+    out["dense"] = {"decode_ms": round(dn_ms, 4),
+                    "gbps": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)}
+    out["speedup_vs_dense"] = round(dn_ms / out["lists_per_kv_head"]["decode_ms"], 3)
+    del qd, kd, vd, ld, od, idx, cnt, wsd, flush
+    return out
 
 
 def main(argv=None) -> int:
@@ -349,6 +417,12 @@ def main(argv=None) -> int:
             "tflops": round(tiles128 * tile_flops(w.head_dim) / (b128_ms * 1e-3) / 1e12, 3),
         }
         del s128, idx128, cnt128
+
+        # Decode: one new token per sequence over a 40k-token cache, 4K-token budget
+        # (90 % sparsity), lists per KV group and per query head.  HBM-bound: the
+        # algorithmic bytes are the K and V rows of each KV group's selected blocks
+        # (read once per group), plus q, o and the lists.
+        result["decode"] = decode_bench(seer, wl, torch, dev, args)
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")

@@ -25,7 +25,8 @@ EXPORTED = (
     "seer_status_string", "seer_version", "seer_topk_budget", "seer_build_mask",
     "seer_sparse_prefill_workspace_size", "seer_sparse_prefill", "seer_sparse_prefill_block",
     "seer_pooled_attn_map_workspace_size", "seer_pooled_attn_map", "seer_pooled_target_mse",
-    "seer_attn_gate_workspace_size", "seer_attn_gate_scores",
+    "seer_attn_gate_workspace_size", "seer_attn_gate_scores", "seer_build_mask_decode",
+    "seer_sparse_decode_workspace_size", "seer_sparse_decode",
 )
 
 _lib = None
@@ -82,6 +83,15 @@ def load() -> ctypes.CDLL:
     lib.seer_pooled_target_mse.restype = c_int
     lib.seer_pooled_target_mse.argtypes = [c_void, c_void, c_int, c_int, c_int, c_void, c_void,
                                            c_void, c_void]
+    lib.seer_build_mask_decode.restype = c_int
+    lib.seer_build_mask_decode.argtypes = [c_void, c_void, c_int, c_int, c_int, c_int, c_int,
+                                           c_float, c_int, c_int, c_void, c_void, c_int, c_void]
+    lib.seer_sparse_decode_workspace_size.restype = c_size
+    lib.seer_sparse_decode_workspace_size.argtypes = [c_int] * 8
+    lib.seer_sparse_decode.restype = c_int
+    lib.seer_sparse_decode.argtypes = [c_void, c_void, c_void, c_void, c_int, c_int, c_int, c_int,
+                                       c_int, c_float, c_int, c_void, c_void, c_int, c_int,
+                                       c_void, c_void, c_size, c_void]
     _lib = lib
     return lib
 
@@ -284,3 +294,63 @@ def seer_attn_gate_scores(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor, wk
         _stream(stream)))
     return scores
 
+
+
+def seer_build_mask_decode(scores: torch.Tensor, kv_len: torch.Tensor, block: int, mode: int,
+                           threshold: float, k_blocks: int, keep_sink: bool, max_k: int,
+                           kv_idx: Optional[torch.Tensor] = None,
+                           kv_cnt: Optional[torch.Tensor] = None, stream=None):
+    """Decode lists: scores fp32 [B,H,nKB], kv_len int32 [B] ->
+    (kv_idx int32 [B,H,max_k], kv_cnt int32 [B,H])."""
+    lib = load()
+    b, h, nkb = scores.shape
+    _need(scores, "scores", torch.float32, (b, h, nkb))
+    _need(kv_len, "kv_len", torch.int32, (b,))
+    if kv_idx is None:
+        kv_idx = torch.empty((b, h, max_k), dtype=torch.int32, device=scores.device)
+    if kv_cnt is None:
+        kv_cnt = torch.empty((b, h), dtype=torch.int32, device=scores.device)
+    _need(kv_idx, "kv_idx", torch.int32, (b, h, max_k))
+    _need(kv_cnt, "kv_cnt", torch.int32, (b, h))
+    _check("seer_build_mask_decode", lib.seer_build_mask_decode(
+        _ptr(scores), _ptr(kv_len), b, h, nkb, int(block), int(mode), float(threshold),
+        int(k_blocks), int(bool(keep_sink)), _ptr(kv_idx), _ptr(kv_cnt), int(max_k),
+        _stream(stream)))
+    return kv_idx, kv_cnt
+
+
+def sparse_decode_workspace_size(b: int, hq: int, hkv: int, tmax: int, d: int, list_heads: int,
+                                 max_k: int, block: int) -> int:
+    return load().seer_sparse_decode_workspace_size(b, hq, hkv, tmax, d, list_heads, max_k,
+                                                    block)
+
+
+def seer_sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       kv_len: torch.Tensor, kv_idx: torch.Tensor, kv_cnt: torch.Tensor,
+                       block: int = BLOCK, sm_scale: Optional[float] = None,
+                       out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Block-sparse decode: q [B,Hq,D], cache [B,Hkv,Tmax,D] (bf16), kv_len int32 [B],
+    lists [B,H,max_k] / [B,H] with H = Hq or Hkv -> O bf16 [B,Hq,D]."""
+    lib = load()
+    b, hq, d = q.shape
+    hkv, tmax = k_cache.shape[1], k_cache.shape[2]
+    _need(q, "q", torch.bfloat16, (b, hq, d))
+    _need(k_cache, "k_cache", torch.bfloat16, (b, hkv, tmax, d))
+    _need(v_cache, "v_cache", torch.bfloat16, (b, hkv, tmax, d))
+    _need(kv_len, "kv_len", torch.int32, (b,))
+    lh, max_k = kv_idx.shape[1], kv_idx.shape[2]
+    _need(kv_idx, "kv_idx", torch.int32, (b, lh, max_k))
+    _need(kv_cnt, "kv_cnt", torch.int32, (b, lh))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, (b, hq, d))
+    if workspace is None:
+        workspace = _workspace(sparse_decode_workspace_size(b, hq, hkv, tmax, d, lh, max_k,
+                                                            int(block)), q.device)
+    scale = (1.0 / d ** 0.5) if sm_scale is None else float(sm_scale)
+    _check("seer_sparse_decode", lib.seer_sparse_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), b, hq, hkv, tmax, d, scale,
+        int(block), _ptr(kv_idx), _ptr(kv_cnt), lh, max_k, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out

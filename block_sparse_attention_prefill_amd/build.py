@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libseer.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "build_mask.hip", "attention.hip", "pooled_target.hip", "attn_gate.hip"]
+SOURCES = ["api.cpp", "build_mask.hip", "attention.hip", "pooled_target.hip", "attn_gate.hip", "decode.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

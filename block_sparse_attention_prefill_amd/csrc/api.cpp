@@ -186,4 +186,79 @@ int seer_attn_gate_scores(const void* q, const void* k, int B, int Hq, int Hkv, 
   return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
 }
 
+int seer_build_mask_decode(const float* scores, const int32_t* kv_len, int B, int H, int nKB,
+                           int block, int mode, float threshold, int k_blocks, int keep_sink,
+                           int32_t* kv_idx, int32_t* kv_cnt, int max_k, void* stream) {
+  if (B < 0 || H < 0 || nKB < 0) return SEER_ERR_INVALID_ARG;
+  if (block != 64 && block != 128) return SEER_ERR_UNSUPPORTED;
+  if (nKB > SEER_MAX_QUERY_BLOCKS) return SEER_ERR_UNSUPPORTED;
+  if (mode != SEER_MASK_TOPK && mode != SEER_MASK_THRESHOLD) return SEER_ERR_INVALID_ARG;
+  if (!items_fit(B, H, 1)) return SEER_ERR_UNSUPPORTED;
+  if (mode == SEER_MASK_TOPK && k_blocks < 1) return SEER_ERR_INVALID_ARG;
+  if (mode == SEER_MASK_THRESHOLD && !isfinite(threshold)) return SEER_ERR_INVALID_ARG;
+  if (max_k < 1) return SEER_ERR_CAPACITY;
+  if ((long long)B * H == 0) return SEER_OK;
+  if (!scores || !kv_len || !kv_idx || !kv_cnt) return SEER_ERR_INVALID_ARG;
+  const int forced = keep_sink ? 2 : 1;
+  if (mode == SEER_MASK_TOPK) {
+    const int want = k_blocks > forced ? k_blocks : forced;
+    if (max_k < (want < nKB ? want : nKB)) return SEER_ERR_CAPACITY;
+  } else {
+    if (max_k < ((keep_sink && nKB > 1) ? 2 : 1)) return SEER_ERR_CAPACITY;
+  }
+  const hipError_t err = seer::launch_build_mask_decode(
+      scores, kv_len, B, H, nKB, block, mode, threshold, k_blocks, keep_sink ? 1 : 0, kv_idx,
+      kv_cnt, max_k, (hipStream_t)stream);
+  return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
+}
+
+namespace {
+
+// Checks shared by the decode workspace size and the decode call.
+int decode_sizes(int B, int Hq, int Hkv, int Tmax, int D, int list_heads, int max_k, int block) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Tmax < 1 || max_k < 1) return SEER_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return SEER_ERR_INVALID_ARG;
+  if (list_heads != Hq && list_heads != Hkv) return SEER_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return SEER_ERR_UNSUPPORTED;
+  if (block != 64 && block != 128) return SEER_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 8) return SEER_ERR_UNSUPPORTED;
+  if ((Tmax + (long long)block - 1) / block > 32768) return SEER_ERR_UNSUPPORTED;
+  if ((long long)B * Hq * max_k > (long long)INT_MAX) return SEER_ERR_UNSUPPORTED;
+  if (seer::sparse_decode_grid(B, Hq, Hkv, Tmax, D, list_heads, max_k, block) > INT_MAX)
+    return SEER_ERR_UNSUPPORTED;
+  return SEER_OK;
+}
+
+}  // namespace
+
+size_t seer_sparse_decode_workspace_size(int B, int Hq, int Hkv, int Tmax, int D,
+                                         int list_heads, int max_k, int block) {
+  if (decode_sizes(B, Hq, Hkv, Tmax, D, list_heads, max_k, block) != SEER_OK) return 0;
+  return seer::sparse_decode_workspace_bytes(B, Hq, Hkv, Tmax, D, list_heads, max_k, block) +
+         256;
+}
+
+int seer_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* kv_len, int B, int Hq, int Hkv, int Tmax, int D,
+                       float sm_scale, int block, const int32_t* kv_idx, const int32_t* kv_cnt,
+                       int list_heads, int max_k, void* o, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  const int st = decode_sizes(B, Hq, Hkv, Tmax, D, list_heads, max_k, block);
+  if (st != SEER_OK) return st;
+  if (!(isfinite(sm_scale) && sm_scale > 0.f)) return SEER_ERR_INVALID_ARG;
+  if (B == 0) return SEER_OK;
+  if (!q || !k_cache || !v_cache || !kv_len || !kv_idx || !kv_cnt || !o)
+    return SEER_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return SEER_ERR_INVALID_ARG;
+  const size_t need = seer_sparse_decode_workspace_size(B, Hq, Hkv, Tmax, D, list_heads, max_k,
+                                                        block);
+  if (!workspace || workspace_bytes < need || !aligned256(workspace)) return SEER_ERR_WORKSPACE;
+  const hipError_t err = seer::launch_sparse_decode(q, k_cache, v_cache, kv_len, B, Hq, Hkv,
+                                                    Tmax, D, sm_scale, block, kv_idx, kv_cnt,
+                                                    list_heads, max_k, o, workspace,
+                                                    (hipStream_t)stream);
+  return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
+}
+
 }  // extern "C"

@@ -15,6 +15,12 @@
 // toward lower block indices by a running count in index order, which is also
 // the output order, so each list comes out ascending without a sort.
 //
+// Decode rows (one per sequence and head, the new token's row) use the same
+// rule over the blocks holding the sequence's kv_len tokens: the last of them,
+// which holds the token itself, takes the diagonal's place, and TopK keeps a
+// fixed number of blocks (a token budget over the block size) instead of a
+// density of the row.
+//
 // One wave64 owns one row.  Row i's candidates sit in registers, candidate
 // j = 64 * c + lane in slot c, so the score row is read from HBM once and the
 // compaction is a ballot + popcount per 64 candidates.  The digit histograms
@@ -60,14 +66,20 @@ template <int NPL>
 __global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
     const float* __restrict__ scores, long long rows, int nqb, int nkb, int mode, float tau,
     double density, int keep_sink, int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
-    int max_k) {
+    int max_k, const int32_t* __restrict__ kv_len, int heads, int block, int k_blocks) {
   __shared__ int hist_all[kWavesPerGroup][256];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const long long row = (long long)blockIdx.x * kWavesPerGroup + wv;
   if (row >= rows) return;
   int* hist = hist_all[wv];
-  const int i = (int)(row % nqb);
+  int i;  // last candidate block of the row (-1: no candidate)
+  if (kv_len) {
+    const int len = kv_len[row / heads];
+    i = len > 0 ? min((len - 1) / block, nkb - 1) : -1;
+  } else {
+    i = (int)(row % nqb);
+  }
   const int n = i + 1;
   const float* srow = scores + row * (long long)nkb;
   int32_t* out = idx + row * (long long)max_k;
@@ -94,8 +106,8 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
   int k;
   if (mode == 1) {
     const int forced = (i == 0) ? 1 : (keep_sink ? 2 : 1);
-    const double cf = ceil(density * (double)(i + 1));
-    k = min(i + 1, max(forced, (int)cf));
+    const int want = kv_len ? k_blocks : (int)ceil(density * (double)(i + 1));
+    k = min(i + 1, max(forced, want));
   } else {
     k = min(npos, max_k);
   }
@@ -167,25 +179,45 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
 
 }  // namespace
 
+namespace {
+
+hipError_t launch_rows(const float* scores, long long rows, int nqb, int nkb, int row_len,
+                       int mode, float threshold, double density, int keep_sink, int32_t* idx,
+                       int32_t* cnt, int max_k, const int32_t* kv_len, int heads, int block,
+                       int k_blocks, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + kWavesPerGroup - 1) / kWavesPerGroup));
+  const dim3 threads(64 * kWavesPerGroup);
+#define SEER_MASK_LAUNCH(NPL)                                                                  \
+  hipLaunchKernelGGL(build_mask_kernel<NPL>, grid, threads, 0, stream, scores, rows, nqb, nkb, \
+                     mode, threshold, density, keep_sink, idx, cnt, max_k, kv_len, heads,      \
+                     block, k_blocks)
+  if (row_len <= 64 * 1) SEER_MASK_LAUNCH(1);
+  else if (row_len <= 64 * 4) SEER_MASK_LAUNCH(4);
+  else if (row_len <= 64 * 8) SEER_MASK_LAUNCH(8);
+  else if (row_len <= 64 * 16) SEER_MASK_LAUNCH(16);
+  else if (row_len <= 64 * 32) SEER_MASK_LAUNCH(32);
+  else if (row_len <= 64 * 64) SEER_MASK_LAUNCH(64);
+  else return hipErrorInvalidValue;  // the host layer rejects rows over 4096 blocks first
+#undef SEER_MASK_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_build_mask(const float* scores, int B, int H, int nqb, int nkb, int mode,
                              float threshold, double density, int keep_sink, int32_t* idx,
                              int32_t* cnt, int max_k, hipStream_t stream) {
-  const long long rows = (long long)B * H * nqb;
-  if (rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)((rows + kWavesPerGroup - 1) / kWavesPerGroup));
-  const dim3 block(64 * kWavesPerGroup);
-#define SEER_MASK_LAUNCH(NPL)                                                                  \
-  hipLaunchKernelGGL(build_mask_kernel<NPL>, grid, block, 0, stream, scores, rows, nqb, nkb,   \
-                     mode, threshold, density, keep_sink, idx, cnt, max_k)
-  if (nqb <= 64 * 1) SEER_MASK_LAUNCH(1);
-  else if (nqb <= 64 * 4) SEER_MASK_LAUNCH(4);
-  else if (nqb <= 64 * 8) SEER_MASK_LAUNCH(8);
-  else if (nqb <= 64 * 16) SEER_MASK_LAUNCH(16);
-  else if (nqb <= 64 * 32) SEER_MASK_LAUNCH(32);
-  else if (nqb <= 64 * 64) SEER_MASK_LAUNCH(64);
-  else return hipErrorInvalidValue;  // the host layer rejects nQB > 4096 first
-#undef SEER_MASK_LAUNCH
-  return hipGetLastError();
+  return launch_rows(scores, (long long)B * H * nqb, nqb, nkb, nqb, mode, threshold, density,
+                     keep_sink, idx, cnt, max_k, nullptr, 1, 64, 0, stream);
+}
+
+hipError_t launch_build_mask_decode(const float* scores, const int32_t* kv_len, int B, int H,
+                                    int nkb, int block, int mode, float threshold, int k_blocks,
+                                    int keep_sink, int32_t* idx, int32_t* cnt, int max_k,
+                                    hipStream_t stream) {
+  return launch_rows(scores, (long long)B * H, 1, nkb, nkb, mode, threshold, 1.0, keep_sink, idx,
+                     cnt, max_k, kv_len, H, block, k_blocks, stream);
 }
 
 }  // namespace seer

@@ -1,0 +1,490 @@
+// Block-sparse decode: the one new token of each sequence attends to the listed
+// KV blocks of a cache.  The abstract of "SeerAttention-R: Sparse Attention
+// Adaptation for Long Reasoning" carries the learned block sparsity over to
+// auto-regressive decoding with a token budget and sparse-attention blocks of
+// 64 or 128 tokens; the attention itself is the one of the rebuttal's
+// "Weakness 5 (Pseudo code of Inference Kernel)" for a single query row.
+//
+// Decode reads every selected K/V byte once and does little arithmetic with
+// it, so the kernels are built around HBM streaming:
+// * The work of one (sequence, KV group) is a list of blocks: the group's own
+//   list when its query heads share one, else the union of the heads' lists
+//   with a mask of the heads that chose each block (decode_union_kernel), so a
+//   block is read once for the whole group.
+// * decode_attn_kernel splits that list into chunks of a few blocks.  Its
+//   workgroup streams the chunk's 64-token tiles (next tile's loads in flight
+//   while the current one is used); each of the four waves owns 16 keys of
+//   every tile and keeps its own online-softmax state, so the loop needs no
+//   barrier:
+//     S^T (16 keys x 16 head slots) = K . Q^T with v_mfma_f32_16x16x32_bf16,
+//       K rows loaded from HBM straight into the MFMA operand layout;
+//     exp2-domain online softmax per head, rescale only when a max moves;
+//     acc[head][8 dims] += P . V on the VALU, v_dot2_f32_bf16 over key pairs,
+//       V rows loaded coalesced and paired with v_perm.
+//   The waves' states are merged in LDS into one partial (m, l, acc) per head.
+// * decode_combine_kernel merges the chunk partials of each query head.
+#include "seer_internal.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace seer {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kUnionThreads = 256;
+constexpr int kDecThreads = 256;  // four waves
+constexpr int kDecTile = 64;      // tokens per tile; each wave owns 16 of them
+constexpr int kDecTileTokensPerWg = 256;  // tokens of listed blocks per workgroup chunk
+constexpr int kMaxChunkTiles = 16;        // upper bound of kDecTileTokensPerWg / kDecTile
+constexpr int kCombineThreads = 256;
+
+// ---------------------------------------------------------------------------
+// Union of a KV group's per-head lists, in ascending block order.  Entry =
+// block | (mask of the group's heads that listed it) << 24.  Entries outside
+// [0, nb) are dropped.  One workgroup per (sequence, KV group); the flags live
+// in LDS, one byte per block of the cache.
+__global__ __launch_bounds__(kUnionThreads) void decode_union_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
+    const int32_t* __restrict__ kv_len, int Hkv, int G, int Tmax, int bs, int max_k, int umax,
+    int32_t* __restrict__ uni, int32_t* __restrict__ ucnt) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t flags[];
+  __shared__ int wtot[kUnionThreads / 64];
+  const int bg = blockIdx.x;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int len = min(max(kv_len[b], 0), Tmax);
+  const int nb = len > 0 ? (len - 1) / bs + 1 : 0;
+  uint32_t* fw = reinterpret_cast<uint32_t*>(flags);
+  for (int x = tid; x < (nb + 3) / 4; x += kUnionThreads) fw[x] = 0u;
+  __syncthreads();
+  for (int h = 0; h < G; ++h) {
+    const size_t row = (size_t)b * Hkv * G + (size_t)g * G + h;  // list row of query head
+    const int n = min(max(cnt[row], 0), max_k);
+    // A list holds each block at most once, so no two lanes update the same byte.
+    for (int x = tid; x < n; x += kUnionThreads) {
+      const int j = idx[row * max_k + x];
+      if (j >= 0 && j < nb) flags[j] = (uint8_t)(flags[j] | (1u << h));
+    }
+    __syncthreads();
+  }
+  // Thread t compacts blocks [lo, hi) after an exclusive scan of the counts.
+  const int per = (nb + kUnionThreads - 1) / kUnionThreads;
+  const int lo = min(tid * per, nb), hi = min(lo + per, nb);
+  int c = 0;
+  for (int j = lo; j < hi; ++j) c += flags[j] != 0;
+  int incl = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wtot[wv] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int x = 0; x < kUnionThreads / 64; ++x) {
+    base += x < wv ? wtot[x] : 0;
+    total += wtot[x];
+  }
+  int pos = base + incl - c;
+  int32_t* out = uni + (size_t)bg * umax;
+  for (int j = lo; j < hi; ++j)
+    if (flags[j]) out[pos++] = j | ((int)flags[j] << 24);
+  if (tid == 0) ucnt[bg] = total;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA row i of a wave's S^T tile is key kappa(i) of the wave's 16 keys, chosen
+// so that the 4 accumulator rows a lane receives (rows 4(l/16) .. +3) are keys
+// l/16 + 4v: exactly the key rows that lane later needs for P . V.
+__device__ __forceinline__ int kappa(int i) { return (i >> 2) + 4 * (i & 3); }
+
+template <int D, int GM, bool UNION>
+__global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
+    const int32_t* __restrict__ kv_len, int Hkv, int G, int Tmax, float c2, int bs,
+    const int32_t* __restrict__ list, const int32_t* __restrict__ lcnt, int lstride, int chunk,
+    int nsplit, float* __restrict__ part_ml, float* __restrict__ part_acc) {
+  constexpr int KK = D / 32;        // MFMA k-steps
+  constexpr int C8 = D / 8;         // 16-byte chunks per row
+  constexpr int NR = C8 / 4;        // V rows per lane (4 at D 128, 2 at D 64)
+  constexpr int SUBS = 4 / NR;      // lanes sharing one S lane-group's keys
+  __shared__ __attribute__((aligned(16))) float red_acc[4][GM][D];
+  __shared__ float red_m[4][GM], red_l[4][GM];
+  __shared__ __attribute__((aligned(16))) uint16_t p_lds[4][16][16];  // [wave][head][slot]
+  __shared__ __attribute__((aligned(16))) float a_lds[4][16];
+  __shared__ int t_pos[kMaxChunkTiles];
+  __shared__ uint32_t t_mask[kMaxChunkTiles];
+  __shared__ int t_num;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = blockIdx.x % nsplit;
+  const int bg = blockIdx.x / nsplit;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int U = UNION ? lcnt[bg] : min(max(lcnt[bg], 0), lstride);
+  const int e0 = s * chunk;
+  if (e0 >= U) return;  // the combine step reads only chunks below U
+  const int len = min(max(kv_len[b], 0), Tmax);
+  const int nb = len > 0 ? (len - 1) / bs + 1 : 0;
+  const int32_t* lrow = list + (size_t)bg * lstride;
+  const uint32_t all_heads = (1u << G) - 1u;
+  const __bf16* kbase = kc + (size_t)bg * Tmax * D;
+  const __bf16* vbase = vc + (size_t)bg * Tmax * D;
+
+  // Wave 0 turns the chunk's entries into its list of 64-token tiles (entry
+  // order, then sub-tile order), in LDS for all waves.
+  if (w == 0) {
+    const int per = bs / kDecTile;  // tiles per listed block
+    const int e = e0 + lane / per, t = lane % per;
+    int pos = -1;
+    uint32_t mask = 0u;
+    if (lane < chunk * per && e < U) {
+      const int v = lrow[e];
+      const int j = UNION ? (v & 0xFFFFFF) : v;
+      if (j >= 0 && j < nb && j * bs + kDecTile * t < len) {
+        pos = j * bs + kDecTile * t;
+        mask = UNION ? ((uint32_t)v >> 24) : all_heads;
+      }
+    }
+    const uint64_t valid = __ballot(pos >= 0);
+    if (pos >= 0) {
+      const int slot = __builtin_amdgcn_mbcnt_hi((uint32_t)(valid >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)valid, 0u));
+      t_pos[slot] = pos;
+      t_mask[slot] = mask;
+    }
+    if (lane == 0) t_num = __popcll(valid);
+  }
+  __syncthreads();
+  const int ntiles = t_num;
+
+  // Q^T as the MFMA B operand: lane l holds head l % 16, dims 8 (l / 16) + 32 kk.
+  const int hs = lane & 15, kg = lane >> 4;
+  bf16x8 qb[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    qb[kk] = bf16x8{};
+    if (hs < G)
+      qb[kk] = *reinterpret_cast<const bf16x8*>(q + ((size_t)bg * G + hs) * D + 8 * kg + 32 * kk);
+  }
+  // P . V lane layout: dims 8 pc .. 8 pc + 7; keys pg + 4 (NR psub + i), i < NR.
+  const int pc = lane % C8, pq = lane / C8;
+  const int pg = pq / SUBS, psub = pq % SUBS;
+  const int ks_key = kappa(hs);  // this lane's K row for the S^T operand
+
+  float m_run = -INFINITY, l_run = 0.f;  // per head hs (replicated over kg)
+  float acc[GM][8];
+#pragma unroll
+  for (int h = 0; h < GM; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+
+  // Rows past the sequence load its last row instead (in bounds, finite); their
+  // logits are masked to -inf, so they get P = 0.
+  auto load = [&](bf16x8 (&kr)[KK], bf16x8 (&vr)[NR], int pos) {
+    const int krow = min(pos + 16 * w + ks_key, len - 1);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      kr[kk] = *reinterpret_cast<const bf16x8*>(kbase + (size_t)krow * D + 8 * kg + 32 * kk);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int vrow = min(pos + 16 * w + pg + 4 * (NR * psub + i), len - 1);
+      vr[i] = *reinterpret_cast<const bf16x8*>(vbase + (size_t)vrow * D + 8 * pc);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the previous tile's math
+  };
+  auto compute = [&](bf16x8 (&kr)[KK], bf16x8 (&vr)[NR], int pos, uint32_t mask) {
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk], qb[kk], sa, 0, 0, 0);
+    // Lane: head hs, keys kg + 4 v of the wave's 16.
+    const bool hv = hs < G && ((mask >> hs) & 1u);
+    const int key0 = pos + 16 * w + kg;
+    float sv[4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      sv[v] = (hv && key0 + 4 * v < len) ? sa[v] * c2 : -INFINITY;
+      tmax = fmaxf(tmax, sv[v]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    uint16_t pb[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const __bf16 p = (__bf16)__builtin_amdgcn_exp2f(sv[v] - m_use);
+      pb[v] = __builtin_bit_cast(uint16_t, p);
+      psum += (float)p;
+    }
+    l_run = alpha * l_run + psum;
+    const bool moved = m_new != m_run;
+    m_run = m_new;
+    const uint64_t rescale = __ballot(hs < G && moved);
+    asm volatile("" ::: "memory");
+    *reinterpret_cast<uint64_t*>(&p_lds[w][hs][4 * kg]) =
+        (uint64_t)(pb[0] | ((uint32_t)pb[1] << 16)) |
+        ((uint64_t)(pb[2] | ((uint32_t)pb[3] << 16)) << 32);
+    if (lane < 16) a_lds[w][lane] = alpha;
+    asm volatile("" ::: "memory");
+    if (rescale) {
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        if (h < G) {
+          const float a = a_lds[w][h];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] *= a;
+        }
+      }
+    }
+    // Pairs of key rows (i, i + 1): v_perm builds (V[r0][d], V[r1][d]) per dim.
+#pragma unroll
+    for (int i = 0; i < NR; i += 2) {
+      const u32x4 a0 = __builtin_bit_cast(u32x4, vr[i]);
+      const u32x4 a1 = __builtin_bit_cast(u32x4, vr[i + 1]);
+      uint32_t xv[8];
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd) {
+        xv[2 * dd] = __builtin_amdgcn_perm(a1[dd], a0[dd], 0x05040100u);
+        xv[2 * dd + 1] = __builtin_amdgcn_perm(a1[dd], a0[dd], 0x07060302u);
+      }
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        if (h < G) {
+          const uint32_t pp = *reinterpret_cast<const uint32_t*>(
+              &p_lds[w][h][4 * pg + NR * psub + i]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            acc[h][e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp),
+                                                        __builtin_bit_cast(bf16x2, xv[e]),
+                                                        acc[h][e], false);
+        }
+      }
+    }
+    asm volatile("" ::: "memory");
+  };
+
+  // Two register buffers; the next tile's loads are always issued and both
+  // halves always run (an odd count computes the last tile again with no head
+  // selected, which leaves the state unchanged), so no load sits on a
+  // conditional path and every wait is on the oldest buffer only.
+  bf16x8 k0[KK], v0[NR], k1[KK], v1[NR];
+  if (ntiles > 0) load(k0, v0, t_pos[0]);
+  for (int n = 0; n < ntiles; n += 2) {
+    const int n1 = min(n + 1, ntiles - 1);
+    const int pos1 = t_pos[n1];
+    const uint32_t mask1 = n + 1 < ntiles ? t_mask[n1] : 0u;
+    load(k1, v1, pos1);
+    compute(k0, v0, t_pos[n], t_mask[n]);
+    load(k0, v0, t_pos[min(n + 2, ntiles - 1)]);
+    compute(k1, v1, pos1, mask1);
+  }
+
+  // Merge inside the wave (lanes with the same dims / the same head), then
+  // across the four waves in LDS.
+#pragma unroll
+  for (int off = C8; off < 64; off <<= 1)
+#pragma unroll
+    for (int h = 0; h < GM; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (lane < C8) {
+#pragma unroll
+    for (int h = 0; h < GM; ++h)
+      if (h < G) {
+        *reinterpret_cast<f32x4*>(&red_acc[w][h][8 * lane]) =
+            f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+        *reinterpret_cast<f32x4*>(&red_acc[w][h][8 * lane + 4]) =
+            f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+      }
+  }
+  if (lane < G) {
+    red_m[w][lane] = m_run;
+    red_l[w][lane] = l_run;
+  }
+  __syncthreads();
+  const size_t slot = ((size_t)bg * nsplit + s) * G;
+  for (int x = tid; x < G * D; x += kDecThreads) {
+    const int h = x / D, d = x % D;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, red_m[ww][h]);
+    float a = 0.f, l = 0.f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float f = __builtin_amdgcn_exp2f(red_m[ww][h] - mm);  // 0 for an empty wave
+        a = fmaf(f, red_acc[ww][h][d], a);
+        l = fmaf(f, red_l[ww][h], l);
+      }
+    }
+    part_acc[(slot + h) * D + d] = a;
+    if (d == 0) {
+      part_ml[2 * (slot + h)] = mm;
+      part_ml[2 * (slot + h) + 1] = l;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup per (sequence, query head) merges the chunk partials: thread t
+// reads 4 dims (t % (D/4)) of chunks s = t / (D/4) + SG n, all loads of a
+// thread independent; the SG groups are then summed in LDS in a fixed order.
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
+    const float* __restrict__ part_ml, const float* __restrict__ part_acc,
+    const int32_t* __restrict__ lcnt, int lstride, bool is_union, int Hq, int Hkv, int chunk,
+    int nsplit, __bf16* __restrict__ o) {
+  constexpr int TPS = D / 4;                   // threads per chunk row
+  constexpr int SG = kCombineThreads / TPS;    // chunk rows read at once
+  __shared__ __attribute__((aligned(16))) float red[SG][D];
+  __shared__ float redl[SG], redm[kCombineThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int item = blockIdx.x;  // b * Hq + hq
+  const int G = Hq / Hkv;
+  const int b = item / Hq, hq = item % Hq;
+  const int bg = b * Hkv + hq / G, h = hq % G;
+  const int U = is_union ? lcnt[bg] : min(max(lcnt[bg], 0), lstride);
+  const int ns = min((U + chunk - 1) / chunk, nsplit);
+  const size_t base = (size_t)bg * nsplit * G + h;  // slot of chunk s: base + s * G
+  float mm = -INFINITY;
+  for (int s = tid; s < ns; s += kCombineThreads) mm = fmaxf(mm, part_ml[2 * (base + (size_t)s * G)]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 64));
+  if (lane == 0) redm[tid >> 6] = mm;
+  __syncthreads();
+  mm = fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3]));
+  const int c4 = tid % TPS, sg = tid / TPS;
+  f32x4 a = {0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  if (mm != -INFINITY) {
+#pragma unroll 4
+    for (int s = sg; s < ns; s += SG) {
+      const size_t slot = base + (size_t)s * G;
+      const float f = __builtin_amdgcn_exp2f(part_ml[2 * slot] - mm);  // 0 for an empty chunk
+      const f32x4 x = *reinterpret_cast<const f32x4*>(part_acc + slot * D + 4 * c4);
+      a += f * x;
+      l = fmaf(f, part_ml[2 * slot + 1], l);
+    }
+  }
+  *reinterpret_cast<f32x4*>(&red[sg][4 * c4]) = a;
+  if (c4 == 0) redl[sg] = l;
+  __syncthreads();
+  if (tid < D) {
+    float acc = 0.f, ls = 0.f;
+#pragma unroll
+    for (int x = 0; x < SG; ++x) {
+      acc += red[x][tid];
+      ls += redl[x];
+    }
+    o[(size_t)item * D + tid] = (__bf16)(ls > 0.f ? acc / ls : 0.f);
+  }
+}
+
+struct DecodePlan {
+  bool is_union;
+  int gm, umax, lstride, chunk, nsplit;
+  size_t off_ucnt, off_ml, off_acc, bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+DecodePlan plan_decode(int B, int Hq, int Hkv, int Tmax, int D, int list_heads, int max_k,
+                       int bs) {
+  DecodePlan p{};
+  const int G = Hq / Hkv;
+  const int nbmax = (Tmax + bs - 1) / bs;
+  p.is_union = list_heads == Hq && G > 1;
+  p.gm = G <= 4 ? 4 : 8;
+  p.umax = p.is_union ? (int)std::min<long long>((long long)G * max_k, nbmax) : max_k;
+  p.lstride = p.umax;
+  p.chunk = std::max(1, kDecTileTokensPerWg / bs);
+  p.nsplit = std::max(1, (p.umax + p.chunk - 1) / p.chunk);
+  const size_t groups = (size_t)B * Hkv;
+  size_t off = p.is_union ? align256(groups * p.umax * sizeof(int32_t)) : 0;
+  p.off_ucnt = off;
+  off += p.is_union ? align256(groups * sizeof(int32_t)) : 0;
+  p.off_ml = off;
+  off += align256(groups * p.nsplit * G * 2 * sizeof(float));
+  p.off_acc = off;
+  off += align256(groups * p.nsplit * G * (size_t)D * sizeof(float));
+  p.bytes = off;
+  return p;
+}
+
+}  // namespace
+
+size_t sparse_decode_workspace_bytes(int B, int Hq, int Hkv, int Tmax, int D, int list_heads,
+                                     int max_k, int block) {
+  return plan_decode(B, Hq, Hkv, Tmax, D, list_heads, max_k, block).bytes;
+}
+
+long long sparse_decode_grid(int B, int Hq, int Hkv, int Tmax, int D, int list_heads, int max_k,
+                             int block) {
+  const DecodePlan p = plan_decode(B, Hq, Hkv, Tmax, D, list_heads, max_k, block);
+  return (long long)B * Hkv * p.nsplit;
+}
+
+hipError_t launch_sparse_decode(const void* q, const void* k, const void* v,
+                                const int32_t* kv_len, int B, int Hq, int Hkv, int Tmax, int D,
+                                float sm_scale, int block, const int32_t* kv_idx,
+                                const int32_t* kv_cnt, int list_heads, int max_k, void* o,
+                                void* ws, hipStream_t stream) {
+  if ((long long)B * Hq == 0) return hipSuccess;
+  const DecodePlan p = plan_decode(B, Hq, Hkv, Tmax, D, list_heads, max_k, block);
+  const int G = Hq / Hkv;
+  char* base = static_cast<char*>(ws);
+  const int32_t* list = kv_idx;
+  const int32_t* lcnt = kv_cnt;
+  if (p.is_union) {
+    int32_t* uni = reinterpret_cast<int32_t*>(base);
+    int32_t* ucnt = reinterpret_cast<int32_t*>(base + p.off_ucnt);
+    const int nbmax = (Tmax + block - 1) / block;
+    const size_t lds = (size_t)(nbmax + 3) / 4 * 4;
+    hipLaunchKernelGGL(decode_union_kernel, dim3((unsigned)(B * Hkv)), dim3(kUnionThreads), lds,
+                       stream, kv_idx, kv_cnt, kv_len, Hkv, G, Tmax, block, max_k, p.umax, uni,
+                       ucnt);
+    list = uni;
+    lcnt = ucnt;
+  }
+  float* part_ml = reinterpret_cast<float*>(base + p.off_ml);
+  float* part_acc = reinterpret_cast<float*>(base + p.off_acc);
+  const float c2 = sm_scale * 1.4426950408889634f;
+  const dim3 grid((unsigned)((size_t)B * Hkv * p.nsplit));
+#define SEER_DECODE(DD, GMM, UN)                                                               \
+  hipLaunchKernelGGL((decode_attn_kernel<DD, GMM, UN>), grid, dim3(kDecThreads), 0, stream,   \
+                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),             \
+                     static_cast<const __bf16*>(v), kv_len, Hkv, G, Tmax, c2, block, list,     \
+                     lcnt, p.lstride, p.chunk, p.nsplit, part_ml, part_acc)
+  if (D == 128) {
+    if (p.gm == 4) { if (p.is_union) SEER_DECODE(128, 4, true); else SEER_DECODE(128, 4, false); }
+    else           { if (p.is_union) SEER_DECODE(128, 8, true); else SEER_DECODE(128, 8, false); }
+  } else {
+    if (p.gm == 4) { if (p.is_union) SEER_DECODE(64, 4, true); else SEER_DECODE(64, 4, false); }
+    else           { if (p.is_union) SEER_DECODE(64, 8, true); else SEER_DECODE(64, 8, false); }
+  }
+#undef SEER_DECODE
+  const dim3 cgrid((unsigned)((size_t)B * Hq));
+  if (D == 128)
+    hipLaunchKernelGGL(decode_combine_kernel<128>, cgrid, dim3(kCombineThreads), 0, stream,
+                       part_ml, part_acc, lcnt, p.lstride, p.is_union, Hq, Hkv, p.chunk, p.nsplit,
+                       static_cast<__bf16*>(o));
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<64>, cgrid, dim3(kCombineThreads), 0, stream,
+                       part_ml, part_acc, lcnt, p.lstride, p.is_union, Hq, Hkv, p.chunk, p.nsplit,
+                       static_cast<__bf16*>(o));
+  return hipGetLastError();
+}
+
+}  // namespace seer

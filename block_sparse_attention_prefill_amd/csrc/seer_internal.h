@@ -24,6 +24,13 @@ hipError_t launch_build_mask(const float* scores, int B, int H, int nqb, int nkb
                              float threshold, double density, int keep_sink, int32_t* idx,
                              int32_t* cnt, int max_k, hipStream_t stream);
 
+// Decode rows: B*H rows of nkb scores; row (b, h) ranks the blocks holding
+// kv_len[b] tokens (block tokens each).
+hipError_t launch_build_mask_decode(const float* scores, const int32_t* kv_len, int B, int H,
+                                    int nkb, int block, int mode, float threshold, int k_blocks,
+                                    int keep_sink, int32_t* idx, int32_t* cnt, int max_k,
+                                    hipStream_t stream);
+
 // block: list block size in tokens, 64 or 128 (checked by the caller).
 hipError_t launch_sparse_prefill(const void* q, const void* k, const void* v, int B, int Hq,
                                  int Hkv, int T, int D, float sm_scale, int block,
@@ -43,5 +50,17 @@ size_t attn_gate_workspace_floats(int B, int Hq, int Hkv, int nqb, int dg);
 hipError_t launch_attn_gate(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
                             const float* wq, const float* wk, int dg, float scale,
                             float rope_base, float* scores, float* ws, hipStream_t stream);
+
+// Decode: workspace bytes and grid size of launch_sparse_decode (list_heads is
+// Hq or Hkv; the caller checks the arguments).
+size_t sparse_decode_workspace_bytes(int B, int Hq, int Hkv, int Tmax, int D, int list_heads,
+                                     int max_k, int block);
+long long sparse_decode_grid(int B, int Hq, int Hkv, int Tmax, int D, int list_heads, int max_k,
+                             int block);
+hipError_t launch_sparse_decode(const void* q, const void* k, const void* v,
+                                const int32_t* kv_len, int B, int Hq, int Hkv, int Tmax, int D,
+                                float sm_scale, int block, const int32_t* kv_idx,
+                                const int32_t* kv_cnt, int list_heads, int max_k, void* o,
+                                void* ws, hipStream_t stream);
 
 }  // namespace seer

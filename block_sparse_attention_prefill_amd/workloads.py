@@ -20,6 +20,12 @@ NumPy PCG64 generator.
 Seeds: ``seed = 1000 * workload_id + stream`` with stream 0 = Q, 1 = K, 2 = V,
 3 = scores, 4 = stripe columns, 5 = sampled query blocks, 6 = block maps,
 7 = gate weights.
+
+Decode workloads (one new token per sequence over a KV cache) follow the
+abstract of "SeerAttention-R: Sparse Attention Adaptation for Long Reasoning":
+a 4K-token budget, blocks of 64 or 128 tokens and 90 % sparsity, here with
+Llama-3.1-8B attention shapes.  Same seeding, streams 0-2 = q and the K/V cache,
+3 = decode scores, 4 = stripe columns.
 """
 
 from __future__ import annotations
@@ -204,3 +210,79 @@ def sample_qblocks(w: Workload, count: Optional[int] = None) -> np.ndarray:
             for i in sorted(picks):
                 out.append((b, h, i))
     return np.asarray(out, dtype=np.int64)
+
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode step: batch sequences with kv_lens cached tokens each (the last
+    being the new token) in a [B, Hkv, tmax, D] cache; block lists per KV head
+    (list_heads "kv") or per query head ("q")."""
+    wid: int
+    name: str
+    batch: int
+    hq: int
+    hkv: int
+    head_dim: int
+    tmax: int
+    kv_lens: tuple
+    block: int = BLOCK
+    budget_tokens: int = 4096
+    list_heads: str = "kv"
+    keep_sink: bool = True
+
+    @property
+    def nkb(self) -> int:
+        return (self.tmax + self.block - 1) // self.block
+
+    @property
+    def k_blocks(self) -> int:
+        return max(1, self.budget_tokens // self.block)
+
+    @property
+    def lh(self) -> int:
+        return self.hkv if self.list_heads == "kv" else self.hq
+
+    def seed(self, stream: int) -> int:
+        return 1000 * self.wid + stream
+
+
+# Eight sequences at 40k tokens (a 4K budget is 90 % sparsity), Llama-3.1-8B shape.
+DEC1 = DecodeWorkload(11, "llama3.1-8b_decode_b8_kv40960_budget4096", 8, 32, 8, 128, 40960,
+                      (40960,) * 8, block=64, budget_tokens=4096, list_heads="kv")
+DEC2 = dataclasses.replace(DEC1, wid=12, name="llama3.1-8b_decode_b8_kv40960_budget4096_perhead",
+                           list_heads="q")
+
+
+def make_decode_inputs(dw: DecodeWorkload, tail_nan: bool = False):
+    """q [B,Hq,D] and the K/V cache [B,Hkv,tmax,D], bf16 N(0,1) on the CPU.  With
+    tail_nan the cache slots past each sequence's length hold NaN, which no
+    consumer may read."""
+    q = _normal_bf16((dw.batch, dw.hq, dw.head_dim), dw.seed(0), 1.0)
+    k = _normal_bf16((dw.batch, dw.hkv, dw.tmax, dw.head_dim), dw.seed(1), 1.0)
+    v = _normal_bf16((dw.batch, dw.hkv, dw.tmax, dw.head_dim), dw.seed(2), 1.0)
+    if tail_nan:
+        for b, n in enumerate(dw.kv_lens):
+            k[b, :, n:] = float("nan")
+            v[b, :, n:] = float("nan")
+    kv_len = torch.tensor(dw.kv_lens, dtype=torch.int32)
+    return q, k, v, kv_len
+
+
+def make_decode_scores(dw: DecodeWorkload) -> torch.Tensor:
+    """Decode block scores [B, H, nKB] fp32 (H = list heads): N(0,1) plus 4 on the
+    last 4 blocks of the sequence (the local window) and on 8 stripe columns per
+    head; entries past the sequence hold 1e6, which selection must never read."""
+    lh, nkb = dw.lh, dw.nkb
+    rng = np.random.Generator(np.random.PCG64(dw.seed(3)))
+    srng = np.random.Generator(np.random.PCG64(dw.seed(4)))
+    s = rng.standard_normal(size=(dw.batch, lh, nkb), dtype=np.float32)
+    jj = np.arange(nkb)
+    for b, n in enumerate(dw.kv_lens):
+        nb = (n + dw.block - 1) // dw.block
+        s[b] += np.float32(4.0) * ((jj >= nb - 4) & (jj < nb)).astype(np.float32)
+        for h in range(lh):
+            cols = srng.choice(max(nb, 1), size=min(8, max(nb, 1)), replace=False)
+            s[b, h, cols] += np.float32(4.0)
+        s[b, :, nb:] = np.float32(1e6)
+    return torch.from_numpy(np.ascontiguousarray(s))

@@ -235,6 +235,78 @@ int seer_attn_gate_scores(const void* q, const void* k, int B, int Hq, int Hkv, 
 int seer_pooled_target_mse(const float* amap, const float* gate, int B, int H, int nQB,
                            float* target, float* row_sse, float* loss, void* stream);
 
+/*
+ * Decode (one new token per sequence over a KV cache)
+ * ---------------------------------------------------
+ * The abstract of "SeerAttention-R: Sparse Attention Adaptation for Long
+ * Reasoning" carries the learned block sparsity over to auto-regressive
+ * decoding, with a token budget (4K tokens) and sparse-attention blocks of 64
+ * or 128 tokens.  Conventions of the two decode calls:
+ * - The cache is K, V : bf16 [B, Hkv, Tmax, D] (16-byte aligned); sequence b
+ *   holds kv_len[b] tokens at positions 0 .. kv_len[b] - 1, the last of them
+ *   being the new token, whose query is q[b] : bf16 [B, Hq, D].  kv_len is
+ *   device int32 [B]; values are clamped to [0, Tmax] (no access outside the
+ *   cache); a sequence with 0 tokens outputs zeros.
+ * - Blocks are `block` tokens, block in {64, 128}; sequence b has
+ *   nb = ceil(kv_len[b] / block) of them, the last one possibly short.
+ * - Lists have one row per list head: list_heads = Hq (each query head its own
+ *   list) or list_heads = Hkv (the G = Hq / Hkv query heads of a KV group share
+ *   one list); query head h reads list head h or h / G.
+ */
+
+/*
+ * Decode block lists: scores fp32 [B, H, nKB] (row stride nKB; row (b, h)
+ * reads entries j < nb) -> kv_idx int32 [B, H, max_k] (ascending, -1 padded),
+ * kv_cnt int32 [B, H].  The rule is the prefill row rule for the new token:
+ * forced blocks are nb - 1 (holds the token) and block 0 if keep_sink; TopK
+ * keeps min(nb, max(|forced|, k_blocks)) blocks (k_blocks = token budget /
+ * block, >= 1); threshold keeps the forced blocks and every block whose fp32
+ * score >= (float)threshold, the best-ranked ones first if max_k is short.
+ * Ranking, ties and NaN as for seer_build_mask.  nb is capped at nKB.
+ * nKB <= SEER_MAX_QUERY_BLOCKS (else SEER_ERR_UNSUPPORTED).
+ * max_k   TopK: >= min(nKB, max(k_blocks, 2 if keep_sink else 1));
+ *         threshold: >= 2 if keep_sink and nKB > 1, else >= 1.
+ *         Otherwise SEER_ERR_CAPACITY.
+ */
+int seer_build_mask_decode(const float* scores, const int32_t* kv_len, int B, int H, int nKB,
+                           int block, int mode, float threshold, int k_blocks, int keep_sink,
+                           int32_t* kv_idx, int32_t* kv_cnt, int max_k, void* stream);
+
+/* Bytes of device workspace seer_sparse_decode needs (the union of a KV
+ * group's per-head lists, and one partial softmax state per chunk of blocks
+ * and query head).  0 for invalid sizes. */
+size_t seer_sparse_decode_workspace_size(int B, int Hq, int Hkv, int Tmax, int D,
+                                         int list_heads, int max_k, int block);
+
+/*
+ * Block-sparse decode attention: for each sequence b and query head h,
+ *   o[b,h] = softmax over the allowed keys c of sm_scale <q[b,h], k[b,g,c]>,
+ *            times v[b,g,c],   g = h / G,
+ * where c is allowed iff c < kv_len[b] and block c / block is listed in
+ * kv_idx[b, lh, 0:min(kv_cnt[b, lh], max_k)] (lh the list head of h).  The
+ * same definition as seer_sparse_prefill's for the last query row
+ * (rebuttal "SeerAttention: Learning Intrinsic Sparse Attention in Your
+ * LLMs", "Weakness 5 (Pseudo code of Inference Kernel)").
+ *
+ * q        device bf16 [B, Hq, D]; k_cache, v_cache device bf16 [B, Hkv, Tmax, D];
+ *          D in {64, 128}; Hq % Hkv == 0 and G = Hq / Hkv <= 8; Tmax >= 1 and
+ *          ceil(Tmax / block) <= 32768.
+ * kv_len   device int32 [B] (see above).
+ * kv_idx   device int32 [B, list_heads, max_k], kv_cnt device int32
+ *          [B, list_heads]; list_heads in {Hq, Hkv}.  Entries outside [0, nb)
+ *          are skipped, order does not matter, a list must not repeat a block.
+ *          A head with no valid entry outputs zeros.
+ * o        device bf16 out [B, Hq, D], rounded to nearest even.
+ * workspace device, >= seer_sparse_decode_workspace_size(...) bytes, 256-byte
+ *          aligned; overwritten.
+ * Each selected block is read once per KV group.  Results are bit-reproducible.
+ */
+int seer_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* kv_len, int B, int Hq, int Hkv, int Tmax, int D,
+                       float sm_scale, int block, const int32_t* kv_idx, const int32_t* kv_cnt,
+                       int list_heads, int max_k, void* o, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

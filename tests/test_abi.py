@@ -158,3 +158,55 @@ def test_attn_gate_rejects_on_host():
     assert call(p2=0) == 0             # empty
     assert seer.load().seer_attn_gate_workspace_size(1, 4, 2, 256, 64) >= (4 + 2) * 4 * 64 * 4
 
+
+
+def test_build_mask_decode_rejects_on_host():
+    lib = seer.load()
+    # scores, kv_len, B, H, nKB, block, mode, threshold, k_blocks, keep_sink, idx, cnt, max_k
+    a = [FAKE, FAKE, 2, 8, 640, 64, 1, 0.0, 64, 1, FAKE, FAKE, 64, None]
+    def call(**kw):
+        b = list(a)
+        for i, v in kw.items():
+            b[int(i[1:])] = v
+        return lib.seer_build_mask_decode(*b)
+    assert call(p5=96) == 2            # block size
+    assert call(p4=4097) == 2          # row longer than the mask kernel takes
+    assert call(p6=7) == 1             # mode
+    assert call(p8=0) == 1             # TopK budget
+    assert call(p12=63) == 3           # max_k below the budget
+    assert call(p4=40, p12=39) == 3    # budget capped at nKB = 40
+    assert call(p6=0, p7=float("inf")) == 1   # threshold
+    assert call(p6=0, p12=1) == 3      # sink + last block need 2
+    assert call(p0=None) == 1 and call(p1=None) == 1
+    assert call(p2=-1) == 1
+    assert call(p2=0) == 0             # empty
+
+
+def test_sparse_decode_rejects_on_host():
+    lib = seer.load()
+    # q, k, v, kv_len, B, Hq, Hkv, Tmax, D, scale, block, idx, cnt, list_heads, max_k, o, ws, bytes, s
+    a = [FAKE, FAKE, FAKE, FAKE, 2, 32, 8, 4096, 128, 0.088, 64, FAKE, FAKE, 8, 64, FAKE, FAKE,
+         1 << 30, None]
+    def call(**kw):
+        b = list(a)
+        for i, v in kw.items():
+            b[int(i[1:])] = v
+        return lib.seer_sparse_decode(*b)
+    assert call(p8=96) == 2            # head dim
+    assert call(p10=32) == 2           # block size
+    assert call(p5=72) == 2            # 9 query heads per KV head
+    assert call(p5=30) == 1            # Hq % Hkv
+    assert call(p13=16) == 1           # list heads neither Hq nor Hkv
+    assert call(p7=0) == 1             # empty cache capacity
+    assert call(p7=64 * 32769) == 2    # more blocks than the union flags hold
+    assert call(p9=0.0) == 1 and call(p9=float("nan")) == 1
+    assert call(p14=0) == 1            # max_k
+    assert call(p3=None) == 1 and call(p15=None) == 1
+    assert call(p16=None) == 4         # workspace
+    assert call(p17=1024) == 4         # workspace too small
+    assert call(p4=0) == 0             # empty batch
+    ws = lib.seer_sparse_decode_workspace_size
+    assert ws(2, 32, 8, 4096, 128, 8, 64, 64) > 0
+    assert ws(2, 32, 8, 4096, 128, 32, 64, 64) > ws(2, 32, 8, 4096, 128, 8, 64, 64)
+    assert ws(2, 32, 8, 4096, 128, 16, 64, 64) == 0
+    assert ws(2, 32, 8, 0, 128, 8, 64, 64) == 0

@@ -621,3 +621,169 @@ def test_attn_gate_repeat_bitexact():
         torch.cuda.synchronize()
         assert torch.equal(s, s0)
 
+
+
+# ------------------------------------------------------------------ decode
+
+
+def _decode_case(wid, batch, hq, hkv, tmax, d, kv_lens, block=64, list_heads="q",
+                 budget_tokens=4096, keep_sink=True):
+    return wl.DecodeWorkload(wid, f"decode{wid}", batch, hq, hkv, d, tmax, tuple(kv_lens),
+                             block=block, budget_tokens=budget_tokens, list_heads=list_heads,
+                             keep_sink=keep_sink)
+
+
+def _decode_mask_scores(seed, dw, ties_nan=False):
+    s = wl.make_decode_scores(dw)
+    if ties_nan:
+        rng = np.random.default_rng(seed)
+        vals = np.array([0.1, 0.2, 0.2, 0.5, -0.0, 0.0, np.nan, 0.9], np.float32)
+        s = torch.from_numpy(rng.choice(vals, size=tuple(s.shape)).astype(np.float32))
+    return s
+
+
+@pytest.mark.parametrize("block", [64, 128])
+@pytest.mark.parametrize("mode,thr,kb,sink", [
+    (wl.MODE_TOPK, 0.0, 3, True), (wl.MODE_TOPK, 0.0, 1, False), (wl.MODE_TOPK, 0.0, 64, True),
+    (wl.MODE_THRESHOLD, 2.0, 0, True), (wl.MODE_THRESHOLD, 0.15, 0, False)])
+@pytest.mark.parametrize("ties_nan", [False, True])
+def test_decode_mask_bitexact(block, mode, thr, kb, sink, ties_nan):
+    dw = _decode_case(70, 5, 4, 2, 2000, 64, (2000, 1, 0, 777, 129), block=block, keep_sink=sink)
+    announce(f"decode mask block {block} mode {mode} thr {thr} kb {kb} sink {sink} "
+             f"ties {ties_nan}")
+    s = _decode_mask_scores(71, dw, ties_nan)
+    nkb = s.shape[-1]
+    max_k = nkb if mode == wl.MODE_THRESHOLD else max(2, min(nkb, kb))
+    if mode == wl.MODE_THRESHOLD and thr == 2.0:
+        max_k = 6  # lists longer than max_k keep the best-ranked passing blocks
+    kv_len = torch.tensor(dw.kv_lens, dtype=torch.int32)
+    gi, gc = seer.seer_build_mask_decode(_dev(s), _dev(kv_len), block, mode, thr, max(kb, 1),
+                                         sink, max_k)
+    torch.cuda.synchronize()
+    ri, rc = oracle.build_mask_decode_ref(s.numpy(), dw.kv_lens, block, mode, thr, max(kb, 1),
+                                          sink, max_k)
+    np.testing.assert_array_equal(gc.cpu().numpy(), rc)
+    np.testing.assert_array_equal(gi.cpu().numpy(), ri)
+
+
+def _decode_lists(seed, dw, max_k, dense=False):
+    """Random valid block sets per list head (any order), some with entries past
+    the sequence that must be skipped; dense=True lists every block."""
+    rng = np.random.default_rng(seed)
+    lh = dw.lh
+    idx = np.full((dw.batch, lh, max_k), -1, np.int32)
+    cnt = np.zeros((dw.batch, lh), np.int32)
+    for b, n in enumerate(dw.kv_lens):
+        nb = (n + dw.block - 1) // dw.block
+        for h in range(lh):
+            if dense:
+                sel = list(range(min(nb, max_k)))
+            else:
+                m = int(rng.integers(0, min(nb, max_k - 1) + 1)) if nb else 0
+                sel = [int(x) for x in rng.choice(nb, size=m, replace=False)] if m else []
+                if len(sel) < max_k and rng.random() < 0.3:
+                    sel.append(nb + int(rng.integers(0, 4)))
+            rng.shuffle(sel)
+            idx[b, h, : len(sel)] = sel
+            cnt[b, h] = len(sel)
+    return idx, cnt
+
+
+def _run_decode(dw, q, k, v, kv_len, idx, cnt, scale=None):
+    o = seer.seer_sparse_decode(_dev(q), _dev(k), _dev(v), _dev(kv_len), _dev(torch.from_numpy(idx)),
+                                _dev(torch.from_numpy(cnt)), dw.block, scale)
+    torch.cuda.synchronize()
+    return o
+
+
+DECODE_CASES = {
+    "gqa2_d128_b64_perhead": dict(batch=4, hq=4, hkv=2, tmax=700, d=128,
+                                  kv_lens=(700, 1, 333, 0), block=64, list_heads="q", max_k=8),
+    "gqa8_d64_b128_perhead": dict(batch=2, hq=8, hkv=1, tmax=1000, d=64, kv_lens=(1000, 450),
+                                  block=128, list_heads="q", max_k=5),
+    "gqa5_d128_b64_shared": dict(batch=2, hq=5, hkv=1, tmax=333, d=128, kv_lens=(333, 64),
+                                 block=64, list_heads="kv", max_k=4),
+    "mha_d64_b64": dict(batch=2, hq=2, hkv=2, tmax=257, d=64, kv_lens=(257, 200), block=64,
+                        list_heads="q", max_k=5),
+    "qwen_gqa5_d128_b128_perhead": dict(batch=1, hq=40, hkv=8, tmax=4096, d=128,
+                                        kv_lens=(4001,), block=128, list_heads="q", max_k=12),
+    "gqa4_d128_b64_dense_long": dict(batch=2, hq=8, hkv=2, tmax=5000, d=128,
+                                     kv_lens=(5000, 3001), block=64, list_heads="q", max_k=79,
+                                     dense=True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(DECODE_CASES))
+def test_sparse_decode_parity(case):
+    c = dict(DECODE_CASES[case])
+    max_k, dense = c.pop("max_k"), c.pop("dense", False)
+    dw = _decode_case(80 + sorted(DECODE_CASES).index(case), **c)
+    announce(f"decode {case}")
+    q, k, v, kv_len = wl.make_decode_inputs(dw, tail_nan=True)
+    idx, cnt = _decode_lists(dw.wid, dw, max_k, dense)
+    scale = 1.0 / math.sqrt(dw.head_dim)
+    got = _run_decode(dw, q, k, v, kv_len, idx, cnt, scale).float().cpu().numpy()
+    ref = oracle.sparse_decode_ref(q, k, v, dw.kv_lens, idx, cnt, scale, dw.block)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max()
+    announce(f"decode {case}: max err {err:.2e}")
+    assert err <= O_TOL
+    for b, n in enumerate(dw.kv_lens):
+        if n == 0:
+            assert (got[b] == 0).all()
+
+
+def test_sparse_decode_shared_equals_repeated_per_head_lists():
+    """Ascending shared lists and the same lists repeated per query head go through
+    the direct and the union path; both visit the same tiles in the same order."""
+    dw = _decode_case(90, 3, 8, 2, 3000, 128, (3000, 1234, 65), list_heads="kv")
+    q, k, v, kv_len = wl.make_decode_inputs(dw)
+    idx, cnt = _decode_lists(91, dw, 20)
+    for b in range(dw.batch):
+        for h in range(dw.lh):
+            row = sorted(int(j) for j in idx[b, h, : cnt[b, h]]
+                         if 0 <= j < (dw.kv_lens[b] + 63) // 64)
+            idx[b, h] = -1
+            idx[b, h, : len(row)] = row
+            cnt[b, h] = len(row)
+    shared = _run_decode(dw, q, k, v, kv_len, idx, cnt)
+    g = dw.hq // dw.hkv
+    per = _run_decode(dw, q, k, v, kv_len, np.ascontiguousarray(np.repeat(idx, g, axis=1)),
+                      np.ascontiguousarray(np.repeat(cnt, g, axis=1)))
+    assert torch.equal(shared, per)
+
+
+@pytest.mark.parametrize("dw", [wl.DEC1, wl.DEC2], ids=lambda d: d.name)
+def test_sparse_decode_bench_workload(dw):
+    """The benchmarked decode step at full size: GPU lists from the decode scores,
+    bit-exact against the oracle's; outputs of two sampled sequences (all heads)
+    against the oracle."""
+    announce(f"decode bench workload {dw.name}")
+    q, k, v, kv_len = wl.make_decode_inputs(dw)
+    s = wl.make_decode_scores(dw)
+    max_k = min(dw.nkb, max(dw.k_blocks, 2))
+    gi, gc = seer.seer_build_mask_decode(_dev(s), _dev(kv_len), dw.block, wl.MODE_TOPK, 0.0,
+                                         dw.k_blocks, dw.keep_sink, max_k)
+    ri, rc = oracle.build_mask_decode_ref(s.numpy(), dw.kv_lens, dw.block, wl.MODE_TOPK, 0.0,
+                                          dw.k_blocks, dw.keep_sink, max_k)
+    np.testing.assert_array_equal(gc.cpu().numpy(), rc)
+    np.testing.assert_array_equal(gi.cpu().numpy(), ri)
+    o = seer.seer_sparse_decode(_dev(q), _dev(k), _dev(v), _dev(kv_len), gi, gc, dw.block)
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    for b in (0, dw.batch - 1):
+        ref = oracle.sparse_decode_ref(q[b:b + 1], k[b:b + 1], v[b:b + 1], [dw.kv_lens[b]],
+                                       ri[b:b + 1], rc[b:b + 1], None, dw.block)
+        err = np.abs(got[b:b + 1] - ref).max()
+        announce(f"decode {dw.name} seq {b}: max err {err:.2e}")
+        assert err <= O_TOL
+
+
+def test_sparse_decode_repeat_bitexact():
+    dw = _decode_case(92, 2, 32, 8, 8192, 128, (8192, 5000), list_heads="q")
+    q, k, v, kv_len = wl.make_decode_inputs(dw)
+    idx, cnt = _decode_lists(93, dw, 40)
+    a = _run_decode(dw, q, k, v, kv_len, idx, cnt)
+    b = _run_decode(dw, q, k, v, kv_len, idx, cnt)
+    assert torch.equal(a, b)
