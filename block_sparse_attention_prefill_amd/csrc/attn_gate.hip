@@ -13,14 +13,15 @@
 // Four kernels:
 // * gate_pool_kernel: one wave per (batch, head, 64-token block) pools the block
 //   (16-byte loads all in flight, lane shuffles to combine).
-// * gate_project_kernel: one workgroup per (batch, head, 16 blocks) applies the
-//   head's linear layer (an LDS-tiled fp32 GEMM) and the block RoPE, whose
-//   angles are formed in fp64 so that far block positions keep their accuracy.
+// * gate_project_kernel: one workgroup per (batch, head, 64 blocks) applies the
+//   head's linear layer on the fp32 matrix cores (v_mfma_f32_32x32x2f32, fp32
+//   operands and accumulation) and the block RoPE, whose angles are formed and
+//   reduced in fp64 so that far block positions keep their accuracy.
 // * gate_logits_kernel: one workgroup per causal 64 x 64 tile of block pairs
-//   (LDS-tiled fp32 Q~ K~^T) writes the scaled logits and each row's tile max
-//   and sum of exponentials; gate_softmax_kernel then combines a row's tile
-//   pairs in a fixed order and normalises the row in place, zeros above the
-//   diagonal.
+//   (Q~ K~^T on the fp32 matrix cores) writes the scaled logits and each row's
+//   tile max and sum of exponentials; gate_softmax_kernel
+//   then combines a row's partials in a fixed order and normalises the row in
+//   place, zeros above the diagonal.
 #include "seer_internal.h"
 
 #include <math.h>
@@ -28,11 +29,8 @@
 namespace seer {
 namespace {
 
-constexpr int kProjThreads = 256;
 constexpr int kScoreThreads = 256;
 constexpr int kTile = 64;  // query and key blocks per scores tile; tokens per block
-constexpr int kWRows = 32; // weight rows per LDS chunk of the linear layer
-constexpr int kProjRows = 16;  // pooled rows (blocks) per projection workgroup
 
 // Pooling: one wave per (batch, head slot, 64-token block).  Lane L reads
 // 16-byte chunk L % C of rows L / C, L / C + 64 / C, ... (C = D / 8 chunks per
@@ -113,26 +111,50 @@ __global__ __launch_bounds__(64 * kPoolWaves) void gate_pool_kernel(
   }
 }
 
-// Linear layer + block RoPE: one workgroup per (batch, head slot, 16-block
-// tile) computes the 16 x DG tile of pooled rows times the head's weights,
-// streaming 32-row chunks of both through LDS (16-byte loads, issued before the
-// barrier that frees the previous chunk).  Thread (ty, tx) owns row ty and
-// columns tx + 16 c, which include both columns e and e + DG/2 of every RoPE
-// pair it owns, so the rotation needs no exchange.  Angles are formed in fp64
-// so that far block positions keep their accuracy.
+// Linear layer + block RoPE on the fp32 matrix cores.  One workgroup (two
+// waves) per (batch, head slot, 64 pooled rows, column group); wave w computes
+// rows 32 w .. 32 w + 31 of the group's 32-column tiles with
+// v_mfma_f32_32x32x2f32, streaming 32-dim chunks of the rows and of the weights
+// (stored transposed) through LDS, the next chunk's loads in flight during the
+// current chunk's MFMAs.  In each group of 4 MFMAs a lane feeds 4 consecutive
+// dims from one 16-byte read (lanes 0-31 and 32-63 take the two halves of an
+// 8-dim group: any assignment of dims to MFMA k-slots works as long as both
+// operands use the same one).  A column group is the tile pair {cg, cg + DG/64}
+// that holds both columns e and e + DG/2 of a RoPE pair in the same lane; for
+// DG = 32 the single tile holds the pair in lanes l and l ^ 16.  The block angle
+// i * base^(-2e/DG) is formed and reduced mod 2 pi in fp64; sin and cos of the
+// reduced angle are fp32.
+constexpr int kProjWaves = 2;
+constexpr int kProjTileRows = 32 * kProjWaves;  // pooled rows per workgroup
+constexpr int kKChunk = 32;                     // input dims per LDS chunk
+
 template <int DG>
-__global__ __launch_bounds__(kProjThreads) void gate_project_kernel(
+struct ProjCfg {
+  static constexpr int NT = DG / 32;               // 32-column tiles of the output
+  static constexpr int NTW = NT >= 2 ? 2 : 1;      // tiles per workgroup
+  static constexpr int NG = NT >= 2 ? NT / 2 : 1;  // column groups
+};
+
+template <int DG>
+__global__ __launch_bounds__(64 * kProjWaves) void gate_project_kernel(
     const float* __restrict__ pq, const float* __restrict__ pk, int B, int Hq, int Hkv, int D,
     int nqb, const float* __restrict__ wq, const float* __restrict__ wk, float rope_base,
     float* __restrict__ qt, float* __restrict__ kt) {
-  constexpr int NC = DG / 16;  // columns per thread
-  __shared__ __attribute__((aligned(16))) float as[kProjRows][kWRows];
-  __shared__ __attribute__((aligned(16))) float ws[kWRows * DG];
+  constexpr int NT = ProjCfg<DG>::NT;
+  constexpr int NTW = ProjCfg<DG>::NTW;
+  constexpr int NG = ProjCfg<DG>::NG;
+  constexpr int NTH = 64 * kProjWaves;
+  constexpr int WC = 32 * NTW;  // weight columns per workgroup
+  __shared__ __attribute__((aligned(16))) float as[kProjTileRows][kKChunk + 4];
+  __shared__ __attribute__((aligned(16))) float wt[WC][kKChunk + 4];
   const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;  // row ty, columns tx + 16 c
-  const int ntiles = (nqb + kProjRows - 1) / kProjRows;
-  const int tile = blockIdx.x % ntiles;
-  const int bh = blockIdx.x / ntiles;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int lr = lane & 31, hf = lane >> 5;
+  const int ntiles = (nqb + kProjTileRows - 1) / kProjTileRows;
+  const int cg = blockIdx.x % NG;
+  const int tile = (blockIdx.x / NG) % ntiles;
+  const int bh = blockIdx.x / NG / ntiles;
   const int b = bh / (Hq + Hkv);
   const int slot = bh % (Hq + Hkv);
   const bool is_q = slot < Hq;
@@ -141,57 +163,112 @@ __global__ __launch_bounds__(kProjThreads) void gate_project_kernel(
   const int din = is_q ? D : 2 * D;
   const float* a = (is_q ? pq : pk) + ((size_t)b * nheads + head) * nqb * din;
   const float* w = (is_q ? wq : wk) + (size_t)head * din * DG;
-  const int i0 = kProjRows * tile;
-  constexpr int kWVec = kWRows * DG / 4 / kProjThreads;  // 16-byte weight loads per thread
-  float acc[NC] = {};
-  for (int d0 = 0; d0 < din; d0 += kWRows) {
-    f32x4 va = {}, vw[kWVec];
-    const int ar = tid / (kWRows / 4), ad = 4 * (tid % (kWRows / 4));  // 16 rows x 8 vectors
-    if (tid < kProjRows * kWRows / 4 && i0 + ar < nqb)
-      va = *reinterpret_cast<const f32x4*>(a + (size_t)(i0 + ar) * din + d0 + ad);
+  const int i0 = kProjTileRows * tile;
+  auto col0 = [&](int u) { return 32 * (cg + u * NG); };  // first column of tile u
+  constexpr int kAVec = kProjTileRows * kKChunk / 4 / NTH;  // 16-byte row loads per thread
+  constexpr int kWVec = kKChunk * WC / 4 / NTH;             // 16-byte weight loads per thread
+  f32x4 va[kAVec], vw[kWVec];
+  auto load = [&](int d0) {
 #pragma unroll
-    for (int n = 0; n < kWVec; ++n)
-      vw[n] = reinterpret_cast<const f32x4*>(w + (size_t)d0 * DG)[tid + kProjThreads * n];
+    for (int n = 0; n < kAVec; ++n) {
+      const int x = tid + NTH * n;
+      const int r = x / (kKChunk / 4), c4 = x % (kKChunk / 4);
+      va[n] = (i0 + r < nqb)
+                  ? *reinterpret_cast<const f32x4*>(a + (size_t)(i0 + r) * din + d0 + 4 * c4)
+                  : f32x4{};
+    }
+#pragma unroll
+    for (int n = 0; n < kWVec; ++n) {
+      const int x = tid + NTH * n;
+      const int r = x / (WC / 4), c4 = x % (WC / 4);  // c4: 4-column group within WC
+      const int col = col0(c4 / 8) + 4 * (c4 % 8);
+      vw[n] = *reinterpret_cast<const f32x4*>(w + (size_t)(d0 + r) * DG + col);
+    }
+  };
+  f32x16 acc[NTW];
+#pragma unroll
+  for (int u = 0; u < NTW; ++u) acc[u] = f32x16{};
+  load(0);
+  for (int d0 = 0; d0 < din; d0 += kKChunk) {
     __syncthreads();  // the previous chunk has been used
-    if (tid < kProjRows * kWRows / 4) *reinterpret_cast<f32x4*>(&as[ar][ad]) = va;
 #pragma unroll
-    for (int n = 0; n < kWVec; ++n) reinterpret_cast<f32x4*>(ws)[tid + kProjThreads * n] = vw[n];
+    for (int n = 0; n < kAVec; ++n) {
+      const int x = tid + NTH * n;
+      *reinterpret_cast<f32x4*>(&as[x / (kKChunk / 4)][4 * (x % (kKChunk / 4))]) = va[n];
+    }
+#pragma unroll
+    for (int n = 0; n < kWVec; ++n) {
+      const int x = tid + NTH * n;
+      const int r = x / (WC / 4), c4 = x % (WC / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wt[4 * c4 + e][r] = vw[n][e];
+    }
     __syncthreads();
-#pragma unroll 8
-    for (int d = 0; d < kWRows; ++d) {
-      const float av = as[ty][d];
+    if (d0 + kKChunk < din) load(d0 + kKChunk);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) acc[c] = fmaf(av, ws[d * DG + tx + 16 * c], acc[c]);
+    for (int g = 0; g < kKChunk / 8; ++g) {
+      const f32x4 av = *reinterpret_cast<const f32x4*>(&as[32 * wv + lr][8 * g + 4 * hf]);
+      f32x4 bv[NTW];
+#pragma unroll
+      for (int u = 0; u < NTW; ++u)
+        bv[u] = *reinterpret_cast<const f32x4*>(&wt[32 * u + lr][8 * g + 4 * hf]);
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+        for (int u = 0; u < NTW; ++u)
+          acc[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[k4], bv[u][k4], acc[u], 0, 0, 0);
     }
   }
-  const int i = i0 + ty;
-  if (i >= nqb) return;
-  float* out = (is_q ? qt : kt) + (((size_t)b * nheads + head) * nqb + i) * DG;
-#pragma unroll
-  for (int c = 0; c < NC / 2; ++c) {
-    const int e = tx + 16 * c;  // e < DG / 2; its partner e + DG / 2 is column c + NC / 2
+  // acc[u][v]: row 32 wv + 8 (v / 4) + 4 hf + v % 4, column col0(u) + lr.
+  float* out = (is_q ? qt : kt) + ((size_t)b * nheads + head) * nqb * DG;
+  const double two_pi = 6.283185307179586476925287;
+  auto rotate = [&](int i, int e, float x1, float x2, float& y1, float& y2) {
     const double ang = (double)i * pow((double)rope_base, -2.0 * e / (double)DG);
-    const double cs = cos(ang), sn = sin(ang);
-    const double x1 = acc[c], x2 = acc[c + NC / 2];
-    out[e] = (float)(x1 * cs - x2 * sn);
-    out[e + DG / 2] = (float)(x2 * cs + x1 * sn);
+    const float r = (float)(ang - two_pi * rint(ang / two_pi));
+    float sn, cs;
+    sincosf(r, &sn, &cs);
+    y1 = x1 * cs - x2 * sn;
+    y2 = x2 * cs + x1 * sn;
+  };
+  (void)NT;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int i = i0 + 32 * wv + 8 * (v / 4) + 4 * hf + (v % 4);
+    if constexpr (NTW == 2) {
+      const int e = col0(0) + lr;  // its partner e + DG/2 is column col0(1) + lr
+      float y1, y2;
+      rotate(i, e, acc[0][v], acc[1][v], y1, y2);
+      if (i < nqb) {
+        out[(size_t)i * DG + e] = y1;
+        out[(size_t)i * DG + e + DG / 2] = y2;
+      }
+    } else {
+      const float x = acc[0][v];
+      const float xp = __shfl_xor(x, 16, 64);
+      const bool low = lr < 16;  // column lr is e (low) or e + 16 (high) of its pair
+      float y1, y2;
+      rotate(i, low ? lr : lr - 16, low ? x : xp, low ? xp : x, y1, y2);
+      if (i < nqb) out[(size_t)i * DG + lr] = low ? y1 : y2;
+    }
   }
 }
 
 // Logits of one 64 x 64 tile of (query block, key block) pairs, tile (it, jt)
-// with jt <= it, enumerated per head in row-major lower-triangular order.
-// Thread (ty, tx) of the 16 x 16 grid owns rows ty + 16 a and columns tx + 16 c
-// (a, c = 0..3); the 16 threads of a row are 16 consecutive lanes, so row
-// reductions are lane shuffles.  Writes the scaled logits (-inf above the
-// diagonal) and, per row, the tile's max and sum of exp(logit - max).
+// with jt <= it, enumerated per head in row-major lower-triangular order, on
+// the fp32 matrix cores: wave w computes the 32 x 32 quadrant (rows 32 (w / 2),
+// columns 32 (w % 2)) with v_mfma_f32_32x32x2f32 from the two tiles in LDS
+// (4 consecutive dims per lane and 16-byte read, as in the projection).
+// Writes the scaled logits (-inf above the diagonal) and, per row, the tile's
+// max and sum of exp(logit - max).
 template <int DG>
 __global__ __launch_bounds__(kScoreThreads) void gate_logits_kernel(
     const float* __restrict__ qt, const float* __restrict__ kt, int Hq, int Hkv, int nqb,
     float scale, float* __restrict__ scores, float2* __restrict__ part) {
-  __shared__ float qs[kTile][DG + 1];
-  __shared__ float ks[kTile][DG + 1];
+  // The Q and K tiles, later the 64 x 65 scaled logits (2 x 64 x 36 >= 64 x 65).
+  __shared__ __attribute__((aligned(16))) float smem[2][kTile][DG + 4];
+  float (*qs)[DG + 4] = smem[0];
+  float (*ks)[DG + 4] = smem[1];
   const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
   const int ntiles = (nqb + kTile - 1) / kTile;
   const int npairs = ntiles * (ntiles + 1) / 2;
   const int pair = blockIdx.x % npairs;
@@ -221,50 +298,62 @@ __global__ __launch_bounds__(kScoreThreads) void gate_logits_kernel(
     for (int n = 0; n < kVec; ++n) {
       const int x = tid + kScoreThreads * n;
       const int r = x / (DG / 4), d = 4 * (x % (DG / 4));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qs[r][d + e] = vq[n][e];
-        ks[r][d + e] = vk[n][e];
-      }
+      *reinterpret_cast<f32x4*>(&qs[r][d]) = vq[n];
+      *reinterpret_cast<f32x4*>(&ks[r][d]) = vk[n];
     }
   }
   __syncthreads();
-  float acc[4][4] = {};
+  const int lane = tid & 63, wv = tid >> 6;
+  const int lr = lane & 31, hf = lane >> 5;
+  const int rb = 32 * (wv >> 1), cb = 32 * (wv & 1);
+  f32x16 acc = {};
 #pragma unroll 4
-  for (int d = 0; d < DG; ++d) {
-    float qa[4], kc[4];
+  for (int g8 = 0; g8 < DG / 8; ++g8) {
+    const f32x4 av = *reinterpret_cast<const f32x4*>(&qs[rb + lr][8 * g8 + 4 * hf]);
+    const f32x4 bv = *reinterpret_cast<const f32x4*>(&ks[cb + lr][8 * g8 + 4 * hf]);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) qa[a] = qs[ty + 16 * a][d];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) kc[c] = ks[tx + 16 * c][d];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(qa[a], kc[c], acc[a][c]);
+    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u], bv[u], acc, 0, 0, 0);
   }
+  // acc[v]: tile row rb + 8 (v / 4) + 4 hf + v % 4, tile column cb + lr.  The
+  // scaled, masked tile goes through LDS (over the Q tile) so that four threads
+  // own each row: coalesced score rows and two-step row reductions.
+  __syncthreads();  // every wave is done with qs and ks
+  float (*st)[kTile + 1] = reinterpret_cast<float (*)[kTile + 1]>(&smem[0][0][0]);
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = i0 + ty + 16 * a;
-    float s[4];
-    float mx = -INFINITY;
+  for (int v = 0; v < 16; ++v) {
+    const int r = rb + 8 * (v / 4) + 4 * hf + (v % 4);
+    const int i = i0 + r, j = j0 + cb + lr;
+    st[r][cb + lr] = (i < nqb && j <= i) ? acc[v] * scale : -INFINITY;
+  }
+  __syncthreads();
+  const int r = tid >> 2, qq = tid & 3;  // row r, columns 16 qq .. 16 qq + 15
+  const int i = i0 + r;
+  float x[16];
+  float mx = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = j0 + tx + 16 * c;
-      s[c] = (i < nqb && j <= i) ? acc[a][c] * scale : -INFINITY;
-      mx = fmaxf(mx, s[c]);
+  for (int c = 0; c < 16; ++c) {
+    x[c] = st[r][16 * qq + c];
+    mx = fmaxf(mx, x[c]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+  float l = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) l += expf(x[c] - mx);  // exp(-inf) = 0 for masked entries
+  }
+  l += __shfl_xor(l, 1, 64);
+  l += __shfl_xor(l, 2, 64);
+  if (i < nqb) {
+    float* srow = scores + ((size_t)bh * nqb + i) * nqb + j0 + 16 * qq;
+    if (j0 + 16 * qq + 16 <= nqb && (reinterpret_cast<uintptr_t>(srow) & 15) == 0) {
+#pragma unroll
+      for (int c = 0; c < 16; c += 4)
+        *reinterpret_cast<f32x4*>(srow + c) = f32x4{x[c], x[c + 1], x[c + 2], x[c + 3]};
+    } else {
+      for (int c = 0; c < 16 && j0 + 16 * qq + c < nqb; ++c) srow[c] = x[c];
     }
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    float l = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = j0 + tx + 16 * c;
-      if (mx != -INFINITY && s[c] != -INFINITY) l += expf(s[c] - mx);
-      if (i < nqb && j < nqb) scores[((size_t)bh * nqb + i) * nqb + j] = s[c];
-    }
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) l += __shfl_xor(l, off, 64);
-    if (tx == 0 && i < nqb) part[((size_t)bh * nqb + i) * ntiles + jt] = make_float2(mx, l);
+    if (qq == 0) part[((size_t)bh * nqb + i) * ntiles + jt] = make_float2(mx, l);
   }
 }
 
@@ -283,8 +372,8 @@ __global__ __launch_bounds__(64 * kRowWaves) void gate_softmax_kernel(
   const int it = i / kTile;
   const float2* pr = part + row * ntiles;
   float m = -INFINITY, l = 0.f;
-  for (int jt = 0; jt <= it; ++jt) {  // same order in every lane
-    const float2 p = pr[jt];
+  for (int x = 0; x <= it; ++x) {  // same order in every lane
+    const float2 p = pr[x];
     if (p.x == -INFINITY) continue;
     const float mn = fmaxf(m, p.x);
     l = (m == -INFINITY ? 0.f : l * expf(m - mn)) + p.y * expf(p.x - mn);
@@ -325,10 +414,11 @@ hipError_t launch_attn_gate(const void* q, const void* k, int B, int Hq, int Hkv
                        (const __bf16*)q, (const __bf16*)k, B, Hq, Hkv, T, nqb, pq, pk);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const dim3 jgrid((unsigned)((size_t)B * (Hq + Hkv) * ((nqb + kProjRows - 1) / kProjRows)));
+  const size_t prow_tiles = (size_t)B * (Hq + Hkv) * ((nqb + kProjTileRows - 1) / kProjTileRows);
 #define SEER_GATE_PROJECT(DG)                                                                  \
-  hipLaunchKernelGGL(gate_project_kernel<DG>, jgrid, dim3(kProjThreads), 0, stream, pq, pk, B, \
-                     Hq, Hkv, D, nqb, wq, wk, rope_base, qt, kt)
+  hipLaunchKernelGGL(gate_project_kernel<DG>, dim3((unsigned)(prow_tiles * ProjCfg<DG>::NG)),   \
+                     dim3(64 * kProjWaves), 0, stream, pq, pk, B, Hq, Hkv, D, nqb, wq, wk,       \
+                     rope_base, qt, kt)
   if (dg == 128) SEER_GATE_PROJECT(128);
   else if (dg == 64) SEER_GATE_PROJECT(64);
   else SEER_GATE_PROJECT(32);
