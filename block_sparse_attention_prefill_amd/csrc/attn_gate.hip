@@ -114,7 +114,7 @@ __global__ __launch_bounds__(64 * kPoolWaves) void gate_pool_kernel(
 // Linear layer + block RoPE on the fp32 matrix cores.  One workgroup (two
 // waves) per (batch, head slot, 64 pooled rows, column group); wave w computes
 // rows 32 w .. 32 w + 31 of the group's 32-column tiles with
-// v_mfma_f32_32x32x2f32, streaming 32-dim chunks of the rows and of the weights
+// v_mfma_f32_32x32x2f32, streaming 64-dim chunks of the rows and of the weights
 // (stored transposed) through LDS, the next chunk's loads in flight during the
 // current chunk's MFMAs.  In each group of 4 MFMAs a lane feeds 4 consecutive
 // dims from one 16-byte read (lanes 0-31 and 32-63 take the two halves of an
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(64 * kPoolWaves) void gate_pool_kernel(
 // reduced angle are fp32.
 constexpr int kProjWaves = 2;
 constexpr int kProjTileRows = 32 * kProjWaves;  // pooled rows per workgroup
-constexpr int kKChunk = 32;                     // input dims per LDS chunk
+constexpr int kKChunk = 64;                     // input dims per LDS chunk
 
 template <int DG>
 struct ProjCfg {
@@ -222,8 +222,11 @@ __global__ __launch_bounds__(64 * kProjWaves) void gate_project_kernel(
   // acc[u][v]: row 32 wv + 8 (v / 4) + 4 hf + v % 4, column col0(u) + lr.
   float* out = (is_q ? qt : kt) + ((size_t)b * nheads + head) * nqb * DG;
   const double two_pi = 6.283185307179586476925287;
-  auto rotate = [&](int i, int e, float x1, float x2, float& y1, float& y2) {
-    const double ang = (double)i * pow((double)rope_base, -2.0 * e / (double)DG);
+  // Frequency of this lane's pair: e = col0(0) + lr, or lr % 16 for DG = 32.
+  const int e_lane = NTW == 2 ? col0(0) + lr : (lr & 15);
+  const double inv_freq = pow((double)rope_base, -2.0 * e_lane / (double)DG);
+  auto rotate = [&](int i, float x1, float x2, float& y1, float& y2) {
+    const double ang = (double)i * inv_freq;
     const float r = (float)(ang - two_pi * rint(ang / two_pi));
     float sn, cs;
     sincosf(r, &sn, &cs);
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(64 * kProjWaves) void gate_project_kernel(
     if constexpr (NTW == 2) {
       const int e = col0(0) + lr;  // its partner e + DG/2 is column col0(1) + lr
       float y1, y2;
-      rotate(i, e, acc[0][v], acc[1][v], y1, y2);
+      rotate(i, acc[0][v], acc[1][v], y1, y2);
       if (i < nqb) {
         out[(size_t)i * DG + e] = y1;
         out[(size_t)i * DG + e + DG / 2] = y2;
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(64 * kProjWaves) void gate_project_kernel(
       const float xp = __shfl_xor(x, 16, 64);
       const bool low = lr < 16;  // column lr is e (low) or e + 16 (high) of its pair
       float y1, y2;
-      rotate(i, low ? lr : lr - 16, low ? x : xp, low ? xp : x, y1, y2);
+      rotate(i, low ? x : xp, low ? xp : x, y1, y2);
       if (i < nqb) out[(size_t)i * DG + lr] = low ? y1 : y2;
     }
   }
@@ -257,17 +260,23 @@ __global__ __launch_bounds__(64 * kProjWaves) void gate_project_kernel(
 // with jt <= it, enumerated per head in row-major lower-triangular order, on
 // the fp32 matrix cores: wave w computes the 32 x 32 quadrant (rows 32 (w / 2),
 // columns 32 (w % 2)) with v_mfma_f32_32x32x2f32 from the two tiles in LDS
-// (4 consecutive dims per lane and 16-byte read, as in the projection).
+// (4 consecutive dims per lane and 16-byte read, as in the projection).  The
+// tiles pass through LDS in two halves of the head dims, the second half's
+// loads in flight during the first half's MFMAs (half the LDS: more
+// workgroups per CU).
 // Writes the scaled logits (-inf above the diagonal) and, per row, the tile's
 // max and sum of exp(logit - max).
 template <int DG>
 __global__ __launch_bounds__(kScoreThreads) void gate_logits_kernel(
     const float* __restrict__ qt, const float* __restrict__ kt, int Hq, int Hkv, int nqb,
     float scale, float* __restrict__ scores, float2* __restrict__ part) {
-  // The Q and K tiles, later the 64 x 65 scaled logits (2 x 64 x 36 >= 64 x 65).
-  __shared__ __attribute__((aligned(16))) float smem[2][kTile][DG + 4];
-  float (*qs)[DG + 4] = smem[0];
-  float (*ks)[DG + 4] = smem[1];
+  constexpr int DH = DG / 2;  // dims per half: the tiles go through LDS in two halves
+  constexpr int kHalfTile = kTile * (DH + 4);
+  constexpr int kSmem = 2 * kHalfTile > kTile * (kTile + 1) ? 2 * kHalfTile : kTile * (kTile + 1);
+  // The Q and K half-tiles, later the 64 x 65 scaled logits.
+  __shared__ __attribute__((aligned(16))) float smem[kSmem];
+  float (*qs)[DH + 4] = reinterpret_cast<float (*)[DH + 4]>(smem);
+  float (*ks)[DH + 4] = reinterpret_cast<float (*)[DH + 4]>(smem + kHalfTile);
   const int tid = threadIdx.x;
   const int ntiles = (nqb + kTile - 1) / kTile;
   const int npairs = ntiles * (ntiles + 1) / 2;
@@ -281,44 +290,50 @@ __global__ __launch_bounds__(kScoreThreads) void gate_logits_kernel(
   const float* qrow = qt + (size_t)bh * nqb * DG;
   const float* krow = kt + ((size_t)b * Hkv + g) * nqb * DG;
   const int i0 = kTile * it, j0 = kTile * jt;
-  {
-    // Both 64 x DG tiles: 16-byte loads, all issued before the LDS stores.
-    constexpr int kVec = kTile * DG / 4 / kScoreThreads;
-    f32x4 vq[kVec], vk[kVec];
+  constexpr int kVec = kTile * DH / 4 / kScoreThreads;  // 16-byte loads per thread and half
+  f32x4 vq[kVec], vk[kVec];
+  auto load = [&](int h) {
 #pragma unroll
     for (int n = 0; n < kVec; ++n) {
       const int x = tid + kScoreThreads * n;
-      const int r = x / (DG / 4), d4 = x % (DG / 4);
+      const int r = x / (DH / 4), d4 = x % (DH / 4) + h * (DH / 4);
       vq[n] = (i0 + r < nqb) ? reinterpret_cast<const f32x4*>(qrow + (size_t)(i0 + r) * DG)[d4]
                              : f32x4{};
       vk[n] = (j0 + r < nqb) ? reinterpret_cast<const f32x4*>(krow + (size_t)(j0 + r) * DG)[d4]
                              : f32x4{};
     }
-#pragma unroll
-    for (int n = 0; n < kVec; ++n) {
-      const int x = tid + kScoreThreads * n;
-      const int r = x / (DG / 4), d = 4 * (x % (DG / 4));
-      *reinterpret_cast<f32x4*>(&qs[r][d]) = vq[n];
-      *reinterpret_cast<f32x4*>(&ks[r][d]) = vk[n];
-    }
-  }
-  __syncthreads();
+  };
   const int lane = tid & 63, wv = tid >> 6;
   const int lr = lane & 31, hf = lane >> 5;
   const int rb = 32 * (wv >> 1), cb = 32 * (wv & 1);
   f32x16 acc = {};
-#pragma unroll 4
-  for (int g8 = 0; g8 < DG / 8; ++g8) {
-    const f32x4 av = *reinterpret_cast<const f32x4*>(&qs[rb + lr][8 * g8 + 4 * hf]);
-    const f32x4 bv = *reinterpret_cast<const f32x4*>(&ks[cb + lr][8 * g8 + 4 * hf]);
+  load(0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u], bv[u], acc, 0, 0, 0);
+  for (int h = 0; h < 2; ++h) {
+    if (h == 1) __syncthreads();  // every wave is done with the first half
+#pragma unroll
+    for (int n = 0; n < kVec; ++n) {
+      const int x = tid + kScoreThreads * n;
+      const int r = x / (DH / 4), d = 4 * (x % (DH / 4));
+      *reinterpret_cast<f32x4*>(&qs[r][d]) = vq[n];
+      *reinterpret_cast<f32x4*>(&ks[r][d]) = vk[n];
+    }
+    __syncthreads();
+    if (h == 0) load(1);  // in flight during the first half's MFMAs
+#pragma unroll 4
+    for (int g8 = 0; g8 < DH / 8; ++g8) {
+      const f32x4 av = *reinterpret_cast<const f32x4*>(&qs[rb + lr][8 * g8 + 4 * hf]);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(&ks[cb + lr][8 * g8 + 4 * hf]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u], bv[u], acc, 0, 0, 0);
+    }
   }
   // acc[v]: tile row rb + 8 (v / 4) + 4 hf + v % 4, tile column cb + lr.  The
   // scaled, masked tile goes through LDS (over the Q tile) so that four threads
   // own each row: coalesced score rows and two-step row reductions.
   __syncthreads();  // every wave is done with qs and ks
-  float (*st)[kTile + 1] = reinterpret_cast<float (*)[kTile + 1]>(&smem[0][0][0]);
+  float (*st)[kTile + 1] = reinterpret_cast<float (*)[kTile + 1]>(smem);
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int r = rb + 8 * (v / 4) + 4 * hf + (v % 4);
@@ -371,17 +386,36 @@ __global__ __launch_bounds__(64 * kRowWaves) void gate_softmax_kernel(
   const int ntiles = (nqb + kTile - 1) / kTile;
   const int it = i / kTile;
   const float2* pr = part + row * ntiles;
+  float* sr = scores + row * (long long)nqb;
+  // Causal part of the row in chunks of 512; the first chunk's loads are issued
+  // before the partials are combined, so the two round trips overlap.
+  constexpr int kPer = 8;
+  float x[kPer];
+  auto fetch = [&](int base) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = base + lane + 64 * u;
+      x[u] = (j <= i) ? sr[j] : 0.f;
+    }
+  };
+  fetch(0);
   float m = -INFINITY, l = 0.f;
-  for (int x = 0; x <= it; ++x) {  // same order in every lane
-    const float2 p = pr[x];
+  for (int t = 0; t <= it; ++t) {  // same order in every lane
+    const float2 p = pr[t];
     if (p.x == -INFINITY) continue;
     const float mn = fmaxf(m, p.x);
     l = (m == -INFINITY ? 0.f : l * expf(m - mn)) + p.y * expf(p.x - mn);
     m = mn;
   }
   const float inv = 1.0f / l;
-  float* sr = scores + row * (long long)nqb;
-  for (int j = lane; j < nqb; j += 64) sr[j] = (j <= i) ? expf(sr[j] - m) * inv : 0.f;
+  for (int base = 0; base < nqb; base += 64 * kPer) {
+    if (base > 0) fetch(base);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = base + lane + 64 * u;
+      if (j < nqb) sr[j] = (j <= i) ? expf(x[u] - m) * inv : 0.f;
+    }
+  }
 }
 
 }  // namespace
