@@ -545,10 +545,12 @@ def _gate_case(case):
         return wl.custom(81, 2, 4, 2, 128, 1000), 64
     if case == "d64":
         return wl.custom(82, 1, 6, 3, 64, 2000), 128
+    if case == "far128k":  # block positions up to 2047: RoPE angles of ~2000 rad
+        return wl.custom(86, 1, 2, 1, 64, 131072), 64
     return wl.custom(83, 1, 32, 8, 128, 8192, qkv_scale=1.0 / math.sqrt(128.0)), 128
 
 
-@pytest.mark.parametrize("case", ["tiny", "ragged", "d64", "llama8k"])
+@pytest.mark.parametrize("case", ["tiny", "ragged", "d64", "far128k", "llama8k"])
 def test_attn_gate_scores(case):
     w, dg = _gate_case(case)
     announce(f"attn gate scores {w.name} dg={dg}")
@@ -787,3 +789,16 @@ def test_sparse_decode_repeat_bitexact():
     a = _run_decode(dw, q, k, v, kv_len, idx, cnt)
     b = _run_decode(dw, q, k, v, kv_len, idx, cnt)
     assert torch.equal(a, b)
+
+
+def test_sparse_decode_kv_len_clamped():
+    """kv_len values above Tmax act as Tmax and negative ones as 0 (the call's
+    documented clamping): compared with the oracle on the clamped lengths."""
+    dw = _decode_case(94, 3, 4, 2, 640, 128, (640, 0, 300), list_heads="q")
+    q, k, v, _ = wl.make_decode_inputs(dw)
+    idx, cnt = _decode_lists(95, dw, 6)
+    given = torch.tensor([640 + 100, -5, 300], dtype=torch.int32)
+    got = _run_decode(dw, q, k, v, given, idx, cnt).float().cpu().numpy()
+    ref = oracle.sparse_decode_ref(q, k, v, [640, 0, 300], idx, cnt, None, dw.block)
+    assert np.abs(got - ref).max() <= O_TOL
+    assert (got[1] == 0).all()
