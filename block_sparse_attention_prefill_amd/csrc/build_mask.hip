@@ -118,6 +118,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
   if (k < npos) {
     uint32_t prefix = 0u, mask = 0u;
     int remaining = k;
+    bool exact = true;  // false: the select stopped at a fully needed bin
     for (int shift = 24; shift >= 0; shift -= 8) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) hist[lane + 64 * b] = 0;
@@ -136,12 +137,13 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
       }
       const int incl = wave_incl_scan(local, lane);
       int above = incl - local;
-      int sel_bin = -1, sel_above = 0;
+      int sel_bin = -1, sel_above = 0, sel_cnt = 0;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         if (sel_bin < 0 && above < remaining && remaining <= above + hc[b]) {
           sel_bin = 255 - 4 * lane - b;
           sel_above = above;
+          sel_cnt = hc[b];
         }
         above += hc[b];
       }
@@ -149,13 +151,25 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
       const int src = __builtin_ctzll(who);
       sel_bin = __shfl(sel_bin, src, 64);
       sel_above = __shfl(sel_above, src, 64);
+      sel_cnt = __shfl(sel_cnt, src, 64);
       prefix |= (uint32_t)sel_bin << shift;
       mask |= 0xFFu << shift;
       remaining -= sel_above;
       __builtin_amdgcn_wave_barrier();
+      if (remaining == sel_cnt) {
+        // Every key of the boundary bin is needed: keep exactly the keys whose
+        // digits so far are >= the prefix (lower digits zero), no tie rank.
+        exact = false;
+        break;
+      }
     }
-    t = prefix;
-    need = remaining;
+    if (exact) {
+      t = prefix;
+      need = remaining;
+    } else {
+      t = prefix > 0u ? prefix - 1u : 0u;
+      need = 0;
+    }
   }
 
   int base = 0, ties = 0;
