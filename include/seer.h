@@ -204,7 +204,9 @@ size_t seer_attn_gate_workspace_size(int B, int Hq, int Hkv, int T, int Dg);
  * scores   device fp32 out [B, Hq, nQB, nQB].
  * workspace device, >= seer_attn_gate_workspace_size(B, Hq, Hkv, T, Dg) bytes,
  *          256-byte aligned; overwritten.
- * Arithmetic is fp32 (RoPE angles in fp64); results are bit-reproducible.
+ * Arithmetic is fp32 (the linear layers and Q~K~^T on the fp32 matrix cores;
+ * RoPE angles formed and reduced mod 2 pi in fp64, then fp32 sin/cos); results
+ * are bit-reproducible.
  */
 int seer_attn_gate_scores(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
                           const float* wq, const float* wk, int Dg, float scale, float rope_base,
