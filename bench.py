@@ -197,6 +197,8 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run one plain device copy of this many MiB (to scale HBM "
                          "byte counters) and exit")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only run the sparse decode measurement and print it as JSON")
     args = ap.parse_args(argv)
 
     if args.copy_calibration_mib:
@@ -224,6 +226,9 @@ def main(argv=None) -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     seer.load()
     dev = torch.device("cuda:0")
+    if args.decode_only:
+        print(json.dumps({"decode": decode_bench(seer, wl, torch, dev, args)}), flush=True)
+        return 0
     w = wl.WORKLOADS[args.workload]
     assert w.kind == "sparse"
     log(f"[bench] generating {w.name}")
