@@ -9,8 +9,9 @@
 // are written as 0 and never read.
 //
 // HBM-bound: one wave64 per map row reads the row once to sum it and once more
-// to normalise (the second read hits L2), with coalesced 4-byte lanes.  The
-// sums use a fixed reduction order, so results are bit-reproducible.
+// to normalise (the second read hits L2), with coalesced 16-byte lanes when
+// the rows allow it (4-byte lanes otherwise).  The sums use a fixed reduction
+// order, so results are bit-reproducible.
 #include "seer_internal.h"
 
 namespace seer {
@@ -25,9 +26,14 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Row value of the target: a / s for a causal entry of a row whose sum s is
+// positive, else 0.
+__device__ __forceinline__ float norm_entry(float a, float s) { return s > 0.f ? a / s : 0.f; }
+
+// Scalar form: any nQB and any 4-byte alignment.
 __global__ __launch_bounds__(64 * kWaves) void pooled_target_kernel(
-    const float* __restrict__ amap, const float* __restrict__ gate, long long rows, int nqb,
-    float* target, float* __restrict__ row_sse) {
+    const float* amap, const float* __restrict__ gate, long long rows, int nqb, float* target,
+    float* __restrict__ row_sse) {
   const int lane = threadIdx.x & 63;
   const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -41,7 +47,7 @@ __global__ __launch_bounds__(64 * kWaves) void pooled_target_kernel(
   for (int j = lane; j < nqb; j += 64) {
     float v = 0.f;
     if (j <= i) {
-      v = s > 0.f ? a[j] / s : 0.f;
+      v = norm_entry(a[j], s);
       if (gate) {
         const float d = gate[row * (long long)nqb + j] - v;
         e = fmaf(d, d, e);
@@ -55,14 +61,155 @@ __global__ __launch_bounds__(64 * kWaves) void pooled_target_kernel(
   }
 }
 
+// 16-byte form (nQB % 4 == 0, all rows 16-byte aligned): lane L takes the
+// 4-float chunks L, L + 64, ...; chunks wholly inside j <= i move as one
+// 16-byte access, the chunk the diagonal cuts is read element by element so
+// that no entry j > i is read, and the chunks past it are written as zeros.
+// In place is safe: every chunk is read and written by the same lane, reads
+// first.
+__global__ __launch_bounds__(64 * kWaves) void pooled_target_vec_kernel(
+    const float* amap, const float* __restrict__ gate, long long rows, int nqb, float* target,
+    float* __restrict__ row_sse) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int i = (int)(row % nqb);
+  const int nch = nqb >> 2;
+  const int full = (i + 1) >> 2;  // chunks 0 .. full - 1 lie wholly in j <= i
+  const int rem = (i + 1) & 3;    // causal entries of chunk `full`
+  const float* a = amap + row * (long long)nqb;
+  const float4* a4 = reinterpret_cast<const float4*>(a);
+  float s = 0.f;
+  for (int c = lane; c < full; c += 64) {
+    const float4 x = a4[c];
+    s += (x.x + x.y) + (x.z + x.w);
+  }
+  if (rem && lane == (full & 63))
+    for (int u = 0; u < rem; ++u) s += a[4 * full + u];
+  s = wave_sum(s);  // every lane's reads of the row are done past this point
+  float4* t4 = reinterpret_cast<float4*>(target + row * (long long)nqb);
+  const float* g = gate ? gate + row * (long long)nqb : nullptr;
+  float e = 0.f;
+  for (int c = lane; c < nch; c += 64) {
+    float4 v = {0.f, 0.f, 0.f, 0.f};
+    if (c < full) {
+      const float4 x = a4[c];
+      v = {norm_entry(x.x, s), norm_entry(x.y, s), norm_entry(x.z, s), norm_entry(x.w, s)};
+      if (g) {
+        const float4 y = reinterpret_cast<const float4*>(g)[c];
+        const float d0 = y.x - v.x, d1 = y.y - v.y, d2 = y.z - v.z, d3 = y.w - v.w;
+        e = fmaf(d0, d0, e);
+        e = fmaf(d1, d1, e);
+        e = fmaf(d2, d2, e);
+        e = fmaf(d3, d3, e);
+      }
+    } else if (c == full && rem) {
+      float w[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < rem; ++u) {
+        w[u] = norm_entry(a[4 * c + u], s);
+        if (g) {
+          const float d = g[4 * c + u] - w[u];
+          e = fmaf(d, d, e);
+        }
+      }
+      v = {w[0], w[1], w[2], w[3]};
+    }
+    t4[c] = v;
+  }
+  if (gate && row_sse) {
+    e = wave_sum(e);
+    if (lane == 0) row_sse[row] = e;
+  }
+}
+
+// 16-byte form with the row held in registers (nQB <= 256 NC): the causal
+// chunks of the map and of the gate are all requested before the row sum, so a
+// row costs one memory round trip; the map is read once.  Same chunk rules as
+// above.
+template <int NC>
+__global__ __launch_bounds__(64 * kWaves) void pooled_target_reg_kernel(
+    const float* amap, const float* __restrict__ gate, long long rows, int nqb, float* target,
+    float* __restrict__ row_sse) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int i = (int)(row % nqb);
+  const int nch = nqb >> 2;
+  const int full = (i + 1) >> 2;
+  const int rem = (i + 1) & 3;
+  const float* a = amap + row * (long long)nqb;
+  const float* g = gate ? gate + row * (long long)nqb : nullptr;
+  const float4 zero = {0.f, 0.f, 0.f, 0.f};
+  float4 x[NC], y[NC];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    const int c = lane + 64 * u;
+    x[u] = zero;
+    y[u] = zero;
+    if (c < full) {
+      x[u] = reinterpret_cast<const float4*>(a)[c];
+      if (g) y[u] = reinterpret_cast<const float4*>(g)[c];
+    } else if (c == full && rem) {
+      float xa[4] = {0.f, 0.f, 0.f, 0.f}, ya[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < rem; ++k) {
+        xa[k] = a[4 * c + k];
+        if (g) ya[k] = g[4 * c + k];
+      }
+      x[u] = {xa[0], xa[1], xa[2], xa[3]};
+      y[u] = {ya[0], ya[1], ya[2], ya[3]};
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < NC; ++u) s += (x[u].x + x[u].y) + (x[u].z + x[u].w);
+  s = wave_sum(s);  // every lane's reads of the row are done past this point
+  float4* t4 = reinterpret_cast<float4*>(target + row * (long long)nqb);
+  float e = 0.f;
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    const int c = lane + 64 * u;
+    if (c >= nch) break;
+    // Entries past the diagonal hold 0 in x and y: their target is 0 and their
+    // error term (0 - 0)^2 adds nothing.
+    const float4 v = {norm_entry(x[u].x, s), norm_entry(x[u].y, s), norm_entry(x[u].z, s),
+                      norm_entry(x[u].w, s)};
+    if (g) {
+      const float d0 = y[u].x - v.x, d1 = y[u].y - v.y, d2 = y[u].z - v.z, d3 = y[u].w - v.w;
+      e = fmaf(d0, d0, e);
+      e = fmaf(d1, d1, e);
+      e = fmaf(d2, d2, e);
+      e = fmaf(d3, d3, e);
+    }
+    t4[c] = v;
+  }
+  if (gate && row_sse) {
+    e = wave_sum(e);
+    if (lane == 0) row_sse[row] = e;
+  }
+}
+
 // Mean of the per-row squared errors over all causal entries; one workgroup,
 // fixed summation order.
 __global__ __launch_bounds__(kLossThreads) void mse_loss_kernel(const float* __restrict__ row_sse,
                                                               long long rows, double count,
                                                               float* __restrict__ loss) {
   __shared__ double part[kLossThreads / 64];
+  // 32 independent loads in flight per thread (indices past the end re-read
+  // the last row and are dropped by a select, so no load is predicated); the
+  // additions keep the fixed order r = tid, tid + 1024, ...
+  constexpr int kBatch = 32;
   double s = 0.0;
-  for (long long r = threadIdx.x; r < rows; r += kLossThreads) s += (double)row_sse[r];
+  for (long long r0 = threadIdx.x; r0 < rows; r0 += (long long)kBatch * kLossThreads) {
+    float x[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const long long r = r0 + (long long)u * kLossThreads;
+      x[u] = row_sse[r < rows ? r : rows - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      s += r0 + (long long)u * kLossThreads < rows ? (double)x[u] : 0.0;
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
@@ -80,8 +227,18 @@ hipError_t launch_pooled_target(const float* amap, const float* gate, int B, int
                                 float* target, float* row_sse, float* loss, hipStream_t stream) {
   const long long rows = (long long)B * H * nqb;
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(pooled_target_kernel, dim3((unsigned)((rows + kWaves - 1) / kWaves)),
-                     dim3(64 * kWaves), 0, stream, amap, gate, rows, nqb, target, row_sse);
+  const bool vec = nqb % 4 == 0 &&
+                   (((uintptr_t)amap | (uintptr_t)gate | (uintptr_t)target) & 15) == 0;
+  auto kernel = pooled_target_kernel;
+  if (vec) {
+    const int per_lane = (nqb / 4 + 63) / 64;  // 16-byte chunks per lane
+    kernel = per_lane <= 2   ? pooled_target_reg_kernel<2>
+             : per_lane <= 4 ? pooled_target_reg_kernel<4>
+             : per_lane <= 8 ? pooled_target_reg_kernel<8>
+                             : pooled_target_vec_kernel;
+  }
+  hipLaunchKernelGGL(kernel, dim3((unsigned)((rows + kWaves - 1) / kWaves)), dim3(64 * kWaves),
+                     0, stream, amap, gate, rows, nqb, target, row_sse);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !loss) return err;
   const double count = (double)B * H * ((double)nqb * (nqb + 1) / 2);

@@ -482,7 +482,10 @@ SSE_RTOL = 1e-4   # per-row squared error (fp32 sums of <= 4096 terms)
 LOSS_RTOL = 1e-5  # loss: fp64 sum of the row errors
 
 
-@pytest.mark.parametrize("b,h,nqb", [(1, 2, 8), (2, 3, 13), (1, 40, 512)])
+# nQB 8 .. 512: rows held in registers (2 chunks per lane); 1000, 2000: 4 and 8
+# chunks per lane; 2052: the re-reading 16-byte form; 13: the 4-byte form.
+@pytest.mark.parametrize("b,h,nqb", [(1, 2, 8), (2, 3, 13), (1, 40, 512), (1, 1, 1000),
+                                     (1, 1, 2000), (1, 1, 2052)])
 def test_pooled_target_random_maps(b, h, nqb):
     announce(f"pooled target b={b} h={h} nqb={nqb}")
     w = wl.custom(40 + nqb, b, h, 1, 64, 64 * nqb, scores="softmax_normal")
@@ -496,8 +499,9 @@ def test_pooled_target_random_maps(b, h, nqb):
     assert abs(float(l.cpu()) - rl) <= LOSS_RTOL * rl
 
 
-def test_pooled_target_in_place_and_without_gate():
-    w = wl.custom(60, 1, 4, 1, 64, 64 * 37, scores="softmax_normal")
+@pytest.mark.parametrize("nqb", [37, 40])  # 4-byte and 16-byte row forms
+def test_pooled_target_in_place_and_without_gate(nqb):
+    w = wl.custom(60, 1, 4, 1, 64, 64 * nqb, scores="softmax_normal")
     amap = wl.make_block_map(w)
     rt, _, _ = oracle.pooled_target_ref(amap.numpy())
     a = _dev(amap)
@@ -505,6 +509,27 @@ def test_pooled_target_in_place_and_without_gate():
     torch.cuda.synchronize()
     assert r is None and l is None and t.data_ptr() == a.data_ptr()
     assert float(np.abs(a.cpu().double().numpy() - rt).max()) <= T_TOL
+
+
+def test_pooled_target_unaligned_buffers():
+    """nQB % 4 == 0 but buffers only 4-byte aligned: the 4-byte row form runs."""
+    w = wl.custom(63, 1, 3, 1, 64, 64 * 24, scores="softmax_normal")
+    amap, gate = wl.make_block_map(w), wl.make_scores(w)
+    n = amap.numel()
+    ab = torch.zeros(n + 1, dtype=torch.float32, device="cuda")
+    gb = torch.zeros(n + 1, dtype=torch.float32, device="cuda")
+    tb = torch.zeros(n + 1, dtype=torch.float32, device="cuda")
+    a, g, t = (x[1:].view(amap.shape) for x in (ab, gb, tb))
+    a.copy_(amap.cuda())
+    g.copy_(gate.cuda())
+    t_out, r, l = seer.seer_pooled_target_mse(a, g, target=t)
+    torch.cuda.synchronize()
+    rt, rr, rl = oracle.pooled_target_ref(amap.numpy(), gate.numpy())
+    assert t_out.data_ptr() == t.data_ptr()
+    assert float(np.abs(t.cpu().double().numpy() - rt).max()) <= T_TOL
+    assert np.allclose(r.cpu().double().numpy(), rr, rtol=SSE_RTOL, atol=1e-12)
+    assert abs(float(l.cpu()) - rl) <= LOSS_RTOL * rl
+    assert float(tb[0]) == 0.0  # nothing written before the view
 
 
 def test_pooled_target_chain_from_pooled_map():
