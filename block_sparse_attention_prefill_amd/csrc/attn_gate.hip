@@ -12,7 +12,7 @@
 //
 // Four kernels:
 // * gate_pool_kernel: one wave per (batch, head, 64-token block) pools the block
-//   (16-byte loads all in flight, lane shuffles to combine).
+//   (non-temporal 16-byte loads all in flight, lane shuffles to combine).
 // * gate_project_kernel: one workgroup per (batch, head, 64 blocks) applies the
 //   head's linear layer on the fp32 matrix cores (v_mfma_f32_32x32x2f32, fp32
 //   operands and accumulation) and the block RoPE, whose angles are formed and
@@ -37,7 +37,7 @@ constexpr int kTile = 64;  // query and key blocks per scores tile; tokens per b
 // row), all its loads in flight at once; lanes holding the same chunk are
 // combined with shuffles.  Q heads are averaged into pq [B, Hq, nQB, D], KV
 // heads max- and min-pooled into pk [B, Hkv, nQB, 2D] ([max | min]).
-constexpr int kPoolWaves = 4;
+constexpr int kPoolWaves = 8;
 
 template <int D>
 __global__ __launch_bounds__(64 * kPoolWaves) void gate_pool_kernel(
@@ -63,7 +63,9 @@ __global__ __launch_bounds__(64 * kPoolWaves) void gate_pool_kernel(
 #pragma unroll
   for (int u = 0; u < kPerLane; ++u) {
     const int r = r0 + rg + R * u;
-    if (r < r1) x[u] = *reinterpret_cast<const bf16x8*>(src + (size_t)r * D + 8 * ch);
+    if (r < r1)  // read once: non-temporal, so it does not displace reused data in L2
+      x[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const bf16x8*>(src + (size_t)r * D + 8 * ch));
   }
   float a[8], m[8];
 #pragma unroll
