@@ -118,6 +118,29 @@ def test_mask_edge_cases(mode, dens, thr, sink, max_k):
     np.testing.assert_array_equal(gi, ri)
 
 
+@pytest.mark.parametrize("n", [3000, 4096])  # the longest rows: 64 key slots per lane
+@pytest.mark.parametrize("mode,dens,thr,max_k", [(wl.MODE_TOPK, 0.05, 0.0, None),
+                                                 (wl.MODE_THRESHOLD, 1.0, 0.15, 700)])
+def test_mask_longest_rows_sampled(n, mode, dens, thr, max_k):
+    announce(f"mask longest rows n={n} mode={mode}")
+    s = _edge_scores(8 + n, 1, n, n)
+    if max_k is None:
+        max_k = oracle.topk_count(n - 1, dens, True)
+    w = wl.custom(92, 1, 1, 1, 64, n * 64, mode=mode, density=dens, threshold=thr,
+                  keep_sink=True)
+    gi, gc = _gpu_mask(w, s, max_k)
+    rows = [(0, 0, i) for i in sorted({0, 1, 2, 63, 64, 65, 1000, 2047, 2048, 2049, n - 2, n - 1})]
+    rows += [(0, 0, int(i)) for i in np.random.default_rng(n).integers(0, n, 8)]
+    ref = oracle.mask_rows_ref(s.numpy(), rows, mode, thr, dens, True, max_k)
+    for (b, h, i), want in ref.items():
+        assert gc[b, h, i] == len(want), (i, gc[b, h, i], len(want))
+        assert gi[b, h, i, : len(want)].tolist() == want, i
+        assert (gi[b, h, i, len(want):] == -1).all()
+    if mode == wl.MODE_TOPK:
+        ks = np.array([oracle.topk_count(i, dens, True) for i in range(n)])
+        assert (gc[0, 0] == ks).all()
+
+
 def test_mask_single_block():
     s = torch.full((2, 3, 1, 1), float("nan"))
     w = wl.custom(91, 2, 3, 3, 64, 64, density=0.1)
@@ -689,6 +712,24 @@ def test_decode_mask_bitexact(block, mode, thr, kb, sink, ties_nan):
     torch.cuda.synchronize()
     ri, rc = oracle.build_mask_decode_ref(s.numpy(), dw.kv_lens, block, mode, thr, max(kb, 1),
                                           sink, max_k)
+    np.testing.assert_array_equal(gc.cpu().numpy(), rc)
+    np.testing.assert_array_equal(gi.cpu().numpy(), ri)
+
+
+@pytest.mark.parametrize("mode,thr,kb", [(wl.MODE_TOPK, 0.0, 64), (wl.MODE_THRESHOLD, 2.0, 0)])
+def test_decode_mask_longest_rows(mode, thr, kb):
+    """nKB = 4096 (the limit): rows of 64 key slots per lane, full and ragged sequences."""
+    dw = _decode_case(72, 3, 2, 1, 4096 * 64, 64, (4096 * 64, 100001, 64 * 4095 + 1))
+    announce(f"decode mask longest rows mode {mode}")
+    s = _decode_mask_scores(73, dw)
+    assert s.shape[-1] == 4096
+    max_k = 4096 if mode == wl.MODE_THRESHOLD else kb
+    kv_len = torch.tensor(dw.kv_lens, dtype=torch.int32)
+    gi, gc = seer.seer_build_mask_decode(_dev(s), _dev(kv_len), 64, mode, thr, max(kb, 1), True,
+                                         max_k)
+    torch.cuda.synchronize()
+    ri, rc = oracle.build_mask_decode_ref(s.numpy(), dw.kv_lens, 64, mode, thr, max(kb, 1),
+                                          True, max_k)
     np.testing.assert_array_equal(gc.cpu().numpy(), rc)
     np.testing.assert_array_equal(gi.cpu().numpy(), ri)
 
