@@ -47,10 +47,11 @@ __global__ __launch_bounds__(64 * kPoolWaves) void gate_pool_kernel(
   constexpr int R = 64 / C;         // rows read together by the wave
   constexpr int kPerLane = kTile / R;
   const int lane = threadIdx.x & 63;
-  const long long unit = (long long)blockIdx.x * kPoolWaves + (threadIdx.x >> 6);
-  if (unit >= (long long)B * (Hq + Hkv) * nqb) return;
-  const int i = (int)(unit % nqb);
-  const int bh = (int)(unit / nqb);  // b * (Hq + Hkv) + head slot
+  // B (Hq + Hkv) nQB < 2^31 (checked by the host layer): 32-bit unit arithmetic.
+  const int unit = blockIdx.x * kPoolWaves + (threadIdx.x >> 6);
+  if (unit >= B * (Hq + Hkv) * nqb) return;
+  const int i = unit % nqb;
+  const int bh = unit / nqb;  // b * (Hq + Hkv) + head slot
   const int b = bh / (Hq + Hkv);
   const int slot = bh % (Hq + Hkv);
   const bool is_q = slot < Hq;
@@ -377,41 +378,47 @@ __global__ __launch_bounds__(kScoreThreads) void gate_logits_kernel(
 // One wave per score row: combine the row's per-tile (max, sum) pairs, then
 // turn its logits into probabilities in place and zero the entries above the
 // diagonal (including the tiles past the diagonal tile, never written above).
+// The pairs (one per lane, 64 tiles at a time) and the row's first 512 entries
+// are all requested before the combine; the combine reads the pairs lane by
+// lane in tile order, so the result does not depend on timing.
 constexpr int kRowWaves = 4;
 
 __global__ __launch_bounds__(64 * kRowWaves) void gate_softmax_kernel(
-    long long rows, int nqb, float* __restrict__ scores, const float2* __restrict__ part) {
+    int rows, int nqb, float* __restrict__ scores, const float2* __restrict__ part) {
   const int lane = threadIdx.x & 63;
-  const long long row = (long long)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+  const int row = blockIdx.x * kRowWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const int i = (int)(row % nqb);
+  const int i = row % nqb;
   const int ntiles = (nqb + kTile - 1) / kTile;
   const int it = i / kTile;
-  const float2* pr = part + row * ntiles;
-  float* sr = scores + row * (long long)nqb;
-  // Causal part of the row in chunks of 512; the first chunk's loads are issued
-  // before the partials are combined, so the two round trips overlap.
+  const float2* pr = part + (size_t)row * ntiles;
+  float* sr = scores + (size_t)row * nqb;
+  // Causal part of the row in chunks of 512: entry j <= i, else a re-read of
+  // entry i that is never used (no entry above the diagonal is read).
   constexpr int kPer = 8;
   float x[kPer];
   auto fetch = [&](int base) {
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int j = base + lane + 64 * u;
-      x[u] = (j <= i) ? sr[j] : 0.f;
-    }
+    for (int u = 0; u < kPer; ++u) x[u] = sr[min(base + lane + 64 * u, i)];
   };
+  float2 mine = lane <= it ? pr[lane] : make_float2(-INFINITY, 0.f);
   fetch(0);
   float m = -INFINITY, l = 0.f;
-  for (int t = 0; t <= it; ++t) {  // same order in every lane
-    const float2 p = pr[t];
-    if (p.x == -INFINITY) continue;
-    const float mn = fmaxf(m, p.x);
-    l = (m == -INFINITY ? 0.f : l * expf(m - mn)) + p.y * expf(p.x - mn);
-    m = mn;
+  for (int t0 = 0; t0 <= it; t0 += 64) {
+    if (t0 > 0) mine = t0 + lane <= it ? pr[t0 + lane] : make_float2(-INFINITY, 0.f);
+    const int tn = min(it - t0, 63);
+    for (int t = 0; t <= tn; ++t) {  // same order in every lane
+      const float px = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.x), t));
+      const float py = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.y), t));
+      if (px == -INFINITY) continue;
+      const float mn = fmaxf(m, px);
+      l = (m == -INFINITY ? 0.f : l * expf(m - mn)) + py * expf(px - mn);
+      m = mn;
+    }
   }
   const float inv = 1.0f / l;
   for (int base = 0; base < nqb; base += 64 * kPer) {
-    if (base > 0) fetch(base);
+    if (base > 0 && base <= i) fetch(base);
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int j = base + lane + 64 * u;
@@ -474,7 +481,7 @@ hipError_t launch_attn_gate(const void* q, const void* k, int B, int Hq, int Hkv
 #undef SEER_GATE_LOGITS
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const long long rows = (long long)B * Hq * nqb;
+  const int rows = B * Hq * nqb;  // < 2^31: the host layer checks B (Hq + Hkv) nQB
   hipLaunchKernelGGL(gate_softmax_kernel, dim3((unsigned)((rows + kRowWaves - 1) / kRowWaves)),
                      dim3(64 * kRowWaves), 0, stream, rows, nqb, scores, part);
   return hipGetLastError();

@@ -32,12 +32,12 @@ __device__ __forceinline__ float norm_entry(float a, float s) { return s > 0.f ?
 
 // Scalar form: any nQB and any 4-byte alignment.
 __global__ __launch_bounds__(64 * kWaves) void pooled_target_kernel(
-    const float* amap, const float* __restrict__ gate, long long rows, int nqb, float* target,
+    const float* amap, const float* __restrict__ gate, int rows, int nqb, float* target,
     float* __restrict__ row_sse) {
   const int lane = threadIdx.x & 63;
-  const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const int i = (int)(row % nqb);
+  const int i = row % nqb;
   const float* a = amap + row * (long long)nqb;
   float* t = target + row * (long long)nqb;
   float s = 0.f;
@@ -68,12 +68,12 @@ __global__ __launch_bounds__(64 * kWaves) void pooled_target_kernel(
 // In place is safe: every chunk is read and written by the same lane, reads
 // first.
 __global__ __launch_bounds__(64 * kWaves) void pooled_target_vec_kernel(
-    const float* amap, const float* __restrict__ gate, long long rows, int nqb, float* target,
+    const float* amap, const float* __restrict__ gate, int rows, int nqb, float* target,
     float* __restrict__ row_sse) {
   const int lane = threadIdx.x & 63;
-  const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const int i = (int)(row % nqb);
+  const int i = row % nqb;
   const int nch = nqb >> 2;
   const int full = (i + 1) >> 2;  // chunks 0 .. full - 1 lie wholly in j <= i
   const int rem = (i + 1) & 3;    // causal entries of chunk `full`
@@ -128,12 +128,12 @@ __global__ __launch_bounds__(64 * kWaves) void pooled_target_vec_kernel(
 // above.
 template <int NC>
 __global__ __launch_bounds__(64 * kWaves) void pooled_target_reg_kernel(
-    const float* amap, const float* __restrict__ gate, long long rows, int nqb, float* target,
+    const float* amap, const float* __restrict__ gate, int rows, int nqb, float* target,
     float* __restrict__ row_sse) {
   const int lane = threadIdx.x & 63;
-  const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const int i = (int)(row % nqb);
+  const int i = row % nqb;
   const int nch = nqb >> 2;
   const int full = (i + 1) >> 2;
   const int rem = (i + 1) & 3;
@@ -237,8 +237,9 @@ hipError_t launch_pooled_target(const float* amap, const float* gate, int B, int
              : per_lane <= 8 ? pooled_target_reg_kernel<8>
                              : pooled_target_vec_kernel;
   }
+  // rows < 2^31: the host layer checks B H nQB.
   hipLaunchKernelGGL(kernel, dim3((unsigned)((rows + kWaves - 1) / kWaves)), dim3(64 * kWaves),
-                     0, stream, amap, gate, rows, nqb, target, row_sse);
+                     0, stream, amap, gate, (int)rows, nqb, target, row_sse);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !loss) return err;
   const double count = (double)B * H * ((double)nqb * (nqb + 1) / 2);
