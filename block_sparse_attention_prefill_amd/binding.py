@@ -157,6 +157,10 @@ def pooled_attn_map_workspace_size(b: int, hq: int, t: int) -> int:
     return load().seer_pooled_attn_map_workspace_size(b, hq, t)
 
 
+def attn_gate_workspace_size(b: int, hq: int, hkv: int, t: int, dg: int) -> int:
+    return load().seer_attn_gate_workspace_size(b, hq, hkv, t, dg)
+
+
 def _workspace(nbytes: int, device) -> torch.Tensor:
     # torch's caching allocator hands out 512-byte aligned blocks.
     return torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=device)
@@ -293,7 +297,6 @@ def seer_attn_gate_scores(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor, wk
         _ptr(scores), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return scores
-
 
 
 def seer_build_mask_decode(scores: torch.Tensor, kv_len: torch.Tensor, block: int, mode: int,

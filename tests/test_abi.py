@@ -54,6 +54,11 @@ def test_workspace_sizes():
     # 64 fp32 per causal tile: 40 heads * 512*513/2 tiles at 32k tokens.
     assert seer.pooled_attn_map_workspace_size(1, 40, 32768) >= 40 * (512 * 513 // 2) * 64 * 4
     assert seer.pooled_attn_map_workspace_size(1, 0, 64) == 0
+    # gate: Q~, K~, tile partials, pooled Q and K (fp32)
+    nqb, nt = 512, 8
+    floats = (32 + 8) * nqb * 128 + 2 * 32 * nqb * nt + (32 + 2 * 8) * nqb * 128
+    assert seer.attn_gate_workspace_size(1, 32, 8, 32768, 128) >= floats * 4
+    assert seer.attn_gate_workspace_size(1, 32, 7, 32768, 128) == 0  # Hq % Hkv != 0
 
 
 FAKE = 1 << 20  # never dereferenced: every call below fails its host checks first
