@@ -390,13 +390,32 @@ def main(argv=None) -> int:
         gcall()
         g_ms = time_calls(gcall, max(3, args.steps // 2), torch)
         g_bytes = 2 * (qd.numel() + kd.numel()) + 4 * gs.numel()
+        # The same gate straight into the bench's TopK lists in one call (no score
+        # map written), against scores + seer_build_mask.
+        gmk = seer.topk_budget(w.nqb, w.density, w.keep_sink)
+        gidx = torch.empty((w.batch, w.hq, w.nqb, gmk), dtype=torch.int32, device=dev)
+        gcnt = torch.empty((w.batch, w.hq, w.nqb), dtype=torch.int32, device=dev)
+        gws2 = torch.empty((seer.attn_gate_mask_workspace_size(
+            w.batch, w.hq, w.hkv, w.seq, dg, False),), dtype=torch.uint8, device=dev)
+        fcall = lambda: seer.seer_attn_gate_mask(qd, kd, wq, wk, w.mode, w.threshold, w.density,
+                                                 w.keep_sink, gmk, kv_idx=gidx, kv_cnt=gcnt,
+                                                 workspace=gws2)
+        tcall2 = lambda: (gcall(), seer.seer_build_mask(gs, w.mode, w.threshold, w.density,
+                                                        w.keep_sink, gmk, kv_idx=gidx,
+                                                        kv_cnt=gcnt))
+        fcall()
+        tcall2()
+        f_ms = time_calls(fcall, max(3, args.steps // 2), torch)
+        t2_ms = time_calls(tcall2, max(3, args.steps // 2), torch)
         result["attn_gate"] = {
             "ms": round(g_ms, 4),
             "gate_dim": dg,
             "gbps": round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
             "algorithmic_bytes": g_bytes,
+            "gate_to_lists_fused_ms": round(f_ms, 4),
+            "gate_then_build_mask_ms": round(t2_ms, 4),
         }
-        del wq, wk, gs, gws
+        del wq, wk, gs, gws, gws2, gidx, gcnt
 
         # The bench workload's shape with 128-token blocks (TopK at the same density).
         w128 = wl.custom(103, w.batch, w.hq, w.hkv, w.head_dim, w.seq, mode=w.mode,

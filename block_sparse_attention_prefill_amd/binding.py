@@ -25,7 +25,8 @@ EXPORTED = (
     "seer_status_string", "seer_version", "seer_topk_budget", "seer_build_mask",
     "seer_sparse_prefill_workspace_size", "seer_sparse_prefill", "seer_sparse_prefill_block",
     "seer_pooled_attn_map_workspace_size", "seer_pooled_attn_map", "seer_pooled_target_mse",
-    "seer_attn_gate_workspace_size", "seer_attn_gate_scores", "seer_build_mask_decode",
+    "seer_attn_gate_workspace_size", "seer_attn_gate_scores", "seer_attn_gate_mask_workspace_size",
+    "seer_attn_gate_mask", "seer_build_mask_decode",
     "seer_sparse_decode_workspace_size", "seer_sparse_decode",
 )
 
@@ -80,6 +81,13 @@ def load() -> ctypes.CDLL:
     lib.seer_attn_gate_scores.argtypes = [c_void, c_void, c_int, c_int, c_int, c_int, c_int,
                                           c_void, c_void, c_int, c_float, c_float, c_void,
                                           c_void, c_size, c_void]
+    lib.seer_attn_gate_mask_workspace_size.restype = c_size
+    lib.seer_attn_gate_mask_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
+    lib.seer_attn_gate_mask.restype = c_int
+    lib.seer_attn_gate_mask.argtypes = [c_void, c_void, c_int, c_int, c_int, c_int, c_int,
+                                        c_void, c_void, c_int, c_float, c_float, c_int, c_float,
+                                        c_double, c_int, c_void, c_void, c_int, c_void, c_void,
+                                        c_size, c_void]
     lib.seer_pooled_target_mse.restype = c_int
     lib.seer_pooled_target_mse.argtypes = [c_void, c_void, c_int, c_int, c_int, c_void, c_void,
                                            c_void, c_void]
@@ -297,6 +305,49 @@ def seer_attn_gate_scores(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor, wk
         _ptr(scores), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return scores
+
+
+def attn_gate_mask_workspace_size(b: int, hq: int, hkv: int, t: int, dg: int,
+                                  with_scores: bool) -> int:
+    return load().seer_attn_gate_mask_workspace_size(b, hq, hkv, t, dg, int(bool(with_scores)))
+
+
+def seer_attn_gate_mask(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor, wk: torch.Tensor,
+                        mode: int, threshold: float, density: float, keep_sink: bool, max_k: int,
+                        scale: Optional[float] = None, rope_base: float = 10000.0,
+                        return_scores: bool = False, kv_idx: Optional[torch.Tensor] = None,
+                        kv_cnt: Optional[torch.Tensor] = None,
+                        scores: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None):
+    """AttnGate scores straight into block lists: (kv_idx [B,Hq,nQB,max_k], kv_cnt
+    [B,Hq,nQB], scores [B,Hq,nQB,nQB] or None).  Scores are written only when
+    return_scores is set or a scores buffer is passed."""
+    lib = load()
+    b, hq, hkv, t, d = _qkv_dims(q, k, k)
+    dg = wq.shape[-1]
+    nqb = (t + BLOCK - 1) // BLOCK
+    _need(wq, "wq", torch.float32, (hq, d, dg))
+    _need(wk, "wk", torch.float32, (hkv, 2 * d, dg))
+    if scores is None and return_scores:
+        scores = torch.empty((b, hq, nqb, nqb), dtype=torch.float32, device=q.device)
+    if scores is not None:
+        _need(scores, "scores", torch.float32, (b, hq, nqb, nqb))
+    if kv_idx is None:
+        kv_idx = torch.empty((b, hq, nqb, max_k), dtype=torch.int32, device=q.device)
+    if kv_cnt is None:
+        kv_cnt = torch.empty((b, hq, nqb), dtype=torch.int32, device=q.device)
+    _need(kv_idx, "kv_idx", torch.int32, (b, hq, nqb, max_k))
+    _need(kv_cnt, "kv_cnt", torch.int32, (b, hq, nqb))
+    need = lib.seer_attn_gate_mask_workspace_size(b, hq, hkv, t, dg, int(scores is not None))
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    sc = (1.0 / dg ** 0.5) if scale is None else float(scale)
+    _check("seer_attn_gate_mask", lib.seer_attn_gate_mask(
+        _ptr(q), _ptr(k), b, hq, hkv, t, d, _ptr(wq), _ptr(wk), int(dg), sc, float(rope_base),
+        int(mode), float(threshold), float(density), int(bool(keep_sink)), _ptr(kv_idx),
+        _ptr(kv_cnt), int(max_k), _ptr(scores), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return kv_idx, kv_cnt, scores
 
 
 def seer_build_mask_decode(scores: torch.Tensor, kv_len: torch.Tensor, block: int, mode: int,

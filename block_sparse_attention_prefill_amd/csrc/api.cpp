@@ -186,6 +186,50 @@ int seer_attn_gate_scores(const void* q, const void* k, int B, int Hq, int Hkv, 
   return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
 }
 
+size_t seer_attn_gate_mask_workspace_size(int B, int Hq, int Hkv, int T, int Dg,
+                                          int with_scores) {
+  const size_t gate = seer_attn_gate_workspace_size(B, Hq, Hkv, T, Dg);
+  if (gate == 0) return 0;
+  const size_t nqb = (size_t)nqb_of(T);
+  return gate + (with_scores ? 0 : (size_t)B * Hq * nqb * nqb * sizeof(float));
+}
+
+int seer_attn_gate_mask(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
+                        const float* wq, const float* wk, int Dg, float scale, float rope_base,
+                        int mode, float threshold, double density, int keep_sink,
+                        int32_t* kv_idx, int32_t* kv_cnt, int max_k, float* scores,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return SEER_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return SEER_ERR_UNSUPPORTED;
+  if (Dg != 32 && Dg != 64 && Dg != 128) return SEER_ERR_UNSUPPORTED;
+  if (!(isfinite(scale) && scale > 0.f)) return SEER_ERR_INVALID_ARG;
+  if (!(isfinite(rope_base) && rope_base > 1.f)) return SEER_ERR_INVALID_ARG;
+  const int nQB = nqb_of(T);
+  if (nQB > SEER_MAX_QUERY_BLOCKS) return SEER_ERR_UNSUPPORTED;
+  if (!items_fit(B, Hq + Hkv, nQB)) return SEER_ERR_UNSUPPORTED;
+  if (mode != SEER_MASK_TOPK && mode != SEER_MASK_THRESHOLD) return SEER_ERR_INVALID_ARG;
+  if (mode == SEER_MASK_TOPK && !(density > 0.0 && density <= 1.0)) return SEER_ERR_INVALID_ARG;
+  if (mode == SEER_MASK_THRESHOLD && !isfinite(threshold)) return SEER_ERR_INVALID_ARG;
+  if (max_k < 1) return SEER_ERR_CAPACITY;
+  if ((long long)B * T == 0) return SEER_OK;
+  if (!q || !k || !wq || !wk || !kv_idx || !kv_cnt) return SEER_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(wq) || !aligned16(wk))
+    return SEER_ERR_INVALID_ARG;
+  if (mode == SEER_MASK_TOPK) {
+    if (max_k < seer_topk_budget(nQB, density, keep_sink)) return SEER_ERR_CAPACITY;
+  } else {
+    const int forced = (keep_sink && nQB > 1) ? 2 : 1;
+    if (max_k < forced) return SEER_ERR_CAPACITY;
+  }
+  const size_t need = seer_attn_gate_mask_workspace_size(B, Hq, Hkv, T, Dg, scores ? 1 : 0);
+  if (!workspace || workspace_bytes < need || !aligned256(workspace)) return SEER_ERR_WORKSPACE;
+  const hipError_t err = seer::launch_attn_gate_mask(
+      q, k, B, Hq, Hkv, T, D, wq, wk, Dg, scale, rope_base, mode, threshold, density,
+      keep_sink ? 1 : 0, kv_idx, kv_cnt, max_k, scores, static_cast<float*>(workspace),
+      (hipStream_t)stream);
+  return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
+}
+
 int seer_build_mask_decode(const float* scores, const int32_t* kv_len, int B, int H, int nKB,
                            int block, int mode, float threshold, int k_blocks, int keep_sink,
                            int32_t* kv_idx, int32_t* kv_cnt, int max_k, void* stream) {

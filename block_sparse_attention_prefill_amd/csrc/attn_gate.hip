@@ -22,7 +22,7 @@
 //   tile max and sum of exponentials; gate_softmax_kernel
 //   then combines a row's partials in a fixed order and normalises the row in
 //   place, zeros above the diagonal.
-#include "seer_internal.h"
+#include "mask_select.h"
 
 #include <math.h>
 
@@ -383,6 +383,26 @@ __global__ __launch_bounds__(kScoreThreads) void gate_logits_kernel(
 // lane in tile order, so the result does not depend on timing.
 constexpr int kRowWaves = 4;
 
+// A row's (max, sum of exponentials) from its tiles' pairs pr[0 .. it], taken
+// in tile order in every lane; `mine` holds pair `lane` (already requested).
+__device__ __forceinline__ void combine_row_partials(const float2* __restrict__ pr, int it,
+                                                     int lane, float2 mine, float& m, float& l) {
+  m = -INFINITY;
+  l = 0.f;
+  for (int t0 = 0; t0 <= it; t0 += 64) {
+    if (t0 > 0) mine = t0 + lane <= it ? pr[t0 + lane] : make_float2(-INFINITY, 0.f);
+    const int tn = min(it - t0, 63);
+    for (int t = 0; t <= tn; ++t) {
+      const float px = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.x), t));
+      const float py = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.y), t));
+      if (px == -INFINITY) continue;
+      const float mn = fmaxf(m, px);
+      l = (m == -INFINITY ? 0.f : l * expf(m - mn)) + py * expf(px - mn);
+      m = mn;
+    }
+  }
+}
+
 __global__ __launch_bounds__(64 * kRowWaves) void gate_softmax_kernel(
     int rows, int nqb, float* __restrict__ scores, const float2* __restrict__ part) {
   const int lane = threadIdx.x & 63;
@@ -403,19 +423,8 @@ __global__ __launch_bounds__(64 * kRowWaves) void gate_softmax_kernel(
   };
   float2 mine = lane <= it ? pr[lane] : make_float2(-INFINITY, 0.f);
   fetch(0);
-  float m = -INFINITY, l = 0.f;
-  for (int t0 = 0; t0 <= it; t0 += 64) {
-    if (t0 > 0) mine = t0 + lane <= it ? pr[t0 + lane] : make_float2(-INFINITY, 0.f);
-    const int tn = min(it - t0, 63);
-    for (int t = 0; t <= tn; ++t) {  // same order in every lane
-      const float px = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.x), t));
-      const float py = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.y), t));
-      if (px == -INFINITY) continue;
-      const float mn = fmaxf(m, px);
-      l = (m == -INFINITY ? 0.f : l * expf(m - mn)) + py * expf(px - mn);
-      m = mn;
-    }
-  }
+  float m, l;
+  combine_row_partials(pr, it, lane, mine, m, l);
   const float inv = 1.0f / l;
   for (int base = 0; base < nqb; base += 64 * kPer) {
     if (base > 0 && base <= i) fetch(base);
@@ -425,6 +434,68 @@ __global__ __launch_bounds__(64 * kRowWaves) void gate_softmax_kernel(
       if (j < nqb) sr[j] = (j <= i) ? expf(x[u] - m) * inv : 0.f;
     }
   }
+}
+
+// Softmax and block selection of a score row in one pass (one wave per row,
+// the whole causal row in registers, candidate j = 64 c + lane in slot c).
+// The probabilities are those of gate_softmax_kernel, bit for bit, and the
+// lists those seer_build_mask makes from them (same keys, same count rule,
+// same select); with write_scores the probabilities also go back to the row.
+template <int NPL>
+__global__ __launch_bounds__(64 * kRowWaves) void gate_softmax_mask_kernel(
+    int rows, int nqb, float* __restrict__ logits, int write_scores,
+    const float2* __restrict__ part, int mode, float tau, double density, int keep_sink,
+    int32_t* __restrict__ idx, int32_t* __restrict__ cnt, int max_k) {
+  __shared__ int hist_all[kRowWaves][256];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int row = blockIdx.x * kRowWaves + wv;
+  if (row >= rows) return;
+  const int i = row % nqb;
+  const int n = i + 1;
+  const int ntiles = (nqb + kTile - 1) / kTile;
+  const int it = i / kTile;
+  const float2* pr = part + (size_t)row * ntiles;
+  float* sr = logits + (size_t)row * nqb;
+  float2 mine = lane <= it ? pr[lane] : make_float2(-INFINITY, 0.f);
+  float x[NPL];
+#pragma unroll
+  for (int c = 0; c < NPL; ++c) x[c] = sr[min(64 * c + lane, i)];  // entries j > i unread
+  float m, l;
+  combine_row_partials(pr, it, lane, mine, m, l);
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int c = 0; c < NPL; ++c) {
+    const int j = 64 * c + lane;
+    x[c] = (j <= i) ? expf(x[c] - m) * inv : 0.f;
+    if (write_scores && j < nqb) sr[j] = x[c];
+  }
+  uint32_t key[NPL];
+  int npos = 0;
+#pragma unroll
+  for (int c = 0; c < NPL; ++c) {
+    const int j = 64 * c + lane;
+    uint32_t kj = 0u;
+    if (j < n) {
+      if (j == i || (keep_sink && j == 0))
+        kj = 0xFFFFFFFFu;
+      else
+        kj = (mode == 1 || x[c] >= tau) ? rowsel::order_key(x[c]) : 0u;
+    }
+    key[c] = kj;
+    npos += kj != 0u;
+  }
+  npos = rowsel::wave_sum(npos);
+  int k;
+  if (mode == 1) {
+    const int forced = (i == 0) ? 1 : (keep_sink ? 2 : 1);
+    k = min(i + 1, max(forced, (int)ceil(density * (double)(i + 1))));
+  } else {
+    k = min(npos, max_k);
+  }
+  const int count = rowsel::wave_select_row<NPL>(key, n, k, npos, lane, hist_all[wv],
+                                                 idx + (size_t)row * max_k, max_k);
+  if (lane == 0) cnt[row] = count;
 }
 
 }  // namespace
@@ -437,11 +508,15 @@ size_t attn_gate_workspace_floats(int B, int Hq, int Hkv, int nqb, int dg) {
          ((size_t)B * Hq + 2 * (size_t)B * Hkv) * nqb * 128;
 }
 
-hipError_t launch_attn_gate(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
-                            const float* wq, const float* wk, int dg, float scale,
-                            float rope_base, float* scores, float* ws, hipStream_t stream) {
+namespace {
+
+// Pooling, linear layers + block RoPE, and the causal logit tiles with their
+// per-row (max, sum) pairs.  The scaled logits go to `logits` [B,Hq,nQB,nQB]
+// (causal tiles only); *part_out points at the pairs in the workspace.
+hipError_t gate_front(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
+                      const float* wq, const float* wk, int dg, float scale, float rope_base,
+                      float* logits, float* ws, float2** part_out, hipStream_t stream) {
   const int nqb = (T + kTile - 1) / kTile;
-  if ((size_t)B * Hq * nqb == 0) return hipSuccess;
   float* qt = ws;
   float* kt = ws + (size_t)B * Hq * nqb * dg;
   const size_t nt = (nqb + kTile - 1) / kTile;
@@ -474,16 +549,63 @@ hipError_t launch_attn_gate(const void* q, const void* k, int B, int Hq, int Hkv
   const dim3 lgrid((unsigned)((size_t)B * Hq * npairs));
 #define SEER_GATE_LOGITS(DG)                                                                   \
   hipLaunchKernelGGL(gate_logits_kernel<DG>, lgrid, dim3(kScoreThreads), 0, stream, qt, kt,    \
-                     Hq, Hkv, nqb, scale, scores, part)
+                     Hq, Hkv, nqb, scale, logits, part)
   if (dg == 128) SEER_GATE_LOGITS(128);
   else if (dg == 64) SEER_GATE_LOGITS(64);
   else SEER_GATE_LOGITS(32);
 #undef SEER_GATE_LOGITS
-  err = hipGetLastError();
+  *part_out = part;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_gate(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
+                            const float* wq, const float* wk, int dg, float scale,
+                            float rope_base, float* scores, float* ws, hipStream_t stream) {
+  const int nqb = (T + kTile - 1) / kTile;
+  if ((size_t)B * Hq * nqb == 0) return hipSuccess;
+  float2* part = nullptr;
+  const hipError_t err = gate_front(q, k, B, Hq, Hkv, T, D, wq, wk, dg, scale, rope_base, scores,
+                                    ws, &part, stream);
   if (err != hipSuccess) return err;
   const int rows = B * Hq * nqb;  // < 2^31: the host layer checks B (Hq + Hkv) nQB
   hipLaunchKernelGGL(gate_softmax_kernel, dim3((unsigned)((rows + kRowWaves - 1) / kRowWaves)),
                      dim3(64 * kRowWaves), 0, stream, rows, nqb, scores, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_gate_mask(const void* q, const void* k, int B, int Hq, int Hkv, int T,
+                                 int D, const float* wq, const float* wk, int dg, float scale,
+                                 float rope_base, int mode, float threshold, double density,
+                                 int keep_sink, int32_t* idx, int32_t* cnt, int max_k,
+                                 float* scores, float* ws, hipStream_t stream) {
+  const int nqb = (T + kTile - 1) / kTile;
+  if ((size_t)B * Hq * nqb == 0) return hipSuccess;
+  // Without a scores buffer the logits live past the gate's own workspace, at
+  // the next 256-byte boundary (within the 256 bytes of slack the workspace
+  // size adds).
+  const size_t off = (attn_gate_workspace_floats(B, Hq, Hkv, nqb, dg) + 63) & ~(size_t)63;
+  float* logits = scores ? scores : ws + off;
+  float2* part = nullptr;
+  hipError_t err = gate_front(q, k, B, Hq, Hkv, T, D, wq, wk, dg, scale, rope_base, logits, ws,
+                              &part, stream);
+  if (err != hipSuccess) return err;
+  const int rows = B * Hq * nqb;
+  const dim3 grid((unsigned)((rows + kRowWaves - 1) / kRowWaves));
+  const int ws_flag = scores ? 1 : 0;
+#define SEER_GATE_MASK(NPL)                                                                    \
+  hipLaunchKernelGGL(gate_softmax_mask_kernel<NPL>, grid, dim3(64 * kRowWaves), 0, stream, rows, \
+                     nqb, logits, ws_flag, part, mode, threshold, density, keep_sink, idx, cnt,  \
+                     max_k)
+  if (nqb <= 64) SEER_GATE_MASK(1);
+  else if (nqb <= 64 * 4) SEER_GATE_MASK(4);
+  else if (nqb <= 64 * 8) SEER_GATE_MASK(8);
+  else if (nqb <= 64 * 16) SEER_GATE_MASK(16);
+  else if (nqb <= 64 * 32) SEER_GATE_MASK(32);
+  else if (nqb <= 64 * 64) SEER_GATE_MASK(64);
+  else return hipErrorInvalidValue;  // the host layer rejects nQB > 4096 first
+#undef SEER_GATE_MASK
   return hipGetLastError();
 }
 

@@ -25,41 +25,16 @@
 // j = 64 * c + lane in slot c, so the score row is read from HBM once and the
 // compaction is a ballot + popcount per 64 candidates.  The digit histograms
 // live in a per-wave 1 KB slice of LDS.
-#include "seer_internal.h"
+#include "mask_select.h"
 
 namespace seer {
 namespace {
 
+using rowsel::order_key;
+using rowsel::wave_select_row;
+using rowsel::wave_sum;
+
 constexpr int kWavesPerGroup = 4;
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (f != f) u = 0xFF800000u;   // NaN ranks as -inf
-  if (u == 0x80000000u) u = 0u;  // -0 ties with +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-// Inclusive prefix sum over the wave (lane order).
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(v, off, 64);
-    if (lane >= off) v += y;
-  }
-  return v;
-}
-
-// Number of set bits of `mask` below this lane.
-__device__ __forceinline__ int popc_below(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
 
 // NPL = key slots per lane (row length <= 64 * NPL).
 template <int NPL>
@@ -112,83 +87,8 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
     k = min(npos, max_k);
   }
 
-  // Keys > t are kept, plus the first `need` keys equal to t in index order.
-  uint32_t t = 0u;
-  int need = 0;
-  if (k < npos) {
-    uint32_t prefix = 0u, mask = 0u;
-    int remaining = k;
-    bool exact = true;  // false: the select stopped at a fully needed bin
-    for (int shift = 24; shift >= 0; shift -= 8) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) hist[lane + 64 * b] = 0;
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int c = 0; c < NPL; ++c)
-        if ((key[c] & mask) == prefix && key[c] != 0u)
-          atomicAdd(&hist[(key[c] >> shift) & 255u], 1);
-      __builtin_amdgcn_wave_barrier();
-      // Lane l owns bins 255-4l .. 252-4l (descending); running count from the top.
-      int hc[4], local = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        hc[b] = hist[255 - 4 * lane - b];
-        local += hc[b];
-      }
-      const int incl = wave_incl_scan(local, lane);
-      int above = incl - local;
-      int sel_bin = -1, sel_above = 0, sel_cnt = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (sel_bin < 0 && above < remaining && remaining <= above + hc[b]) {
-          sel_bin = 255 - 4 * lane - b;
-          sel_above = above;
-          sel_cnt = hc[b];
-        }
-        above += hc[b];
-      }
-      const uint64_t who = __ballot(sel_bin >= 0);
-      const int src = __builtin_ctzll(who);
-      sel_bin = __shfl(sel_bin, src, 64);
-      sel_above = __shfl(sel_above, src, 64);
-      sel_cnt = __shfl(sel_cnt, src, 64);
-      prefix |= (uint32_t)sel_bin << shift;
-      mask |= 0xFFu << shift;
-      remaining -= sel_above;
-      __builtin_amdgcn_wave_barrier();
-      if (remaining == sel_cnt) {
-        // Every key of the boundary bin is needed: keep exactly the keys whose
-        // digits so far are >= the prefix (lower digits zero), no tie rank.
-        exact = false;
-        break;
-      }
-    }
-    if (exact) {
-      t = prefix;
-      need = remaining;
-    } else {
-      t = prefix > 0u ? prefix - 1u : 0u;
-      need = 0;
-    }
-  }
-
-  int base = 0, ties = 0;
-#pragma unroll
-  for (int c = 0; c < NPL; ++c) {
-    if (64 * c >= n) break;
-    const int j = 64 * c + lane;
-    const bool valid = j < n;
-    const bool eq = valid && key[c] == t;
-    const uint64_t eqm = __ballot(eq);
-    const int eq_rank = ties + popc_below(eqm);
-    ties += __popcll(eqm);
-    const bool keep = valid && (key[c] > t || (eq && eq_rank < need));
-    const uint64_t km = __ballot(keep);
-    if (keep) out[base + popc_below(km)] = j;
-    base += __popcll(km);
-  }
-  for (int p = base + lane; p < max_k; p += 64) out[p] = -1;
-  if (lane == 0) cnt[row] = base;
+  const int count = wave_select_row<NPL>(key, n, k, npos, lane, hist, out, max_k);
+  if (lane == 0) cnt[row] = count;
 }
 
 }  // namespace

@@ -51,6 +51,16 @@ hipError_t launch_attn_gate(const void* q, const void* k, int B, int Hq, int Hkv
                             const float* wq, const float* wk, int dg, float scale,
                             float rope_base, float* scores, float* ws, hipStream_t stream);
 
+// Gate scores and block lists in one pass over the logits (nqb <= 4096, checked
+// by the caller).  scores may be null: the logits then live in ws from the
+// first 64-float boundary past attn_gate_workspace_floats(), B*Hq*nqb*nqb
+// more floats.
+hipError_t launch_attn_gate_mask(const void* q, const void* k, int B, int Hq, int Hkv, int T,
+                                 int D, const float* wq, const float* wk, int dg, float scale,
+                                 float rope_base, int mode, float threshold, double density,
+                                 int keep_sink, int32_t* idx, int32_t* cnt, int max_k,
+                                 float* scores, float* ws, hipStream_t stream);
+
 // Decode: workspace bytes and grid size of launch_sparse_decode (list_heads is
 // Hq or Hkv; the caller checks the arguments).
 size_t sparse_decode_workspace_bytes(int B, int Hq, int Hkv, int Tmax, int D, int list_heads,

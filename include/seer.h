@@ -212,6 +212,40 @@ int seer_attn_gate_scores(const void* q, const void* k, int B, int Hq, int Hkv, 
                           const float* wq, const float* wk, int Dg, float scale, float rope_base,
                           float* scores, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace seer_attn_gate_mask needs: that of
+ * seer_attn_gate_scores, plus B * Hq * nQB * nQB fp32 for the logits when no
+ * scores buffer is given (with_scores == 0).  0 for invalid sizes. */
+size_t seer_attn_gate_mask_workspace_size(int B, int Hq, int Hkv, int T, int Dg,
+                                          int with_scores);
+
+/*
+ * AttnGate scores and the block mask in one call: the gate's scores, as
+ * seer_attn_gate_scores defines them, go straight into the per-row threshold
+ * or TopK of seer_build_mask (the gate's soft scores are what the mask is
+ * built from: model card "SeerAttention-Llama-3.1-8B-AttnGates", method
+ * summary).  The lists are those seer_build_mask(scores, B, Hq, nQB, nQB,
+ * mode, threshold, density, keep_sink, ...) returns for the scores
+ * seer_attn_gate_scores returns, bit for bit; the last kernel normalises each
+ * score row in registers and selects from it there, so the score map is
+ * neither written twice nor read back (and not written at all when scores is
+ * NULL).
+ *
+ * q, k, wq, wk, Dg, scale, rope_base: as seer_attn_gate_scores.
+ * mode, threshold, density, keep_sink, kv_idx, kv_cnt, max_k: as
+ *          seer_build_mask with nQB = nKB = ceil(T / 64); nQB <=
+ *          SEER_MAX_QUERY_BLOCKS (else SEER_ERR_UNSUPPORTED); the same
+ *          capacity rules (SEER_ERR_CAPACITY).
+ * scores   device fp32 out [B, Hq, nQB, nQB] (the scores, as
+ *          seer_attn_gate_scores writes them), or NULL.
+ * workspace device, >= seer_attn_gate_mask_workspace_size(B, Hq, Hkv, T, Dg,
+ *          scores != NULL) bytes, 256-byte aligned; overwritten.
+ */
+int seer_attn_gate_mask(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
+                        const float* wq, const float* wk, int Dg, float scale, float rope_base,
+                        int mode, float threshold, double density, int keep_sink,
+                        int32_t* kv_idx, int32_t* kv_cnt, int max_k, float* scores,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Row-normalised distillation target and its MSE against gate scores.  The
  * max-pooled map is normalised per row so that, like the gate's softmax

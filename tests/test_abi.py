@@ -59,6 +59,12 @@ def test_workspace_sizes():
     floats = (32 + 8) * nqb * 128 + 2 * 32 * nqb * nt + (32 + 2 * 8) * nqb * 128
     assert seer.attn_gate_workspace_size(1, 32, 8, 32768, 128) >= floats * 4
     assert seer.attn_gate_workspace_size(1, 32, 7, 32768, 128) == 0  # Hq % Hkv != 0
+    # fused gate + mask: the same, plus the logits map when no scores buffer is given
+    with_s = seer.attn_gate_mask_workspace_size(1, 32, 8, 32768, 128, True)
+    without = seer.attn_gate_mask_workspace_size(1, 32, 8, 32768, 128, False)
+    assert with_s == seer.attn_gate_workspace_size(1, 32, 8, 32768, 128)
+    assert without == with_s + 32 * 512 * 512 * 4
+    assert seer.attn_gate_mask_workspace_size(1, 32, 7, 32768, 128, True) == 0
 
 
 FAKE = 1 << 20  # never dereferenced: every call below fails its host checks first
@@ -163,6 +169,35 @@ def test_attn_gate_rejects_on_host():
     assert call(p2=0) == 0             # empty
     assert seer.load().seer_attn_gate_workspace_size(1, 4, 2, 256, 64) >= (4 + 2) * 4 * 64 * 4
 
+
+
+def test_attn_gate_mask_rejects_on_host():
+    lib = seer.load()
+    # q, k, B, Hq, Hkv, T, D, wq, wk, Dg, scale, rope_base, mode, threshold, density,
+    # keep_sink, kv_idx, kv_cnt, max_k, scores, workspace, workspace_bytes, stream.
+    # The base call fails only on its 16-byte workspace, so nothing ever launches.
+    a = [FAKE, FAKE, 1, 4, 2, 256, 128, FAKE, FAKE, 64, 0.125, 10000.0, 1, 0.0, 0.5, 1, FAKE,
+         FAKE, 3, FAKE, FAKE, 16, None]
+    def call(**kw):
+        b = list(a)
+        for i, v in kw.items():
+            b[int(i[1:])] = v
+        return lib.seer_attn_gate_mask(*b)
+    assert call() == 4                 # workspace too small
+    assert call(p6=96) == 2            # head dim
+    assert call(p9=48) == 2            # gate dim
+    assert call(p4=3) == 1             # Hq % Hkv
+    assert call(p10=0.0) == 1          # scale
+    assert call(p12=5) == 1            # mode
+    assert call(p14=0.0) == 1          # density
+    assert call(p12=0, p13=float("inf")) == 1  # threshold
+    assert call(p18=0) == 3            # max_k < 1
+    assert call(p18=1) == 3            # under the TopK budget (2 of 4 blocks)
+    assert call(p12=0, p15=1, p18=1) == 3  # threshold with sink needs 2 slots
+    assert call(p5=64 * 4097) == 2     # more than SEER_MAX_QUERY_BLOCKS blocks
+    assert call(p16=None) == 1         # lists
+    assert call(p7=None) == 1          # weights
+    assert call(p2=0) == 0             # empty
 
 
 def test_build_mask_decode_rejects_on_host():

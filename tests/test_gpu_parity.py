@@ -661,6 +661,32 @@ def test_attn_gate_to_topk_lists():
     assert exact > 0.9 * (exact + ambiguous)
 
 
+@pytest.mark.parametrize("case", ["tiny", "ragged", "d64", "far128k", "llama8k"])
+@pytest.mark.parametrize("mode", [wl.MODE_TOPK, wl.MODE_THRESHOLD])
+def test_attn_gate_mask_equals_scores_then_mask(case, mode):
+    """The fused call returns, bit for bit, the scores of seer_attn_gate_scores and
+    the lists seer_build_mask makes from them, with and without a scores buffer."""
+    w, dg = _gate_case(case)
+    announce(f"attn gate mask {w.name} dg={dg} mode={mode}")
+    q, k, _ = (_dev(t) for t in wl.make_qkv(w))
+    wq, wk = (_dev(t) for t in wl.make_gate_weights(w, dg, gain=2.0))
+    density, thr = 0.2, 0.02
+    max_k = seer.topk_budget(w.nqb, density, True) if mode == wl.MODE_TOPK else w.nqb // 2 + 2
+    s = seer.seer_attn_gate_scores(q, k, wq, wk)
+    ri, rc = seer.seer_build_mask(s, mode, thr, density, True, max_k)
+    gi, gc, gs = seer.seer_attn_gate_mask(q, k, wq, wk, mode, thr, density, True, max_k,
+                                          return_scores=True)
+    ni, nc, ns = seer.seer_attn_gate_mask(q, k, wq, wk, mode, thr, density, True, max_k)
+    torch.cuda.synchronize()
+    assert ns is None
+    assert torch.equal(gs, s)
+    assert torch.equal(gc, rc) and torch.equal(gi, ri)
+    assert torch.equal(nc, rc) and torch.equal(ni, ri)
+    if mode == wl.MODE_THRESHOLD:
+        announce(f"threshold lists: mean length {float(rc.float().mean()):.2f}, "
+                 f"rows at max_k {int((rc == max_k).sum())}")
+
+
 def test_attn_gate_repeat_bitexact():
     w, dg = _gate_case("ragged")
     q, k, _ = (_dev(t) for t in wl.make_qkv(w))
