@@ -88,6 +88,43 @@ def time_calls(fn, n: int, torch, flush=None):
     return statistics.mean(a.elapsed_time(b) for a, b in evs)
 
 
+def call_stats(fn, n: int, torch, flush=None) -> dict:
+    """Median, min and max duration (ms) of fn() over n calls, timed as in
+    time_calls."""
+    evs = []
+    for _ in range(n):
+        if flush is not None:
+            flush.sum()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in evs]
+    return {"median": round(statistics.median(ts), 4), "min": round(min(ts), 4),
+            "max": round(max(ts), 4), "calls": n}
+
+
+def device_info(torch) -> dict:
+    """Compute units and the clock the runtime reports for device 0."""
+    import ctypes
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate: peak shader clock in kHz
+        attr = 5
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, 0) == 0 and v.value > 0:
+            info["peak_clock_mhz"] = round(v.value / 1000)
+    except OSError:
+        pass
+    return info
+
+
 def cpu_baseline(w, q, k, v, scores, max_k, blocks_per_head: int):
     import numpy as np
 
@@ -303,6 +340,11 @@ def main(argv=None) -> int:
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "mask_build_ms": round(mask_ms, 4),
         "sparse_prefill_ms": round(pre_ms, 4),
+        "sparse_prefill_call_ms": {
+            "median": round(statistics.median(a.elapsed_time(b) for a, b in ev_pre), 4),
+            "min": round(min(a.elapsed_time(b) for a, b in ev_pre), 4),
+            "max": round(max(a.elapsed_time(b) for a, b in ev_pre), 4)},
+        "device": device_info(torch),
         "causal_exact_tflops": round(causal_exact / (ms_per_step * 1e-3) / 1e12, 3),
         "roofline": {
             "kernel": "seer_sparse_prefill (schedule + sparse_prefill_kernel)",
@@ -317,6 +359,14 @@ def main(argv=None) -> int:
     }
 
     if not args.no_extras:
+        # The prefill call with L2 and the 256 MB MALL flushed before each call (a
+        # 1 GiB read), so that K/V start in HBM: median, min and max.
+        log("[bench] flushed prefill calls")
+        flush = torch.ones((1 << 28,), dtype=torch.float32, device=dev)
+        result["sparse_prefill_flushed_ms"] = call_stats(prefill, max(20, args.steps), torch,
+                                                         flush)
+        del flush
+
         # Same kernel at density 1.0 (every causal block listed).
         log("[bench] density 1.0 reference")
         idx1 = torch.empty((w.batch, w.hq, w.nqb, w.nqb), dtype=torch.int32, device=dev)
