@@ -21,7 +21,8 @@ What it computes, each function citing the passage it follows:
 * ``gate``    -- the AttnGate's soft block scores: pooled Q and K, linear layers,
                  block RoPE and a causal softmax (rebuttal "SeerAttention:
                  Learning Intrinsic Sparse Attention in Your LLMs", Weakness 3
-                 and the pooling and RoPE answers).
+                 and the pooling and RoPE answers); and the per-token gate of
+                 decoding, without query pooling (abstract of "SeerAttention-R").
 * ``decode``  -- block-sparse attention of one new token over a KV cache and its
                  block selection with a token budget (abstract of "SeerAttention-R:
                  Sparse Attention Adaptation for Long Reasoning").
@@ -42,7 +43,8 @@ from .attention import (BLOCK, block_probs, allowed_blocks, sparse_attention_ref
                         sparse_attention_blocks_ref)
 from .pooled import pooled_map_ref, pooled_map_blocks_ref
 from .target import pooled_target_ref
-from .gate import pool_qk, block_rope, gate_qk_ref, gate_scores_ref
+from .gate import (pool_qk, block_rope, gate_qk_ref, gate_scores_ref, rope_at,
+                   decode_gate_scores_ref)
 from .decode import decode_blocks, select_decode_row, build_mask_decode_ref, sparse_decode_ref
 
 __all__ = [
@@ -50,6 +52,6 @@ __all__ = [
     "build_mask_ref", "mask_rows_ref", "block_probs", "allowed_blocks",
     "sparse_attention_ref", "sparse_attention_blocks_ref", "pooled_map_ref",
     "pooled_map_blocks_ref", "pooled_target_ref", "pool_qk", "block_rope", "gate_qk_ref",
-    "gate_scores_ref", "decode_blocks", "select_decode_row", "build_mask_decode_ref",
+    "gate_scores_ref", "rope_at", "decode_gate_scores_ref", "decode_blocks", "select_decode_row", "build_mask_decode_ref",
     "sparse_decode_ref",
 ]

@@ -27,6 +27,16 @@ Readings where the pages are silent (also in the design notes):
   base^(-2t/Dg), t = 0 .. Dg/2 - 1, at the block index (i for Q~_i, j for K~_j).
 * Scores: s_ij = scale <rope(Q~_i, i), rope(K~_j, j)> for j <= i, softmax over
   j <= i; entries j > i are 0.  scale defaults to 1/sqrt(Dg), base to 10000.
+
+Decode (abstract of "SeerAttention-R: Sparse Attention Adaptation for Long
+Reasoning": the gate drops query pooling for decoding and keeps 64- or 128-token
+blocks).  Readings where that page is silent: the K side is the prefill gate's
+(block max | min pooling of the cached K, a short last block pooling the tokens
+it has, the same linear layer and block RoPE at the block index); the new token's
+q goes through the same Q linear layer with no pooling and is rotated at its own
+block index nb - 1 (nb = ceil(kv_len / block)), which is where the prefill gate
+rotates the query block holding that token; the softmax runs over the blocks
+j < nb.  Scores are per query head.
 """
 
 from __future__ import annotations
@@ -91,3 +101,47 @@ def gate_scores_ref(q, k, wq, wk, scale: Optional[float] = None, base: float = 1
     s = s - s.max(axis=-1, keepdims=True)
     e = np.where(causal, np.exp(s), 0.0)
     return e / e.sum(axis=-1, keepdims=True)
+
+
+def rope_at(x: np.ndarray, pos, base: float = 10000.0) -> np.ndarray:
+    """Rotate-half RoPE of x [..., Dg] at position(s) pos (broadcast over the leading dims)."""
+    dg = x.shape[-1]
+    half = dg // 2
+    inv = base ** (-2.0 * np.arange(half) / dg)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def decode_gate_scores_ref(q, k_cache, kv_len, wq, wk, block: int = BLOCK,
+                           scale: Optional[float] = None, base: float = 10000.0) -> np.ndarray:
+    """Per-token gate scores [B,Hq,nKB] float64 (nKB = ceil(Tmax / block)) for the new
+    token of each sequence: q [B,Hq,D] (no pooling), the cache K [B,Hkv,Tmax,D] of which
+    the first kv_len[b] tokens exist.  Row (b, h) sums to 1 over j < nb and is 0 beyond
+    (all 0 when kv_len[b] = 0)."""
+    q = _f64(q)
+    kc = _f64(k_cache)
+    kv_len = np.asarray(kv_len)
+    wq = np.asarray(wq, dtype=np.float64)
+    wk = np.asarray(wk, dtype=np.float64)
+    bsz, hq, _ = q.shape
+    hkv, tmax = kc.shape[1], kc.shape[2]
+    grp = hq // hkv
+    nkb = (tmax + block - 1) // block
+    dg = wq.shape[-1]
+    sc = 1.0 / math.sqrt(dg) if scale is None else float(scale)
+    out = np.zeros((bsz, hq, nkb))
+    for b in range(bsz):
+        n = int(kv_len[b])
+        nb = (n + block - 1) // block
+        if nb == 0:
+            continue
+        _, kp = pool_qk(kc[b:b + 1, :, :n], kc[b:b + 1, :, :n], block)  # K pooling only
+        kt = block_rope(np.einsum("gnd,gde->gne", kp[0], wk), base)      # [Hkv, nb, Dg]
+        for h in range(hq):
+            qt = rope_at(q[b, h] @ wq[h], nb - 1, base)
+            s = sc * (kt[h // grp] @ qt)
+            e = np.exp(s - s.max())
+            out[b, h, :nb] = e / e.sum()
+    return out

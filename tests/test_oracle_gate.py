@@ -118,3 +118,70 @@ def test_rope_rotate_half_pairing_dg4():
                2.0 * math.cos(a0) + 0.5 * math.sin(a0),
                0.25 * math.cos(a1) - 1.0 * math.sin(a1)]
         np.testing.assert_allclose(r[p], exp, rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------------------------ decode gate
+
+def _gate_weights(seed, hq, hkv, d, dg):
+    g = torch.Generator().manual_seed(seed)
+    wq = torch.randn(hq, d, dg, generator=g, dtype=torch.float64) / math.sqrt(d)
+    wk = torch.randn(hkv, 2 * d, dg, generator=g, dtype=torch.float64) / math.sqrt(2 * d)
+    return wq.numpy(), wk.numpy()
+
+
+import pytest  # noqa: E402
+
+
+@pytest.mark.parametrize("block", [64, 128])
+@pytest.mark.parametrize("t", [640, 700, 1])
+def test_decode_gate_equals_last_prefill_row(block, t):
+    """With every row of the last block equal to the new token's q, average pooling
+    returns q itself, so the decode gate is the prefill gate's last row."""
+    b, hq, hkv, d, dg = 2, 4, 2, 32, 16
+    q_full, k_full = _qk(31 + t, b, hq, hkv, t, d)
+    nb = (t + block - 1) // block
+    qtok = q_full[:, :, t - 1]
+    q_full[:, :, block * (nb - 1): t] = qtok[:, :, None, :]
+    wq, wk = _gate_weights(32, hq, hkv, d, dg)
+    tmax = t + 300  # cache slots past kv_len hold NaN: never read
+    kc = torch.full((b, hkv, tmax, d), float("nan"), dtype=torch.bfloat16)
+    kc[:, :, :t] = k_full
+    got = oracle.decode_gate_scores_ref(qtok, kc, [t, t], wq, wk, block)
+    want = oracle.gate_scores_ref(q_full, k_full, wq, wk, block=block)[:, :, nb - 1, :nb]
+    np.testing.assert_allclose(got[:, :, :nb], want, rtol=0, atol=1e-12)
+    assert (got[:, :, nb:] == 0).all()
+    np.testing.assert_allclose(got.sum(axis=-1), 1.0, rtol=0, atol=1e-12)
+
+
+def test_decode_gate_edges():
+    b, hq, hkv, d, dg, tmax = 3, 2, 1, 16, 8, 500
+    g = torch.Generator().manual_seed(40)
+    q = torch.randn(b, hq, d, generator=g).to(torch.bfloat16)
+    kc = torch.randn(b, hkv, tmax, d, generator=g).to(torch.bfloat16)
+    wq, wk = _gate_weights(41, hq, hkv, d, dg)
+    s = oracle.decode_gate_scores_ref(q, kc, [0, 65, 500], wq, wk, 64)
+    assert s.shape == (3, 2, 8)
+    assert (s[0] == 0).all()                       # an empty sequence has no blocks
+    assert (s[1, :, 2:] == 0).all() and np.allclose(s[1].sum(-1), 1, atol=1e-12)
+    # zero query weights: every block of the sequence gets 1 / nb
+    z = oracle.decode_gate_scores_ref(q, kc, [0, 65, 500], np.zeros_like(wq), wk, 64)
+    np.testing.assert_allclose(z[2], np.full((2, 8), 1 / 8), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(z[1, :, :2], 0.5, rtol=0, atol=1e-15)
+    # the ragged last block pools only the token it has: its K~ row is that token's
+    kp_last = np.concatenate([kc[1, 0, 64].double().numpy()] * 2)
+    kt_last = oracle.rope_at(kp_last @ wk[0], 1)
+    qt = oracle.rope_at(q[1, 0].double().numpy() @ wq[0], 1)
+    kp0 = np.concatenate([kc[1, 0, :64].double().numpy().max(0),
+                          kc[1, 0, :64].double().numpy().min(0)])
+    kt0 = oracle.rope_at(kp0 @ wk[0], 0)
+    sc = 1 / math.sqrt(dg)
+    l0, l1 = sc * kt0 @ qt, sc * kt_last @ qt
+    want = np.exp([l0, l1]) / np.exp([l0, l1]).sum()
+    np.testing.assert_allclose(s[1, 0, :2], want, rtol=0, atol=1e-12)
+
+
+def test_rope_at_is_block_rope_row():
+    x = np.random.default_rng(5).standard_normal((3, 7, 12))
+    full = oracle.block_rope(x)
+    for i in range(7):
+        np.testing.assert_allclose(oracle.rope_at(x[:, i], i), full[:, i], rtol=0, atol=1e-15)
