@@ -171,6 +171,25 @@ def decode_bench(seer, wl, torch, dev, args):
            "budget_tokens": dw.budget_tokens, "hbm_peak_gbps": 8000.0}
     d, g = dw.head_dim, dw.hq // dw.hkv
     flush = torch.ones((1 << 28,), dtype=torch.float32, device=dev)  # 1 GiB > L2 + 256 MB MALL
+    # The per-token gate over the same cache (Dg 128, seeded weights): gate keys of every
+    # block once, then per step the keys of each sequence's last block and the new
+    # tokens' block scores (the input of the decode mask build).
+    wq, wk = (t.to(dev) for t in wl.make_gate_weights(wl.WORKLOADS[3], 128))  # 32/8/128 weights
+    gsc = torch.empty((dw.batch, dw.hq, dw.nkb), dtype=torch.float32, device=dev)
+    gws = torch.empty((seer.attn_gate_decode_keys_workspace_size(dw.batch, dw.hkv, dw.tmax, d,
+                                                                 dw.block),),
+                      dtype=torch.uint8, device=dev)
+    kg = seer.seer_attn_gate_decode_keys(kd, ld, wk, dw.block, workspace=gws)
+    kall = lambda: seer.seer_attn_gate_decode_keys(kd, ld, wk, dw.block, k_gate=kg, workspace=gws)
+    kstep = lambda: (seer.seer_attn_gate_decode_keys(kd, ld, wk, dw.block, last_block_only=True,
+                                                     k_gate=kg),
+                     seer.seer_attn_gate_decode_scores(qd, kg, ld, wq, dw.tmax, dw.block,
+                                                       scores=gsc))
+    kstep()
+    out["gate_keys_all_blocks_ms"] = round(time_calls(kall, max(3, args.steps // 2), torch,
+                                                      flush), 4)
+    out["gate_step_ms"] = round(time_calls(kstep, max(5, args.steps), torch, flush), 4)
+    del wq, wk, gsc, gws, kg
     for var in (dw, wl.DEC2):
         sc = wl.make_decode_scores(var).to(dev)
         max_k = min(var.nkb, max(var.k_blocks, 2))

@@ -26,7 +26,8 @@ EXPORTED = (
     "seer_sparse_prefill_workspace_size", "seer_sparse_prefill", "seer_sparse_prefill_block",
     "seer_pooled_attn_map_workspace_size", "seer_pooled_attn_map", "seer_pooled_target_mse",
     "seer_attn_gate_workspace_size", "seer_attn_gate_scores", "seer_attn_gate_mask_workspace_size",
-    "seer_attn_gate_mask", "seer_build_mask_decode",
+    "seer_attn_gate_mask", "seer_attn_gate_decode_keys_workspace_size", "seer_attn_gate_decode_keys",
+    "seer_attn_gate_decode_scores", "seer_build_mask_decode",
     "seer_sparse_decode_workspace_size", "seer_sparse_decode",
 )
 
@@ -91,6 +92,16 @@ def load() -> ctypes.CDLL:
     lib.seer_pooled_target_mse.restype = c_int
     lib.seer_pooled_target_mse.argtypes = [c_void, c_void, c_int, c_int, c_int, c_void, c_void,
                                            c_void, c_void]
+    lib.seer_attn_gate_decode_keys_workspace_size.restype = c_size
+    lib.seer_attn_gate_decode_keys_workspace_size.argtypes = [c_int] * 5
+    lib.seer_attn_gate_decode_keys.restype = c_int
+    lib.seer_attn_gate_decode_keys.argtypes = [c_void, c_void, c_int, c_int, c_int, c_int,
+                                               c_void, c_int, c_float, c_int, c_int, c_void,
+                                               c_void, c_size, c_void]
+    lib.seer_attn_gate_decode_scores.restype = c_int
+    lib.seer_attn_gate_decode_scores.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int,
+                                                 c_int, c_int, c_void, c_int, c_float, c_float,
+                                                 c_int, c_void, c_void]
     lib.seer_build_mask_decode.restype = c_int
     lib.seer_build_mask_decode.argtypes = [c_void, c_void, c_int, c_int, c_int, c_int, c_int,
                                            c_float, c_int, c_int, c_void, c_void, c_int, c_void]
@@ -348,6 +359,74 @@ def seer_attn_gate_mask(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor, wk: 
         _ptr(kv_cnt), int(max_k), _ptr(scores), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return kv_idx, kv_cnt, scores
+
+
+def attn_gate_decode_keys_workspace_size(b: int, hkv: int, tmax: int, d: int,
+                                         block: int) -> int:
+    return load().seer_attn_gate_decode_keys_workspace_size(b, hkv, tmax, d, block)
+
+
+def seer_attn_gate_decode_keys(k_cache: torch.Tensor, kv_len: torch.Tensor, wk: torch.Tensor,
+                               block: int = BLOCK, rope_base: float = 10000.0,
+                               last_block_only: bool = False,
+                               k_gate: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None,
+                               stream=None) -> torch.Tensor:
+    """Gate keys K~ [B,Hkv,nKB,Dg] fp32 of k_cache [B,Hkv,Tmax,D] (bf16, before RoPE) for
+    the blocks below kv_len int32 [B]; with last_block_only only each sequence's last
+    block is (re)computed in the given k_gate."""
+    lib = load()
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B,Hkv,Tmax,D]")
+    b, hkv, tmax, d = k_cache.shape
+    dg = wk.shape[-1]
+    nkb = (tmax + block - 1) // block
+    _need(k_cache, "k_cache", torch.bfloat16, (b, hkv, tmax, d))
+    _need(kv_len, "kv_len", torch.int32, (b,))
+    _need(wk, "wk", torch.float32, (hkv, 2 * d, dg))
+    if k_gate is None:
+        if last_block_only:
+            raise ValueError("last_block_only updates an existing k_gate")
+        k_gate = torch.empty((b, hkv, nkb, dg), dtype=torch.float32, device=k_cache.device)
+    _need(k_gate, "k_gate", torch.float32, (b, hkv, nkb, dg))
+    if workspace is None and not last_block_only:
+        workspace = _workspace(lib.seer_attn_gate_decode_keys_workspace_size(
+            b, hkv, tmax, d, int(block)), k_cache.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("seer_attn_gate_decode_keys", lib.seer_attn_gate_decode_keys(
+        _ptr(k_cache), _ptr(kv_len), b, hkv, tmax, d, _ptr(wk), int(dg), float(rope_base),
+        int(block), int(bool(last_block_only)), _ptr(k_gate), _ptr(workspace), nbytes,
+        _stream(stream)))
+    return k_gate
+
+
+def seer_attn_gate_decode_scores(q: torch.Tensor, k_gate: torch.Tensor, kv_len: torch.Tensor,
+                                 wq: torch.Tensor, tmax: int, block: int = BLOCK,
+                                 scale: Optional[float] = None, rope_base: float = 10000.0,
+                                 scores: Optional[torch.Tensor] = None,
+                                 stream=None) -> torch.Tensor:
+    """Per-token gate scores [B,Hq,nKB] fp32 for q [B,Hq,D] (bf16, before RoPE) from the
+    gate keys k_gate [B,Hkv,nKB,Dg] of a cache of tmax slots; kv_len int32 [B]."""
+    lib = load()
+    if q.dim() != 3 or k_gate.dim() != 4:
+        raise ValueError("q must be [B,Hq,D] and k_gate [B,Hkv,nKB,Dg]")
+    b, hq, d = q.shape
+    hkv, nkb, dg = k_gate.shape[1], k_gate.shape[2], k_gate.shape[3]
+    if nkb != (tmax + block - 1) // block:
+        raise ValueError(f"k_gate has {nkb} blocks, a cache of {tmax} slots has "
+                         f"{(tmax + block - 1) // block}")
+    _need(q, "q", torch.bfloat16, (b, hq, d))
+    _need(k_gate, "k_gate", torch.float32, (b, hkv, nkb, dg))
+    _need(kv_len, "kv_len", torch.int32, (b,))
+    _need(wq, "wq", torch.float32, (hq, d, dg))
+    if scores is None:
+        scores = torch.empty((b, hq, nkb), dtype=torch.float32, device=q.device)
+    _need(scores, "scores", torch.float32, (b, hq, nkb))
+    sc = (1.0 / dg ** 0.5) if scale is None else float(scale)
+    _check("seer_attn_gate_decode_scores", lib.seer_attn_gate_decode_scores(
+        _ptr(q), _ptr(k_gate), _ptr(kv_len), b, hq, hkv, tmax, d, _ptr(wq), int(dg), sc,
+        float(rope_base), int(block), _ptr(scores), _stream(stream)))
+    return scores
 
 
 def seer_build_mask_decode(scores: torch.Tensor, kv_len: torch.Tensor, block: int, mode: int,

@@ -230,6 +230,66 @@ int seer_attn_gate_mask(const void* q, const void* k, int B, int Hq, int Hkv, in
   return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
 }
 
+namespace {
+
+// Checks shared by the decode gate's workspace size and the call.
+int decode_gate_sizes(int B, int Hq, int Hkv, int Tmax, int D, int Dg, int block) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Tmax < 1 || Hq % Hkv != 0) return SEER_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return SEER_ERR_UNSUPPORTED;
+  if (Dg != 32 && Dg != 64 && Dg != 128) return SEER_ERR_UNSUPPORTED;
+  if (block != 64 && block != 128) return SEER_ERR_UNSUPPORTED;
+  const long long nkb = (Tmax + (long long)block - 1) / block;
+  if (nkb > SEER_MAX_QUERY_BLOCKS) return SEER_ERR_UNSUPPORTED;
+  if (!items_fit(B, Hq > Hkv ? Hq : Hkv, nkb)) return SEER_ERR_UNSUPPORTED;
+  return SEER_OK;
+}
+
+}  // namespace
+
+size_t seer_attn_gate_decode_keys_workspace_size(int B, int Hkv, int Tmax, int D, int block) {
+  if (decode_gate_sizes(B, Hkv, Hkv, Tmax, D, 32, block) != SEER_OK) return 0;
+  const int nkb = (Tmax + block - 1) / block;
+  return seer::attn_gate_decode_keys_workspace_floats(B, Hkv, nkb, D) * sizeof(float) + 256;
+}
+
+int seer_attn_gate_decode_keys(const void* k_cache, const int32_t* kv_len, int B, int Hkv,
+                               int Tmax, int D, const float* wk, int Dg, float rope_base,
+                               int block, int last_block_only, float* k_gate, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  const int st = decode_gate_sizes(B, Hkv, Hkv, Tmax, D, Dg, block);
+  if (st != SEER_OK) return st;
+  if (!(isfinite(rope_base) && rope_base > 1.f)) return SEER_ERR_INVALID_ARG;
+  if (B == 0) return SEER_OK;
+  if (!k_cache || !kv_len || !wk || !k_gate) return SEER_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(wk)) return SEER_ERR_INVALID_ARG;
+  if (!last_block_only) {  // only the all-block pass pools into the workspace
+    const size_t need = seer_attn_gate_decode_keys_workspace_size(B, Hkv, Tmax, D, block);
+    if (!workspace || workspace_bytes < need || !aligned256(workspace))
+      return SEER_ERR_WORKSPACE;
+  }
+  const hipError_t err = seer::launch_attn_gate_decode_keys(
+      k_cache, kv_len, B, Hkv, Tmax, D, wk, Dg, rope_base, block, last_block_only ? 1 : 0,
+      k_gate, static_cast<float*>(workspace), (hipStream_t)stream);
+  return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
+}
+
+int seer_attn_gate_decode_scores(const void* q, const float* k_gate, const int32_t* kv_len,
+                                 int B, int Hq, int Hkv, int Tmax, int D, const float* wq,
+                                 int Dg, float scale, float rope_base, int block, float* scores,
+                                 void* stream) {
+  const int st = decode_gate_sizes(B, Hq, Hkv, Tmax, D, Dg, block);
+  if (st != SEER_OK) return st;
+  if (!(isfinite(scale) && scale > 0.f)) return SEER_ERR_INVALID_ARG;
+  if (!(isfinite(rope_base) && rope_base > 1.f)) return SEER_ERR_INVALID_ARG;
+  if (B == 0) return SEER_OK;
+  if (!q || !k_gate || !kv_len || !wq || !scores) return SEER_ERR_INVALID_ARG;
+  if (!aligned16(k_gate)) return SEER_ERR_INVALID_ARG;
+  const hipError_t err = seer::launch_attn_gate_decode_scores(
+      q, k_gate, kv_len, B, Hq, Hkv, Tmax, D, wq, Dg, scale, rope_base, block, scores,
+      (hipStream_t)stream);
+  return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
+}
+
 int seer_build_mask_decode(const float* scores, const int32_t* kv_len, int B, int H, int nKB,
                            int block, int mode, float threshold, int k_blocks, int keep_sink,
                            int32_t* kv_idx, int32_t* kv_cnt, int max_k, void* stream) {

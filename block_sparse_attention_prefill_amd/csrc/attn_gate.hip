@@ -127,6 +127,20 @@ __global__ __launch_bounds__(64 * kPoolWaves) void gate_pool_kernel(
 // DG = 32 the single tile holds the pair in lanes l and l ^ 16.  The block angle
 // i * base^(-2e/DG) is formed and reduced mod 2 pi in fp64; sin and cos of the
 // reduced angle are fp32.
+// Rotary pair (x1, x2) at block position pos with frequency inv_freq: the angle
+// is formed and reduced mod 2 pi in fp64, sin and cos of the reduced angle are
+// fp32.
+__device__ __forceinline__ void rope_rotate(double inv_freq, int pos, float x1, float x2,
+                                            float& y1, float& y2) {
+  const double two_pi = 6.283185307179586476925287;
+  const double ang = (double)pos * inv_freq;
+  const float r = (float)(ang - two_pi * rint(ang / two_pi));
+  float sn, cs;
+  sincosf(r, &sn, &cs);
+  y1 = x1 * cs - x2 * sn;
+  y2 = x2 * cs + x1 * sn;
+}
+
 constexpr int kProjWaves = 2;
 constexpr int kProjTileRows = 32 * kProjWaves;  // pooled rows per workgroup
 constexpr int kKChunk = 64;                     // input dims per LDS chunk
@@ -224,17 +238,11 @@ __global__ __launch_bounds__(64 * kProjWaves) void gate_project_kernel(
   }
   // acc[u][v]: row 32 wv + 8 (v / 4) + 4 hf + v % 4, column col0(u) + lr.
   float* out = (is_q ? qt : kt) + ((size_t)b * nheads + head) * nqb * DG;
-  const double two_pi = 6.283185307179586476925287;
   // Frequency of this lane's pair: e = col0(0) + lr, or lr % 16 for DG = 32.
   const int e_lane = NTW == 2 ? col0(0) + lr : (lr & 15);
   const double inv_freq = pow((double)rope_base, -2.0 * e_lane / (double)DG);
   auto rotate = [&](int i, float x1, float x2, float& y1, float& y2) {
-    const double ang = (double)i * inv_freq;
-    const float r = (float)(ang - two_pi * rint(ang / two_pi));
-    float sn, cs;
-    sincosf(r, &sn, &cs);
-    y1 = x1 * cs - x2 * sn;
-    y2 = x2 * cs + x1 * sn;
+    rope_rotate(inv_freq, i, x1, x2, y1, y2);
   };
   (void)NT;
 #pragma unroll
@@ -498,6 +506,271 @@ __global__ __launch_bounds__(64 * kRowWaves) void gate_softmax_mask_kernel(
   if (lane == 0) cnt[row] = count;
 }
 
+// ---------------------------------------------------------------------------
+// Per-token gate of decoding (no query pooling).  Gate keys: K is pooled per block
+// of the cache exactly as above but up to each sequence's own length, and the
+// pooled rows go through gate_project_kernel (K slots only) -- or, to refresh
+// only each sequence's last block (the one a new token joins), one row per
+// (sequence, KV head) through gate_decode_row_kernel.  Scores: the token's q
+// through the Q layer and the rotation at its block index nb - 1, then one
+// workgroup per (sequence, query head) takes the logits over the sequence's
+// blocks and their softmax.
+
+// One wave per (sequence, KV head, block): [max | min] over the block's tokens
+// below kv_len, in 64-row steps (non-temporal loads, lane shuffles to combine).
+// Blocks at or past the end of the sequence are not written.
+template <int D>
+__global__ __launch_bounds__(64 * kPoolWaves) void gate_decode_pool_kernel(
+    const __bf16* __restrict__ k, const int32_t* __restrict__ kv_len, int B, int Hkv, int Tmax,
+    int nkb, int bs, float* __restrict__ pk) {
+  constexpr int C = D / 8;   // chunks per row
+  constexpr int R = 64 / C;  // rows read together by the wave
+  constexpr int kPerLane = kTile / R;
+  const int lane = threadIdx.x & 63;
+  const int unit = blockIdx.x * kPoolWaves + (threadIdx.x >> 6);
+  if (unit >= B * Hkv * nkb) return;
+  const int bg = unit / nkb;
+  const int len = min(max(kv_len[bg / Hkv], 0), Tmax);
+  const int j = unit % nkb;
+  const int r0 = bs * j, r1 = min(r0 + bs, len);
+  if (r0 >= r1) return;
+  const __bf16* src = k + (size_t)bg * Tmax * D;
+  const int ch = lane % C, rg = lane / C;
+  float a[8], m[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = -INFINITY;
+    m[e] = INFINITY;
+  }
+  for (int s0 = r0; s0 < r1; s0 += kTile) {
+    bf16x8 x[kPerLane];
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u) {
+      const int r = s0 + rg + R * u;
+      if (r < r1)
+        x[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const bf16x8*>(src + (size_t)r * D + 8 * ch));
+    }
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u) {
+      if (s0 + rg + R * u >= r1) continue;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = (float)x[u][e];
+        a[e] = fmaxf(a[e], v);
+        m[e] = fminf(m[e], v);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = C; off < 64; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = fmaxf(a[e], __shfl_xor(a[e], off, 64));
+      m[e] = fminf(m[e], __shfl_xor(m[e], off, 64));
+    }
+  if (rg == 0) {
+    float* out = pk + ((size_t)bg * nkb + j) * (2 * D) + 8 * ch;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      out[e] = a[e];
+      out[D + e] = m[e];
+    }
+  }
+}
+
+// Projection of one staged gate row on the VALU by a 256-thread workgroup: xs
+// (LDS, din <= 256 inputs) times W [din, DG]; wave w sums input dims
+// [w din/4, (w+1) din/4) for columns t and t + DG/2 (lane t < DG/2), 16 weight
+// pairs in flight at a time; wave 0 adds the four partial sums in order,
+// rotates the pair at block position pos and stores y[t], y[t + DG/2] (y may be
+// in LDS or global memory).  Called by the whole workgroup; ends with a barrier.
+constexpr int kRowThreads = 256;
+
+template <int DG>
+__device__ __forceinline__ void project_row(const float* xs, int din, const float* __restrict__ wr,
+                                            float (*part)[2][DG / 2], int pos, float rope_base,
+                                            float* y) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int per = din / (kRowThreads / 64);  // din is 64, 128 or 256
+  const int d0 = wv * per;
+  if (lane < DG / 2) {
+    float x1 = 0.f, x2 = 0.f;
+    for (int dd = 0; dd < per; dd += 16) {
+      float w1[16], w2[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const size_t o = (size_t)(d0 + dd + u) * DG + lane;
+        w1[u] = wr[o];
+        w2[u] = wr[o + DG / 2];
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        x1 = fmaf(xs[d0 + dd + u], w1[u], x1);
+        x2 = fmaf(xs[d0 + dd + u], w2[u], x2);
+      }
+    }
+    part[wv][0][lane] = x1;
+    part[wv][1][lane] = x2;
+  }
+  __syncthreads();
+  if (wv == 0 && lane < DG / 2) {
+    const float x1 = ((part[0][0][lane] + part[1][0][lane]) + part[2][0][lane]) + part[3][0][lane];
+    const float x2 = ((part[0][1][lane] + part[1][1][lane]) + part[2][1][lane]) + part[3][1][lane];
+    const double inv_freq = pow((double)rope_base, -2.0 * lane / (double)DG);
+    float y1, y2;
+    rope_rotate(inv_freq, pos, x1, x2, y1, y2);
+    y[lane] = y1;
+    y[lane + DG / 2] = y2;
+  }
+  __syncthreads();
+}
+
+// Gate key of each sequence's last block, one 256-thread workgroup per
+// (sequence, KV head): the block's tokens below kv_len are max- and min-pooled
+// (16 rows x 16 chunks of 8 dims per pass, non-temporal 16-byte loads, the 16
+// row groups then combined in LDS), and the pooled row [max | min] is projected
+// with Wk[g] and rotated at the block index, into k_gate.
+template <int D, int DG>
+__global__ __launch_bounds__(kRowThreads) void gate_decode_last_key_kernel(
+    const __bf16* __restrict__ k, const int32_t* __restrict__ kv_len, int Hkv, int Tmax, int nkb,
+    int bs, const float* __restrict__ wk, float rope_base, float* __restrict__ kt) {
+  constexpr int C = D / 8;                 // 16-byte chunks per row
+  constexpr int RG = kRowThreads / C;      // row groups per pass
+  __shared__ float gmax[RG][D], gmin[RG][D];
+  __shared__ float xs[2 * D];
+  __shared__ float part[kRowThreads / 64][2][DG / 2];
+  const int bg = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int len = min(max(kv_len[bg / Hkv], 0), Tmax);
+  if (len == 0) return;  // the whole workgroup leaves together
+  const int j = (len - 1) / bs;
+  const int r0 = bs * j, r1 = len;
+  const __bf16* src = k + (size_t)bg * Tmax * D;
+  const int ch = tid % C, rg = tid / C;
+  float a[8], m[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = -INFINITY;
+    m[e] = INFINITY;
+  }
+  constexpr int kMaxPass = 128 / RG;  // bs <= 128
+  bf16x8 xv[kMaxPass];
+#pragma unroll
+  for (int u = 0; u < kMaxPass; ++u) {
+    const int r = r0 + rg + RG * u;
+    if (r < r1)
+      xv[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const bf16x8*>(src + (size_t)r * D + 8 * ch));
+  }
+#pragma unroll
+  for (int u = 0; u < kMaxPass; ++u) {
+    if (r0 + rg + RG * u >= r1) continue;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = (float)xv[u][e];
+      a[e] = fmaxf(a[e], v);
+      m[e] = fminf(m[e], v);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    gmax[rg][8 * ch + e] = a[e];
+    gmin[rg][8 * ch + e] = m[e];
+  }
+  __syncthreads();
+  for (int d = tid; d < D; d += kRowThreads) {
+    float mx = gmax[0][d], mn = gmin[0][d];
+#pragma unroll
+    for (int g = 1; g < RG; ++g) {
+      mx = fmaxf(mx, gmax[g][d]);
+      mn = fminf(mn, gmin[g][d]);
+    }
+    xs[d] = mx;
+    xs[D + d] = mn;
+  }
+  __syncthreads();
+  project_row<DG>(xs, 2 * D, wk + (size_t)(bg % Hkv) * 2 * D * DG, part, j, rope_base,
+                  kt + ((size_t)bg * nkb + j) * DG);
+}
+
+// Scores of one (sequence, query head): the token's Q~ (project_row), logits
+// scale <Q~, K~_j> over the blocks j < nb (dims in order), then the softmax; a
+// fixed reduction order, so results are bit-reproducible.  Blocks j >= nb get 0
+// (a whole row when nb = 0).
+constexpr int kDecGateThreads = 256;
+constexpr int kDecGatePer = 4096 / kDecGateThreads;  // nKB <= 4096
+
+template <int DG>
+__global__ __launch_bounds__(kDecGateThreads) void gate_decode_scores_kernel(
+    const __bf16* __restrict__ q, const float* __restrict__ wq, float rope_base, int D,
+    const float* __restrict__ kt, const int32_t* __restrict__ kv_len, int Hq, int Hkv, int Tmax,
+    int bs, int nkb, float scale, float* __restrict__ scores) {
+  __shared__ __attribute__((aligned(16))) float qs[DG];
+  __shared__ float red[kDecGateThreads / 64];
+  __shared__ float xs[128];
+  __shared__ float part[kDecGateThreads / 64][2][DG / 2];
+  const int bh = blockIdx.x;
+  const int b = bh / Hq, h = bh % Hq, g = h / (Hq / Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int len = min(max(kv_len[b], 0), Tmax);
+  const int nb = len > 0 ? (len - 1) / bs + 1 : 0;
+  float* out = scores + (size_t)bh * nkb;
+  if (nb == 0) {
+    for (int j = tid; j < nkb; j += kDecGateThreads) out[j] = 0.f;
+    return;
+  }
+  // Q~ of the token (no pooling): q Wq[h], rotated at block nb - 1, into LDS.
+  for (int d = tid; d < D; d += kDecGateThreads) xs[d] = (float)q[(size_t)bh * D + d];
+  __syncthreads();
+  project_row<DG>(xs, D, wq + (size_t)h * D * DG, part, nb - 1, rope_base, qs);
+  const float* kr = kt + (size_t)(b * Hkv + g) * nkb * DG;
+  float x[kDecGatePer];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kDecGatePer; ++u) {
+    const int j = tid + kDecGateThreads * u;
+    x[u] = -INFINITY;
+    if (j < nb) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < DG; e += 4) {
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(kr + (size_t)j * DG + e);
+        s = fmaf(qs[e], kv[0], s);
+        s = fmaf(qs[e + 1], kv[1], s);
+        s = fmaf(qs[e + 2], kv[2], s);
+        s = fmaf(qs[e + 3], kv[3], s);
+      }
+      x[u] = s * scale;
+      mx = fmaxf(mx, x[u]);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (lane == 0) red[wv] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float l = 0.f;
+#pragma unroll
+  for (int u = 0; u < kDecGatePer; ++u) {
+    const int j = tid + kDecGateThreads * u;
+    x[u] = j < nb ? expf(x[u] - mx) : 0.f;
+    l += x[u];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off, 64);
+  if (lane == 0) red[wv] = l;
+  __syncthreads();
+  l = ((red[0] + red[1]) + red[2]) + red[3];
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int u = 0; u < kDecGatePer; ++u) {
+    const int j = tid + kDecGateThreads * u;
+    if (j < nkb) out[j] = x[u] * inv;  // 0 past the sequence
+  }
+}
+
 }  // namespace
 
 // Workspace (fp32): Q~ [B,Hq,nQB,Dg], K~ [B,Hkv,nQB,Dg], per-row tile (max, sum)
@@ -606,6 +879,81 @@ hipError_t launch_attn_gate_mask(const void* q, const void* k, int B, int Hq, in
   else if (nqb <= 64 * 64) SEER_GATE_MASK(64);
   else return hipErrorInvalidValue;  // the host layer rejects nQB > 4096 first
 #undef SEER_GATE_MASK
+  return hipGetLastError();
+}
+
+// Decode gate keys workspace (fp32): the pooled cache K [B,Hkv,nKB,2D].
+size_t attn_gate_decode_keys_workspace_floats(int B, int Hkv, int nkb, int D) {
+  return (size_t)B * Hkv * nkb * 2 * D;
+}
+
+hipError_t launch_attn_gate_decode_keys(const void* k, const int32_t* kv_len, int B, int Hkv,
+                                        int Tmax, int D, const float* wk, int dg,
+                                        float rope_base, int block, int only_last,
+                                        float* kt, float* ws, hipStream_t stream) {
+  const int nkb = (Tmax + block - 1) / block;
+  if (B == 0) return hipSuccess;
+  if (only_last) {
+#define SEER_GATE_KLAST(DD, DG)                                                                \
+  hipLaunchKernelGGL((gate_decode_last_key_kernel<DD, DG>), dim3((unsigned)(B * Hkv)),         \
+                     dim3(kRowThreads), 0, stream, (const __bf16*)k, kv_len, Hkv, Tmax, nkb,     \
+                     block, wk, rope_base, kt)
+    if (D == 128) {
+      if (dg == 128) SEER_GATE_KLAST(128, 128);
+      else if (dg == 64) SEER_GATE_KLAST(128, 64);
+      else SEER_GATE_KLAST(128, 32);
+    } else {
+      if (dg == 128) SEER_GATE_KLAST(64, 128);
+      else if (dg == 64) SEER_GATE_KLAST(64, 64);
+      else SEER_GATE_KLAST(64, 32);
+    }
+#undef SEER_GATE_KLAST
+    return hipGetLastError();
+  }
+  float* pk = ws;
+  const int units = B * Hkv * nkb;  // < 2^31: checked by the host layer
+  const dim3 pgrid((unsigned)((units + kPoolWaves - 1) / kPoolWaves));
+  if (D == 128)
+    hipLaunchKernelGGL(gate_decode_pool_kernel<128>, pgrid, dim3(64 * kPoolWaves), 0, stream,
+                       (const __bf16*)k, kv_len, B, Hkv, Tmax, nkb, block, pk);
+  else
+    hipLaunchKernelGGL(gate_decode_pool_kernel<64>, pgrid, dim3(64 * kPoolWaves), 0, stream,
+                       (const __bf16*)k, kv_len, B, Hkv, Tmax, nkb, block, pk);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  // Every block slot on the matrix cores (slots past a sequence hold stale pooled
+  // rows; their K~ rows are never read).
+  const size_t prow_tiles = (size_t)B * Hkv * ((nkb + kProjTileRows - 1) / kProjTileRows);
+#define SEER_GATE_KPROJ(DG)                                                                    \
+  hipLaunchKernelGGL(gate_project_kernel<DG>, dim3((unsigned)(prow_tiles * ProjCfg<DG>::NG)),   \
+                     dim3(64 * kProjWaves), 0, stream, nullptr, pk, B, 0, Hkv, D, nkb, nullptr,  \
+                     wk, rope_base, nullptr, kt)
+  if (dg == 128) SEER_GATE_KPROJ(128);
+  else if (dg == 64) SEER_GATE_KPROJ(64);
+  else SEER_GATE_KPROJ(32);
+#undef SEER_GATE_KPROJ
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_gate_decode_scores(const void* q, const float* kt, const int32_t* kv_len,
+                                          int B, int Hq, int Hkv, int Tmax, int D,
+                                          const float* wq, int dg, float scale, float rope_base,
+                                          int block, float* scores, hipStream_t stream) {
+  const int nkb = (Tmax + block - 1) / block;
+  if (B == 0) return hipSuccess;
+#define SEER_GATE_DSC(DG)                                                                      \
+  hipLaunchKernelGGL(gate_decode_scores_kernel<DG>, dim3((unsigned)(B * Hq)),                   \
+                     dim3(kDecGateThreads), 0, stream, (const __bf16*)q, wq, rope_base, D, kt,  \
+                     kv_len, Hq, Hkv, Tmax, block, nkb, scale, scores)
+  if (dg == 128) {
+    SEER_GATE_DSC(128);
+  } else if (dg == 64) {
+    SEER_GATE_DSC(64);
+  } else {
+    SEER_GATE_DSC(32);
+  }
+#undef SEER_GATE_DSC
   return hipGetLastError();
 }
 

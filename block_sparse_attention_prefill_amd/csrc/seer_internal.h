@@ -61,6 +61,19 @@ hipError_t launch_attn_gate_mask(const void* q, const void* k, int B, int Hq, in
                                  int keep_sink, int32_t* idx, int32_t* cnt, int max_k,
                                  float* scores, float* ws, hipStream_t stream);
 
+// Per-token decode gate (block 64 or 128, nKB = ceil(Tmax / block) <= 4096 and
+// B * max(Hq, Hkv) * nKB < 2^31, checked by the caller).  Keys: kt [B,Hkv,nKB,Dg]
+// for every block, or only each sequence's last block.  Scores from kt.
+size_t attn_gate_decode_keys_workspace_floats(int B, int Hkv, int nkb, int D);
+hipError_t launch_attn_gate_decode_keys(const void* k, const int32_t* kv_len, int B, int Hkv,
+                                        int Tmax, int D, const float* wk, int dg,
+                                        float rope_base, int block, int only_last,
+                                        float* kt, float* ws, hipStream_t stream);
+hipError_t launch_attn_gate_decode_scores(const void* q, const float* kt, const int32_t* kv_len,
+                                          int B, int Hq, int Hkv, int Tmax, int D,
+                                          const float* wq, int dg, float scale, float rope_base,
+                                          int block, float* scores, hipStream_t stream);
+
 // Decode: workspace bytes and grid size of launch_sparse_decode (list_heads is
 // Hq or Hkv; the caller checks the arguments).
 size_t sparse_decode_workspace_bytes(int B, int Hq, int Hkv, int Tmax, int D, int list_heads,

@@ -308,6 +308,54 @@ int seer_build_mask_decode(const float* scores, const int32_t* kv_len, int B, in
                            int block, int mode, float threshold, int k_blocks, int keep_sink,
                            int32_t* kv_idx, int32_t* kv_cnt, int max_k, void* stream);
 
+/* Bytes of device workspace seer_attn_gate_decode_keys needs for all blocks:
+ * the pooled cache K [B,Hkv,nKB,2D] fp32, nKB = ceil(Tmax / block).  0 for
+ * invalid sizes. */
+size_t seer_attn_gate_decode_keys_workspace_size(int B, int Hkv, int Tmax, int D, int block);
+
+/*
+ * Per-token AttnGate of decoding.  The abstract of "SeerAttention-R: Sparse
+ * Attention Adaptation for Long Reasoning" keeps the gate for decoding but
+ * drops its query pooling; read here as: the K side is seer_attn_gate_scores's
+ * (block [max | min] pooling of the cached K over the sequence's tokens, a
+ * short last block pooling the tokens it has, the same linear layer and block
+ * RoPE at the block index j), the new token's q goes through the same Q layer
+ * unpooled and is rotated at its own block index nb - 1 (nb = ceil(kv_len[b] /
+ * block)), and
+ *   scores[b,h,j] = softmax over j' < nb of scale <Q~_{b,h}, K~_{b,g,j'}>
+ * for j < nb, 0 for j >= nb (a zero row when kv_len[b] = 0).  The gate keys
+ * K~ depend on the cache only, so a decoder keeps them and refreshes just the
+ * block each new token joins: two calls.
+ *
+ * seer_attn_gate_decode_keys: k_gate [B, Hkv, nKB, Dg] fp32 (in/out) gets K~_j
+ *   for every block j < nb of each sequence, or with last_block_only for block
+ *   nb - 1 only (the rows of other blocks are left as they are).
+ * seer_attn_gate_decode_scores: the scores of the tokens q from k_gate.
+ *
+ * q        device bf16 [B, Hq, D], the new tokens (before the model's RoPE).
+ * k_cache  device bf16 [B, Hkv, Tmax, D] (before the model's RoPE), 16-byte
+ *          aligned; kv_len device int32 [B], clamped to [0, Tmax]; positions
+ *          >= kv_len[b] are never read.
+ * wq, wk, Dg, scale, rope_base: as seer_attn_gate_scores (wk and k_gate
+ *          16-byte aligned).
+ * block    64 or 128 (the list block of seer_build_mask_decode); nKB =
+ *          ceil(Tmax / block) <= SEER_MAX_QUERY_BLOCKS.
+ * scores   device fp32 out [B, Hq, nKB], the input of seer_build_mask_decode.
+ * workspace (keys over all blocks only; may be NULL with last_block_only)
+ *          device, >= seer_attn_gate_decode_keys_workspace_size(B, Hkv, Tmax,
+ *          D, block) bytes, 256-byte aligned; overwritten.
+ * Arithmetic is fp32 (all-block keys on the fp32 matrix cores, single rows on
+ * the VALU, RoPE angles reduced in fp64); results are bit-reproducible.
+ */
+int seer_attn_gate_decode_keys(const void* k_cache, const int32_t* kv_len, int B, int Hkv,
+                               int Tmax, int D, const float* wk, int Dg, float rope_base,
+                               int block, int last_block_only, float* k_gate, void* workspace,
+                               size_t workspace_bytes, void* stream);
+int seer_attn_gate_decode_scores(const void* q, const float* k_gate, const int32_t* kv_len,
+                                 int B, int Hq, int Hkv, int Tmax, int D, const float* wq,
+                                 int Dg, float scale, float rope_base, int block, float* scores,
+                                 void* stream);
+
 /* Bytes of device workspace seer_sparse_decode needs (the union of a KV
  * group's per-head lists, and one partial softmax state per chunk of blocks
  * and query head).  0 for invalid sizes. */

@@ -200,6 +200,48 @@ def test_attn_gate_mask_rejects_on_host():
     assert call(p2=0) == 0             # empty
 
 
+def test_attn_gate_decode_rejects_on_host():
+    lib = seer.load()
+    # scores call: q, k_gate, kv_len, B, Hq, Hkv, Tmax, D, wq, Dg, scale, rope_base, block,
+    # scores, stream.  No call here passes every check, so nothing ever launches.
+    a = [FAKE, FAKE, FAKE, 2, 4, 2, 700, 128, FAKE, 64, 0.125, 10000.0, 64, None, None]
+    def call(**kw):
+        b = list(a)
+        for i, v in kw.items():
+            b[int(i[1:])] = v
+        return lib.seer_attn_gate_decode_scores(*b)
+    assert call() == 1                 # scores
+    assert call(p7=96) == 2            # head dim
+    assert call(p9=48) == 2            # gate dim
+    assert call(p12=32) == 2           # block
+    assert call(p4=3) == 1             # Hq % Hkv
+    assert call(p6=0) == 1             # Tmax
+    assert call(p6=64 * 4097) == 2     # more than SEER_MAX_QUERY_BLOCKS blocks
+    assert call(p10=-1.0) == 1         # scale
+    assert call(p11=0.5) == 1          # rope base
+    assert call(p13=FAKE, p2=None) == 1  # kv_len
+    assert call(p13=FAKE, p1=None) == 1  # k_gate
+    assert call(p3=0) == 0             # empty batch
+    # keys call: k_cache, kv_len, B, Hkv, Tmax, D, wk, Dg, rope_base, block, last_only,
+    # k_gate, workspace, workspace_bytes, stream.  The all-block base call fails only
+    # on its 16-byte workspace; every last-block call here lacks k_gate.
+    k = [FAKE, FAKE, 2, 2, 700, 128, FAKE, 64, 10000.0, 64, 0, FAKE, FAKE, 16, None]
+    def kcall(**kw):
+        b = list(k)
+        for i, v in kw.items():
+            b[int(i[1:])] = v
+        return lib.seer_attn_gate_decode_keys(*b)
+    assert kcall() == 4                # workspace too small for the all-block pass
+    assert kcall(p5=96) == 2 and kcall(p7=48) == 2 and kcall(p9=256) == 2
+    assert kcall(p8=1.0) == 1 and kcall(p11=None) == 1 and kcall(p0=None) == 1
+    assert kcall(p10=1, p11=None) == 1  # last block only still needs k_gate
+    assert kcall(p2=0) == 0
+    ws = lib.seer_attn_gate_decode_keys_workspace_size
+    assert ws(8, 8, 40960, 128, 64) >= 8 * 8 * 640 * 256 * 4
+    assert ws(8, 8, 40960, 128, 128) < ws(8, 8, 40960, 128, 64)
+    assert ws(8, 8, 0, 128, 64) == 0
+
+
 def test_build_mask_decode_rejects_on_host():
     lib = seer.load()
     # scores, kv_len, B, H, nKB, block, mode, threshold, k_blocks, keep_sink, idx, cnt, max_k

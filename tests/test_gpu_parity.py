@@ -760,6 +760,92 @@ def test_decode_mask_longest_rows(mode, thr, kb):
     np.testing.assert_array_equal(gi.cpu().numpy(), ri)
 
 
+DEC_GATE_CASES = {
+    # b, hq, hkv, d, tmax, kv_lens, block, dg
+    "ragged_d64_b64": (3, 4, 2, 64, 700, (700, 1, 0), 64, 32),
+    "gqa4_d128_b128": (2, 8, 2, 128, 1000, (1000, 450), 128, 64),
+    "llama_40k": (2, 32, 8, 128, 40960, (40960, 12345), 64, 128),
+}
+
+
+def _dec_gate_inputs(case):
+    b, hq, hkv, d, tmax, lens, block, dg = DEC_GATE_CASES[case]
+    g = torch.Generator().manual_seed(90 + tmax)
+    q = torch.randn(b, hq, d, generator=g).to(torch.bfloat16)
+    kc = torch.randn(b, hkv, tmax, d, generator=g).to(torch.bfloat16)
+    w = wl.custom(95, b, hq, hkv, d, 64)
+    wq, wk = wl.make_gate_weights(w, dg, gain=2.0)
+    return q, kc, wq, wk, lens, block, tmax
+
+
+@pytest.mark.parametrize("case", sorted(DEC_GATE_CASES))
+def test_attn_gate_decode_scores(case):
+    q, kc, wq, wk, lens, block, tmax = _dec_gate_inputs(case)
+    announce(f"decode gate {case}")
+    for bb, n in enumerate(lens):  # cache slots past each sequence: never read
+        kc[bb, :, n:] = float("nan")
+    kl = _dev(torch.tensor(lens, dtype=torch.int32))
+    kg = seer.seer_attn_gate_decode_keys(_dev(kc), kl, _dev(wk), block)
+    s = seer.seer_attn_gate_decode_scores(_dev(q), kg, kl, _dev(wq), tmax, block)
+    torch.cuda.synchronize()
+    ref = oracle.decode_gate_scores_ref(q, kc, lens, wq.numpy(), wk.numpy(), block)
+    got = s.cpu().double().numpy()
+    err = float(np.abs(got - ref).max())
+    announce(f"max-abs error {err:.3e}")
+    assert err <= G_TOL
+    for bb, n in enumerate(lens):
+        assert (got[bb, :, (n + block - 1) // block:] == 0).all()
+    kg2 = seer.seer_attn_gate_decode_keys(_dev(kc), kl, _dev(wk), block)
+    s2 = seer.seer_attn_gate_decode_scores(_dev(q), kg2, kl, _dev(wq), tmax, block)
+    torch.cuda.synchronize()
+    assert torch.equal(s, s2)
+
+
+@pytest.mark.parametrize("case", ["ragged_d64_b64", "gqa4_d128_b128"])
+def test_attn_gate_decode_last_block_updates(case):
+    """Keys built once, then refreshed for the last block only as tokens are appended
+    (across block boundaries): scores stay within tolerance of the oracle's."""
+    q, kc, wq, wk, lens, block, tmax = _dec_gate_inputs(case)
+    lens = [max(1, n - 70) for n in lens]
+    kcd, wqd, wkd, qd = _dev(kc), _dev(wq), _dev(wk), _dev(q)
+    kg = seer.seer_attn_gate_decode_keys(kcd, _dev(torch.tensor(lens, dtype=torch.int32)), wkd,
+                                         block)
+    worst = 0.0
+    for step in range(70):
+        lens = [min(n + 1, tmax) for n in lens]
+        kl = _dev(torch.tensor(lens, dtype=torch.int32))
+        seer.seer_attn_gate_decode_keys(kcd, kl, wkd, block, last_block_only=True, k_gate=kg)
+        if step % 7 == 6:
+            s = seer.seer_attn_gate_decode_scores(qd, kg, kl, wqd, tmax, block)
+            torch.cuda.synchronize()
+            ref = oracle.decode_gate_scores_ref(q, kc, lens, wq.numpy(), wk.numpy(), block)
+            worst = max(worst, float(np.abs(s.cpu().double().numpy() - ref).max()))
+    announce(f"incremental keys: worst max-abs error {worst:.3e}")
+    assert worst <= G_TOL
+
+
+def test_attn_gate_decode_matches_prefill_gate_last_row():
+    """GPU decode gate against the GPU prefill gate when every row of the last block is
+    the token's q (mean pooling then returns q): equal within the score tolerance."""
+    b, hq, hkv, d, t, dg = 1, 8, 2, 128, 1000, 64
+    g = torch.Generator().manual_seed(97)
+    qf = torch.randn(b, hq, t, d, generator=g).to(torch.bfloat16)
+    kf = torch.randn(b, hkv, t, d, generator=g).to(torch.bfloat16)
+    nb = (t + 63) // 64
+    qtok = qf[:, :, t - 1].clone()
+    qf[:, :, 64 * (nb - 1):] = qtok[:, :, None, :]
+    w = wl.custom(96, b, hq, hkv, d, t)
+    wq, wk = (_dev(x) for x in wl.make_gate_weights(w, dg))
+    pre = seer.seer_attn_gate_scores(_dev(qf), _dev(kf), wq, wk)
+    kl = _dev(torch.tensor([t], dtype=torch.int32))
+    kg = seer.seer_attn_gate_decode_keys(_dev(kf), kl, wk)
+    dec = seer.seer_attn_gate_decode_scores(_dev(qtok), kg, kl, wq, t)
+    torch.cuda.synchronize()
+    err = float((pre[:, :, nb - 1, :].double() - dec.double()).abs().max())
+    announce(f"decode vs prefill gate last row: {err:.3e}")
+    assert err <= 2 * G_TOL
+
+
 def _decode_lists(seed, dw, max_k, dense=False):
     """Random valid block sets per list head (any order), some with entries past
     the sequence that must be skipped; dense=True lists every block."""
