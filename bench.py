@@ -189,7 +189,25 @@ def decode_bench(seer, wl, torch, dev, args):
     out["gate_keys_all_blocks_ms"] = round(time_calls(kall, max(3, args.steps // 2), torch,
                                                       flush), 4)
     out["gate_step_ms"] = round(time_calls(kstep, max(5, args.steps), torch, flush), 4)
-    del wq, wk, gsc, gws, kg
+    # Gate step through to per-query-head lists: keys of the last blocks, then scores
+    # and the mask build as two calls, or the one-pass scores-to-lists call.
+    dv = wl.DEC2
+    gmax_k = min(dv.nkb, max(dv.k_blocks, 2))
+    gidx, gcnt = seer.seer_build_mask_decode(gsc, ld, dv.block, wl.MODE_TOPK, 0.0, dv.k_blocks,
+                                             dv.keep_sink, gmax_k)
+    two = lambda: (kstep(), seer.seer_build_mask_decode(
+        gsc, ld, dv.block, wl.MODE_TOPK, 0.0, dv.k_blocks, dv.keep_sink, gmax_k, kv_idx=gidx,
+        kv_cnt=gcnt))
+    one = lambda: (seer.seer_attn_gate_decode_keys(kd, ld, wk, dw.block, last_block_only=True,
+                                                   k_gate=kg),
+                   seer.seer_attn_gate_decode_mask(qd, kg, ld, wq, dw.tmax, wl.MODE_TOPK, 0.0,
+                                                   dv.k_blocks, dv.keep_sink, gmax_k, dw.block,
+                                                   kv_idx=gidx, kv_cnt=gcnt))
+    one()
+    out["gate_to_lists_two_call_ms"] = round(time_calls(two, max(5, args.steps), torch, flush),
+                                             4)
+    out["gate_to_lists_fused_ms"] = round(time_calls(one, max(5, args.steps), torch, flush), 4)
+    del wq, wk, gsc, gws, kg, gidx, gcnt
     for var in (dw, wl.DEC2):
         sc = wl.make_decode_scores(var).to(dev)
         max_k = min(var.nkb, max(var.k_blocks, 2))

@@ -27,7 +27,7 @@ EXPORTED = (
     "seer_pooled_attn_map_workspace_size", "seer_pooled_attn_map", "seer_pooled_target_mse",
     "seer_attn_gate_workspace_size", "seer_attn_gate_scores", "seer_attn_gate_mask_workspace_size",
     "seer_attn_gate_mask", "seer_attn_gate_decode_keys_workspace_size", "seer_attn_gate_decode_keys",
-    "seer_attn_gate_decode_scores", "seer_build_mask_decode",
+    "seer_attn_gate_decode_scores", "seer_attn_gate_decode_mask", "seer_build_mask_decode",
     "seer_sparse_decode_workspace_size", "seer_sparse_decode",
 )
 
@@ -102,6 +102,11 @@ def load() -> ctypes.CDLL:
     lib.seer_attn_gate_decode_scores.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int,
                                                  c_int, c_int, c_void, c_int, c_float, c_float,
                                                  c_int, c_void, c_void]
+    lib.seer_attn_gate_decode_mask.restype = c_int
+    lib.seer_attn_gate_decode_mask.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int,
+                                               c_int, c_void, c_int, c_float, c_float, c_int,
+                                               c_int, c_float, c_int, c_int, c_void, c_void, c_int,
+                                               c_void, c_void]
     lib.seer_build_mask_decode.restype = c_int
     lib.seer_build_mask_decode.argtypes = [c_void, c_void, c_int, c_int, c_int, c_int, c_int,
                                            c_float, c_int, c_int, c_void, c_void, c_int, c_void]
@@ -427,6 +432,48 @@ def seer_attn_gate_decode_scores(q: torch.Tensor, k_gate: torch.Tensor, kv_len: 
         _ptr(q), _ptr(k_gate), _ptr(kv_len), b, hq, hkv, tmax, d, _ptr(wq), int(dg), sc,
         float(rope_base), int(block), _ptr(scores), _stream(stream)))
     return scores
+
+
+def seer_attn_gate_decode_mask(q: torch.Tensor, k_gate: torch.Tensor, kv_len: torch.Tensor,
+                               wq: torch.Tensor, tmax: int, mode: int, threshold: float,
+                               k_blocks: int, keep_sink: bool, max_k: int, block: int = BLOCK,
+                               scale: Optional[float] = None, rope_base: float = 10000.0,
+                               return_scores: bool = False,
+                               kv_idx: Optional[torch.Tensor] = None,
+                               kv_cnt: Optional[torch.Tensor] = None,
+                               scores: Optional[torch.Tensor] = None, stream=None):
+    """Per-token gate scores and decode lists in one pass: the lists of
+    seer_build_mask_decode on seer_attn_gate_decode_scores's rows ->
+    (kv_idx int32 [B,Hq,max_k], kv_cnt int32 [B,Hq], scores [B,Hq,nKB] or None)."""
+    lib = load()
+    if q.dim() != 3 or k_gate.dim() != 4:
+        raise ValueError("q must be [B,Hq,D] and k_gate [B,Hkv,nKB,Dg]")
+    b, hq, d = q.shape
+    hkv, nkb, dg = k_gate.shape[1], k_gate.shape[2], k_gate.shape[3]
+    if nkb != (tmax + block - 1) // block:
+        raise ValueError(f"k_gate has {nkb} blocks, a cache of {tmax} slots has "
+                         f"{(tmax + block - 1) // block}")
+    _need(q, "q", torch.bfloat16, (b, hq, d))
+    _need(k_gate, "k_gate", torch.float32, (b, hkv, nkb, dg))
+    _need(kv_len, "kv_len", torch.int32, (b,))
+    _need(wq, "wq", torch.float32, (hq, d, dg))
+    if kv_idx is None:
+        kv_idx = torch.empty((b, hq, max_k), dtype=torch.int32, device=q.device)
+    if kv_cnt is None:
+        kv_cnt = torch.empty((b, hq), dtype=torch.int32, device=q.device)
+    _need(kv_idx, "kv_idx", torch.int32, (b, hq, max_k))
+    _need(kv_cnt, "kv_cnt", torch.int32, (b, hq))
+    if return_scores and scores is None:
+        scores = torch.empty((b, hq, nkb), dtype=torch.float32, device=q.device)
+    if scores is not None:
+        _need(scores, "scores", torch.float32, (b, hq, nkb))
+    sc = (1.0 / dg ** 0.5) if scale is None else float(scale)
+    _check("seer_attn_gate_decode_mask", lib.seer_attn_gate_decode_mask(
+        _ptr(q), _ptr(k_gate), _ptr(kv_len), b, hq, hkv, tmax, d, _ptr(wq), int(dg), sc,
+        float(rope_base), int(block), int(mode), float(threshold), int(k_blocks),
+        int(bool(keep_sink)), _ptr(kv_idx), _ptr(kv_cnt), int(max_k), _ptr(scores),
+        _stream(stream)))
+    return kv_idx, kv_cnt, scores
 
 
 def seer_build_mask_decode(scores: torch.Tensor, kv_len: torch.Tensor, block: int, mode: int,

@@ -290,6 +290,37 @@ int seer_attn_gate_decode_scores(const void* q, const float* k_gate, const int32
   return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
 }
 
+int seer_attn_gate_decode_mask(const void* q, const float* k_gate, const int32_t* kv_len, int B,
+                               int Hq, int Hkv, int Tmax, int D, const float* wq, int Dg,
+                               float scale, float rope_base, int block, int mode,
+                               float threshold, int k_blocks, int keep_sink, int32_t* kv_idx,
+                               int32_t* kv_cnt, int max_k, float* scores, void* stream) {
+  const int st = decode_gate_sizes(B, Hq, Hkv, Tmax, D, Dg, block);
+  if (st != SEER_OK) return st;
+  if (!(isfinite(scale) && scale > 0.f)) return SEER_ERR_INVALID_ARG;
+  if (!(isfinite(rope_base) && rope_base > 1.f)) return SEER_ERR_INVALID_ARG;
+  if (mode != SEER_MASK_TOPK && mode != SEER_MASK_THRESHOLD) return SEER_ERR_INVALID_ARG;
+  if (mode == SEER_MASK_TOPK && k_blocks < 1) return SEER_ERR_INVALID_ARG;
+  if (mode == SEER_MASK_THRESHOLD && !isfinite(threshold)) return SEER_ERR_INVALID_ARG;
+  if (max_k < 1) return SEER_ERR_CAPACITY;
+  const int nkb = (Tmax + block - 1) / block;
+  const int forced = keep_sink ? 2 : 1;
+  if (mode == SEER_MASK_TOPK) {
+    const int want = k_blocks > forced ? k_blocks : forced;
+    if (max_k < (want < nkb ? want : nkb)) return SEER_ERR_CAPACITY;
+  } else {
+    if (max_k < ((keep_sink && nkb > 1) ? 2 : 1)) return SEER_ERR_CAPACITY;
+  }
+  if ((long long)B * Hq * max_k > (long long)INT_MAX) return SEER_ERR_UNSUPPORTED;
+  if (B == 0) return SEER_OK;
+  if (!q || !k_gate || !kv_len || !wq || !kv_idx || !kv_cnt) return SEER_ERR_INVALID_ARG;
+  if (!aligned16(k_gate)) return SEER_ERR_INVALID_ARG;
+  const hipError_t err = seer::launch_attn_gate_decode_mask(
+      q, k_gate, kv_len, B, Hq, Hkv, Tmax, D, wq, Dg, scale, rope_base, block, mode, threshold,
+      k_blocks, keep_sink ? 1 : 0, kv_idx, kv_cnt, max_k, scores, (hipStream_t)stream);
+  return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
+}
+
 int seer_build_mask_decode(const float* scores, const int32_t* kv_len, int B, int H, int nKB,
                            int block, int mode, float threshold, int k_blocks, int keep_sink,
                            int32_t* kv_idx, int32_t* kv_cnt, int max_k, void* stream) {

@@ -701,31 +701,24 @@ __global__ __launch_bounds__(kRowThreads) void gate_decode_last_key_kernel(
 constexpr int kDecGateThreads = 256;
 constexpr int kDecGatePer = 4096 / kDecGateThreads;  // nKB <= 4096
 
+struct DecGateShared {
+  float red[kDecGateThreads / 64];
+  float xs[128];
+};
+
+// The probabilities of a row with nb > 0 into x[u] (block j = tid + 256 u; 0 for
+// j >= nb).  Called by the whole workgroup.
 template <int DG>
-__global__ __launch_bounds__(kDecGateThreads) void gate_decode_scores_kernel(
+__device__ __forceinline__ void decode_gate_probs(
     const __bf16* __restrict__ q, const float* __restrict__ wq, float rope_base, int D,
-    const float* __restrict__ kt, const int32_t* __restrict__ kv_len, int Hq, int Hkv, int Tmax,
-    int bs, int nkb, float scale, float* __restrict__ scores) {
-  __shared__ __attribute__((aligned(16))) float qs[DG];
-  __shared__ float red[kDecGateThreads / 64];
-  __shared__ float xs[128];
-  __shared__ float part[kDecGateThreads / 64][2][DG / 2];
-  const int bh = blockIdx.x;
-  const int b = bh / Hq, h = bh % Hq, g = h / (Hq / Hkv);
+    const float* __restrict__ kt, int bh, int h, int kvrow, int nb, int nkb, float scale,
+    float* qs, float (*part)[2][DG / 2], DecGateShared& sh, float (&x)[kDecGatePer]) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int len = min(max(kv_len[b], 0), Tmax);
-  const int nb = len > 0 ? (len - 1) / bs + 1 : 0;
-  float* out = scores + (size_t)bh * nkb;
-  if (nb == 0) {
-    for (int j = tid; j < nkb; j += kDecGateThreads) out[j] = 0.f;
-    return;
-  }
   // Q~ of the token (no pooling): q Wq[h], rotated at block nb - 1, into LDS.
-  for (int d = tid; d < D; d += kDecGateThreads) xs[d] = (float)q[(size_t)bh * D + d];
+  for (int d = tid; d < D; d += kDecGateThreads) sh.xs[d] = (float)q[(size_t)bh * D + d];
   __syncthreads();
-  project_row<DG>(xs, D, wq + (size_t)h * D * DG, part, nb - 1, rope_base, qs);
-  const float* kr = kt + (size_t)(b * Hkv + g) * nkb * DG;
-  float x[kDecGatePer];
+  project_row<DG>(sh.xs, D, wq + (size_t)h * D * DG, part, nb - 1, rope_base, qs);
+  const float* kr = kt + (size_t)kvrow * nkb * DG;
   float mx = -INFINITY;
 #pragma unroll
   for (int u = 0; u < kDecGatePer; ++u) {
@@ -747,9 +740,9 @@ __global__ __launch_bounds__(kDecGateThreads) void gate_decode_scores_kernel(
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if (lane == 0) red[wv] = mx;
+  if (lane == 0) sh.red[wv] = mx;
   __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  mx = fmaxf(fmaxf(sh.red[0], sh.red[1]), fmaxf(sh.red[2], sh.red[3]));
   __syncthreads();
   float l = 0.f;
 #pragma unroll
@@ -760,15 +753,112 @@ __global__ __launch_bounds__(kDecGateThreads) void gate_decode_scores_kernel(
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off, 64);
-  if (lane == 0) red[wv] = l;
+  if (lane == 0) sh.red[wv] = l;
   __syncthreads();
-  l = ((red[0] + red[1]) + red[2]) + red[3];
+  l = ((sh.red[0] + sh.red[1]) + sh.red[2]) + sh.red[3];
   const float inv = 1.0f / l;
+#pragma unroll
+  for (int u = 0; u < kDecGatePer; ++u) x[u] *= inv;
+}
+
+template <int DG>
+__global__ __launch_bounds__(kDecGateThreads) void gate_decode_scores_kernel(
+    const __bf16* __restrict__ q, const float* __restrict__ wq, float rope_base, int D,
+    const float* __restrict__ kt, const int32_t* __restrict__ kv_len, int Hq, int Hkv, int Tmax,
+    int bs, int nkb, float scale, float* __restrict__ scores) {
+  __shared__ __attribute__((aligned(16))) float qs[DG];
+  __shared__ float part[kDecGateThreads / 64][2][DG / 2];
+  __shared__ DecGateShared sh;
+  const int bh = blockIdx.x;
+  const int b = bh / Hq, h = bh % Hq, g = h / (Hq / Hkv);
+  const int tid = threadIdx.x;
+  const int len = min(max(kv_len[b], 0), Tmax);
+  const int nb = len > 0 ? (len - 1) / bs + 1 : 0;
+  float* out = scores + (size_t)bh * nkb;
+  if (nb == 0) {
+    for (int j = tid; j < nkb; j += kDecGateThreads) out[j] = 0.f;
+    return;
+  }
+  float x[kDecGatePer];
+  decode_gate_probs<DG>(q, wq, rope_base, D, kt, bh, h, b * Hkv + g, nb, nkb, scale, qs, part,
+                        sh, x);
 #pragma unroll
   for (int u = 0; u < kDecGatePer; ++u) {
     const int j = tid + kDecGateThreads * u;
-    if (j < nkb) out[j] = x[u] * inv;  // 0 past the sequence
+    if (j < nkb) out[j] = x[u];  // 0 past the sequence
   }
+}
+
+// Scores and the decode block lists of one (sequence, query head) in one pass:
+// the probabilities as gate_decode_scores_kernel computes them, optionally
+// written out, then staged in LDS so that wave 0 holds block j = 64 c + lane in
+// slot c and runs the selection of seer_build_mask_decode's decode rows (same
+// keys, same count rule, same select): the same lists, bit for bit.
+template <int DG, int NPL>
+__global__ __launch_bounds__(kDecGateThreads) void gate_decode_mask_kernel(
+    const __bf16* __restrict__ q, const float* __restrict__ wq, float rope_base, int D,
+    const float* __restrict__ kt, const int32_t* __restrict__ kv_len, int Hq, int Hkv, int Tmax,
+    int bs, int nkb, float scale, float* __restrict__ scores, int mode, float tau, int k_blocks,
+    int keep_sink, int32_t* __restrict__ idx, int32_t* __restrict__ cnt, int max_k) {
+  __shared__ __attribute__((aligned(16))) float qs[DG];
+  __shared__ float part[kDecGateThreads / 64][2][DG / 2];
+  __shared__ DecGateShared sh;
+  __shared__ float prow[64 * NPL];
+  __shared__ int hist[256];
+  const int bh = blockIdx.x;
+  const int b = bh / Hq, h = bh % Hq, g = h / (Hq / Hkv);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int len = min(max(kv_len[b], 0), Tmax);
+  const int nb = len > 0 ? (len - 1) / bs + 1 : 0;
+  if (nb > 0) {
+    float x[kDecGatePer];
+    decode_gate_probs<DG>(q, wq, rope_base, D, kt, bh, h, b * Hkv + g, nb, nkb, scale, qs, part,
+                          sh, x);
+#pragma unroll
+    for (int u = 0; u < kDecGatePer; ++u) {
+      const int j = tid + kDecGateThreads * u;
+      if (j < nkb) {
+        prow[j] = x[u];
+        if (scores) scores[(size_t)bh * nkb + j] = x[u];
+      }
+    }
+  } else if (scores) {
+    for (int j = tid; j < nkb; j += kDecGateThreads) scores[(size_t)bh * nkb + j] = 0.f;
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  // Decode row rule: the last block holds the token (forced, like the diagonal),
+  // block 0 too with keep_sink; TopK keeps min(nb, max(forced, k_blocks)).
+  const int i = nb - 1;
+  const int n = nb;
+  uint32_t key[NPL];
+  int npos = 0;
+#pragma unroll
+  for (int c = 0; c < NPL; ++c) {
+    const int j = 64 * c + lane;
+    uint32_t kj = 0u;
+    if (j < n) {
+      if (j == i || (keep_sink && j == 0)) {
+        kj = 0xFFFFFFFFu;
+      } else {
+        const float p = prow[j];
+        kj = (mode == 1 || p >= tau) ? rowsel::order_key(p) : 0u;
+      }
+    }
+    key[c] = kj;
+    npos += kj != 0u;
+  }
+  npos = rowsel::wave_sum(npos);
+  int k;
+  if (mode == 1) {
+    const int forced = (i == 0) ? 1 : (keep_sink ? 2 : 1);
+    k = min(i + 1, max(forced, k_blocks));
+  } else {
+    k = min(npos, max_k);
+  }
+  const int count = rowsel::wave_select_row<NPL>(key, n, k, npos, lane, hist,
+                                                 idx + (size_t)bh * max_k, max_k);
+  if (lane == 0) cnt[bh] = count;
 }
 
 }  // namespace
@@ -954,6 +1044,38 @@ hipError_t launch_attn_gate_decode_scores(const void* q, const float* kt, const 
     SEER_GATE_DSC(32);
   }
 #undef SEER_GATE_DSC
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_gate_decode_mask(const void* q, const float* kt, const int32_t* kv_len,
+                                        int B, int Hq, int Hkv, int Tmax, int D, const float* wq,
+                                        int dg, float scale, float rope_base, int block,
+                                        int mode, float threshold, int k_blocks, int keep_sink,
+                                        int32_t* idx, int32_t* cnt, int max_k, float* scores,
+                                        hipStream_t stream) {
+  const int nkb = (Tmax + block - 1) / block;
+  if (B == 0) return hipSuccess;
+  const dim3 grid((unsigned)(B * Hq));
+#define SEER_DGM(DG, NPL)                                                                      \
+  hipLaunchKernelGGL((gate_decode_mask_kernel<DG, NPL>), grid, dim3(kDecGateThreads), 0, stream, \
+                     (const __bf16*)q, wq, rope_base, D, kt, kv_len, Hq, Hkv, Tmax, block, nkb,  \
+                     scale, scores, mode, threshold, k_blocks, keep_sink, idx, cnt, max_k)
+#define SEER_DGM_NPL(DG)                                                                       \
+  if (nkb <= 64) SEER_DGM(DG, 1);                                                              \
+  else if (nkb <= 64 * 4) SEER_DGM(DG, 4);                                                     \
+  else if (nkb <= 64 * 8) SEER_DGM(DG, 8);                                                     \
+  else if (nkb <= 64 * 16) SEER_DGM(DG, 16);                                                   \
+  else if (nkb <= 64 * 32) SEER_DGM(DG, 32);                                                   \
+  else SEER_DGM(DG, 64)
+  if (dg == 128) {
+    SEER_DGM_NPL(128);
+  } else if (dg == 64) {
+    SEER_DGM_NPL(64);
+  } else {
+    SEER_DGM_NPL(32);
+  }
+#undef SEER_DGM_NPL
+#undef SEER_DGM
   return hipGetLastError();
 }
 

@@ -73,6 +73,14 @@ hipError_t launch_attn_gate_decode_scores(const void* q, const float* kt, const 
                                           int B, int Hq, int Hkv, int Tmax, int D,
                                           const float* wq, int dg, float scale, float rope_base,
                                           int block, float* scores, hipStream_t stream);
+// Decode gate scores straight into decode block lists (nKB <= 4096; the same
+// argument rules as launch_build_mask_decode); scores may be null.
+hipError_t launch_attn_gate_decode_mask(const void* q, const float* kt, const int32_t* kv_len,
+                                        int B, int Hq, int Hkv, int Tmax, int D, const float* wq,
+                                        int dg, float scale, float rope_base, int block,
+                                        int mode, float threshold, int k_blocks, int keep_sink,
+                                        int32_t* idx, int32_t* cnt, int max_k, float* scores,
+                                        hipStream_t stream);
 
 // Decode: workspace bytes and grid size of launch_sparse_decode (list_heads is
 // Hq or Hkv; the caller checks the arguments).

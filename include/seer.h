@@ -356,6 +356,22 @@ int seer_attn_gate_decode_scores(const void* q, const float* k_gate, const int32
                                  int Dg, float scale, float rope_base, int block, float* scores,
                                  void* stream);
 
+/*
+ * seer_attn_gate_decode_scores and seer_build_mask_decode in one pass: each
+ * (sequence, query head) computes its score row as the scores call does and
+ * selects its blocks from it on chip with the decode rule of
+ * seer_build_mask_decode (H = Hq, nKB = ceil(Tmax / block)), so kv_idx and
+ * kv_cnt equal the two-call result bit for bit and the scores need not go
+ * through memory.  scores may be NULL; if given it receives the same row as
+ * the scores call.  Arguments and errors are those of the two calls; in
+ * addition B * Hq * max_k must fit in int32 (else SEER_ERR_UNSUPPORTED).
+ */
+int seer_attn_gate_decode_mask(const void* q, const float* k_gate, const int32_t* kv_len, int B,
+                               int Hq, int Hkv, int Tmax, int D, const float* wq, int Dg,
+                               float scale, float rope_base, int block, int mode,
+                               float threshold, int k_blocks, int keep_sink, int32_t* kv_idx,
+                               int32_t* kv_cnt, int max_k, float* scores, void* stream);
+
 /* Bytes of device workspace seer_sparse_decode needs (the union of a KV
  * group's per-head lists, and one partial softmax state per chunk of blocks
  * and query head).  0 for invalid sizes. */

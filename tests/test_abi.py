@@ -242,6 +242,42 @@ def test_attn_gate_decode_rejects_on_host():
     assert ws(8, 8, 0, 128, 64) == 0
 
 
+def test_attn_gate_decode_mask_rejects_on_host():
+    lib = seer.load()
+    # q, k_gate, kv_len, B, Hq, Hkv, Tmax, D, wq, Dg, scale, rope_base, block, mode,
+    # threshold, k_blocks, keep_sink, kv_idx, kv_cnt, max_k, scores, stream (nKB = 11).
+    # The base call lacks kv_cnt, and every call that supplies it lacks another pointer.
+    a = [FAKE, FAKE, FAKE, 2, 4, 2, 700, 128, FAKE, 64, 0.125, 10000.0, 64, 1, 0.0, 4, 1,
+         FAKE, None, 16, None, None]
+    def call(**kw):
+        b = list(a)
+        for i, v in kw.items():
+            b[int(i[1:])] = v
+        return lib.seer_attn_gate_decode_mask(*b)
+    assert call() == 1                 # kv_cnt
+    assert call(p7=96) == 2            # head dim
+    assert call(p9=48) == 2            # gate dim
+    assert call(p12=32) == 2           # block
+    assert call(p6=64 * 4097) == 2     # more than SEER_MAX_QUERY_BLOCKS blocks
+    assert call(p4=3) == 1             # Hq % Hkv
+    assert call(p10=-1.0) == 1         # scale
+    assert call(p11=0.5) == 1          # rope base
+    assert call(p13=7) == 1            # mode
+    assert call(p15=0) == 1            # TopK budget
+    assert call(p19=3) == 3            # max_k below the budget
+    assert call(p15=40, p19=10) == 3   # budget capped at nKB = 11
+    assert call(p15=40, p19=11) == 1   # enough room: fails on kv_cnt
+    assert call(p13=0, p14=float("nan")) == 1  # threshold
+    assert call(p13=0, p19=1) == 3     # sink + last block need 2
+    assert call(p19=0) == 3
+    assert call(p19=1 << 30) == 2      # B * Hq * max_k over int32
+    assert call(p18=FAKE, p0=None) == 1 and call(p18=FAKE, p1=None) == 1
+    assert call(p18=FAKE, p2=None) == 1 and call(p18=FAKE, p8=None) == 1
+    assert call(p18=FAKE, p17=None) == 1
+    assert call(p18=FAKE, p1=FAKE + 4) == 1     # k_gate not 16-byte aligned
+    assert call(p3=0) == 0             # empty batch
+
+
 def test_build_mask_decode_rejects_on_host():
     lib = seer.load()
     # scores, kv_len, B, H, nKB, block, mode, threshold, k_blocks, keep_sink, idx, cnt, max_k

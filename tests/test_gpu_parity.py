@@ -846,6 +846,39 @@ def test_attn_gate_decode_matches_prefill_gate_last_row():
     assert err <= 2 * G_TOL
 
 
+@pytest.mark.parametrize("case", sorted(DEC_GATE_CASES))
+def test_attn_gate_decode_mask_equals_scores_then_mask(case):
+    """One-pass decode gate lists equal seer_build_mask_decode on the scores call's
+    rows, bit for bit (TopK and threshold, with and without the sink, a short max_k),
+    and the optional score output equals the scores call's."""
+    q, kc, wq, wk, lens, block, tmax = _dec_gate_inputs(case)
+    announce(f"decode gate mask {case}")
+    kl = _dev(torch.tensor(lens, dtype=torch.int32))
+    qd, wqd = _dev(q), _dev(wq)
+    kg = seer.seer_attn_gate_decode_keys(_dev(kc), kl, _dev(wk), block)
+    ref_s = seer.seer_attn_gate_decode_scores(qd, kg, kl, wqd, tmax, block)
+    nkb = (tmax + block - 1) // block
+    rules = [(seer.SEER_MASK_TOPK, 0.0, 4, True, 8), (seer.SEER_MASK_TOPK, 0.0, 64, False, 64),
+             (seer.SEER_MASK_THRESHOLD, 1.0 / nkb, 1, True, nkb),
+             (seer.SEER_MASK_THRESHOLD, 1.0 / nkb, 1, False, 5)]
+    for mode, tau, kb, sink, max_k in rules:
+        max_k = min(max_k, nkb) if mode == seer.SEER_MASK_TOPK else max_k
+        ri, rc = seer.seer_build_mask_decode(ref_s, kl, block, mode, tau, kb, sink, max_k)
+        fi = torch.full_like(ri, -7)
+        fc = torch.full_like(rc, -7)
+        fi, fc, fs = seer.seer_attn_gate_decode_mask(qd, kg, kl, wqd, tmax, mode, tau, kb, sink,
+                                                     max_k, block, return_scores=True,
+                                                     kv_idx=fi, kv_cnt=fc)
+        ni, nc, none = seer.seer_attn_gate_decode_mask(qd, kg, kl, wqd, tmax, mode, tau, kb,
+                                                       sink, max_k, block)
+        torch.cuda.synchronize()
+        assert none is None
+        assert torch.equal(fs, ref_s)
+        assert torch.equal(fi, ri) and torch.equal(fc, rc), (mode, sink, max_k)
+        assert torch.equal(ni, ri) and torch.equal(nc, rc)
+        assert int(rc.min()) >= 0 and int(rc.max()) <= max_k
+
+
 def _decode_lists(seed, dw, max_k, dense=False):
     """Random valid block sets per list head (any order), some with entries past
     the sequence that must be skipped; dense=True lists every block."""
