@@ -114,19 +114,6 @@ __global__ __launch_bounds__(64 * kPoolWaves) void gate_pool_kernel(
   }
 }
 
-// Linear layer + block RoPE on the fp32 matrix cores.  One workgroup (two
-// waves) per (batch, head slot, 64 pooled rows, column group); wave w computes
-// rows 32 w .. 32 w + 31 of the group's 32-column tiles with
-// v_mfma_f32_32x32x2f32, streaming 64-dim chunks of the rows and of the weights
-// (stored transposed) through LDS, the next chunk's loads in flight during the
-// current chunk's MFMAs.  In each group of 4 MFMAs a lane feeds 4 consecutive
-// dims from one 16-byte read (lanes 0-31 and 32-63 take the two halves of an
-// 8-dim group: any assignment of dims to MFMA k-slots works as long as both
-// operands use the same one).  A column group is the tile pair {cg, cg + DG/64}
-// that holds both columns e and e + DG/2 of a RoPE pair in the same lane; for
-// DG = 32 the single tile holds the pair in lanes l and l ^ 16.  The block angle
-// i * base^(-2e/DG) is formed and reduced mod 2 pi in fp64; sin and cos of the
-// reduced angle are fp32.
 // Rotary pair (x1, x2) at block position pos with frequency inv_freq: the angle
 // is formed and reduced mod 2 pi in fp64, sin and cos of the reduced angle are
 // fp32.
@@ -141,6 +128,19 @@ __device__ __forceinline__ void rope_rotate(double inv_freq, int pos, float x1, 
   y2 = x2 * cs + x1 * sn;
 }
 
+// Linear layer + block RoPE on the fp32 matrix cores.  One workgroup (two
+// waves) per (batch, head slot, 64 pooled rows, column group); wave w computes
+// rows 32 w .. 32 w + 31 of the group's 32-column tiles with
+// v_mfma_f32_32x32x2f32, streaming 64-dim chunks of the rows and of the weights
+// (stored transposed) through LDS, the next chunk's loads in flight during the
+// current chunk's MFMAs.  In each group of 4 MFMAs a lane feeds 4 consecutive
+// dims from one 16-byte read (lanes 0-31 and 32-63 take the two halves of an
+// 8-dim group: any assignment of dims to MFMA k-slots works as long as both
+// operands use the same one).  A column group is the tile pair {cg, cg + DG/64}
+// that holds both columns e and e + DG/2 of a RoPE pair in the same lane; for
+// DG = 32 the single tile holds the pair in lanes l and l ^ 16.  The block angle
+// i * base^(-2e/DG) is formed and reduced mod 2 pi in fp64; sin and cos of the
+// reduced angle are fp32.
 constexpr int kProjWaves = 2;
 constexpr int kProjTileRows = 32 * kProjWaves;  // pooled rows per workgroup
 constexpr int kKChunk = 64;                     // input dims per LDS chunk
@@ -695,46 +695,102 @@ __global__ __launch_bounds__(kRowThreads) void gate_decode_last_key_kernel(
 }
 
 // Scores of one (sequence, query head): the token's Q~ (project_row), logits
-// scale <Q~, K~_j> over the blocks j < nb (dims in order), then the softmax; a
+// scale <Q~, K~_j> over the blocks j < nb, then the softmax; a
 // fixed reduction order, so results are bit-reproducible.  Blocks j >= nb get 0
 // (a whole row when nb = 0).
 constexpr int kDecGateThreads = 256;
 constexpr int kDecGatePer = 4096 / kDecGateThreads;  // nKB <= 4096
 
+// Workgroup L runs on XCD L % 8 (workgroups are dealt round-robin).  This maps
+// L to an item so that XCD x gets the contiguous items x q + min(x, r) ..
+// (q = N / 8, r = N % 8), a bijection of [0, N): the query heads of one KV
+// group, which read the same gate keys, then share an XCD and its L2.
+__device__ __forceinline__ int xcd_contiguous_item(int L, int N) {
+  const int q = N / 8, r = N % 8, x = L % 8, k = L / 8;
+  return x * q + min(x, r) + k;
+}
+
+// v read from another lane of its 16-lane row by a DPP control (all lanes active).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 struct DecGateShared {
   float red[kDecGateThreads / 64];
-  float xs[128];
+  float xs[kDecGateThreads];  // the token, D <= 128 entries used
 };
 
 // The probabilities of a row with nb > 0 into x[u] (block j = tid + 256 u; 0 for
-// j >= nb).  Called by the whole workgroup.
+// j >= nb).  Called by the whole workgroup; lrow (LDS, >= nb floats) holds the
+// logits on the way.  The logits are read with eight lanes per gate key, each
+// lane taking every eighth 16-byte chunk of it, so one wave load covers eight
+// whole rows; a lane sums its chunks in order and the eight partial sums are
+// then added pairwise ((l0 + l1) + (l2 + l3)) + ((l4 + l5) + (l6 + l7)).
 template <int DG>
 __device__ __forceinline__ void decode_gate_probs(
     const __bf16* __restrict__ q, const float* __restrict__ wq, float rope_base, int D,
     const float* __restrict__ kt, int bh, int h, int kvrow, int nb, int nkb, float scale,
-    float* qs, float (*part)[2][DG / 2], DecGateShared& sh, float (&x)[kDecGatePer]) {
+    float* qs, float (*part)[2][DG / 2], DecGateShared& sh, float* lrow,
+    float (&x)[kDecGatePer]) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  // Q~ of the token (no pooling): q Wq[h], rotated at block nb - 1, into LDS.
-  for (int d = tid; d < D; d += kDecGateThreads) sh.xs[d] = (float)q[(size_t)bh * D + d];
+  constexpr int V = DG / 32;    // 16-byte chunks per lane and key
+  constexpr int U = 48 / V;     // keys per lane and batch: 48 loads in flight
+  constexpr int kRowsPerPass = 8 * (kDecGateThreads / 64);
+  const int sub = lane & 7;
+  const int r0 = wv * 8 + (lane >> 3);
+  const float* kr = kt + (size_t)kvrow * nkb * DG;  // uniform base, 32-bit lane offsets
+  f32x4 kv[U][V];
+  auto fetch = [&](int base) {  // rows past nb - 1 re-read row nb - 1 (unused)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t j = (uint32_t)min(base + kRowsPerPass * u + r0, nb - 1);
+#pragma unroll
+      for (int t = 0; t < V; ++t)
+        kv[u][t] = *reinterpret_cast<const f32x4*>(kr + (j * DG + 32 * t + 4 * sub));
+    }
+  };
+  // Q~ of the token (no pooling): q Wq[h], rotated at block nb - 1, into LDS.  The
+  // token (D <= 128 < 256 threads) is requested first, then the first batch of gate
+  // keys, which does not depend on Q~ and loads during the projection.
+  const __bf16 qx = q[(size_t)bh * D + min(tid, D - 1)];  // in bounds, no branch
+  fetch(0);
+  sh.xs[tid] = (float)qx;  // entries D.. are not read
   __syncthreads();
   project_row<DG>(sh.xs, D, wq + (size_t)h * D * DG, part, nb - 1, rope_base, qs);
-  const float* kr = kt + (size_t)kvrow * nkb * DG;
+  f32x4 qv[V];
+#pragma unroll
+  for (int t = 0; t < V; ++t) qv[t] = *reinterpret_cast<const f32x4*>(qs + 4 * (sub + 8 * t));
+  for (int base = 0; base < nb; base += kRowsPerPass * U) {
+    if (base > 0) fetch(base);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float s = 0.f;
+#pragma unroll
+      for (int t = 0; t < V; ++t) {
+        s = fmaf(qv[t][0], kv[u][t][0], s);
+        s = fmaf(qv[t][1], kv[u][t][1], s);
+        s = fmaf(qv[t][2], kv[u][t][2], s);
+        s = fmaf(qv[t][3], kv[u][t][3], s);
+      }
+      // Sum over the 8 lanes of the key: lane pairs, then quads (DPP quad
+      // permutations), then the two quads (half-row mirror); every lane of the
+      // group ends with the same bits.
+      s += dpp_f32<0xB1>(s);   // quad_perm [1, 0, 3, 2]
+      s += dpp_f32<0x4E>(s);   // quad_perm [2, 3, 0, 1]
+      s += dpp_f32<0x141>(s);  // row_half_mirror
+      const int j = base + kRowsPerPass * u + r0;
+      if (sub == 0 && j < nb) lrow[j] = s * scale;
+    }
+  }
+  __syncthreads();
   float mx = -INFINITY;
 #pragma unroll
   for (int u = 0; u < kDecGatePer; ++u) {
     const int j = tid + kDecGateThreads * u;
     x[u] = -INFINITY;
     if (j < nb) {
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < DG; e += 4) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(kr + (size_t)j * DG + e);
-        s = fmaf(qs[e], kv[0], s);
-        s = fmaf(qs[e + 1], kv[1], s);
-        s = fmaf(qs[e + 2], kv[2], s);
-        s = fmaf(qs[e + 3], kv[3], s);
-      }
-      x[u] = s * scale;
+      x[u] = lrow[j];
       mx = fmaxf(mx, x[u]);
     }
   }
@@ -769,7 +825,8 @@ __global__ __launch_bounds__(kDecGateThreads) void gate_decode_scores_kernel(
   __shared__ __attribute__((aligned(16))) float qs[DG];
   __shared__ float part[kDecGateThreads / 64][2][DG / 2];
   __shared__ DecGateShared sh;
-  const int bh = blockIdx.x;
+  __shared__ float lrow[4096];
+  const int bh = xcd_contiguous_item(blockIdx.x, gridDim.x);  // b * Hq + h
   const int b = bh / Hq, h = bh % Hq, g = h / (Hq / Hkv);
   const int tid = threadIdx.x;
   const int len = min(max(kv_len[b], 0), Tmax);
@@ -781,7 +838,7 @@ __global__ __launch_bounds__(kDecGateThreads) void gate_decode_scores_kernel(
   }
   float x[kDecGatePer];
   decode_gate_probs<DG>(q, wq, rope_base, D, kt, bh, h, b * Hkv + g, nb, nkb, scale, qs, part,
-                        sh, x);
+                        sh, lrow, x);
 #pragma unroll
   for (int u = 0; u < kDecGatePer; ++u) {
     const int j = tid + kDecGateThreads * u;
@@ -805,7 +862,7 @@ __global__ __launch_bounds__(kDecGateThreads) void gate_decode_mask_kernel(
   __shared__ DecGateShared sh;
   __shared__ float prow[64 * NPL];
   __shared__ int hist[256];
-  const int bh = blockIdx.x;
+  const int bh = xcd_contiguous_item(blockIdx.x, gridDim.x);  // b * Hq + h
   const int b = bh / Hq, h = bh % Hq, g = h / (Hq / Hkv);
   const int tid = threadIdx.x, lane = tid & 63;
   const int len = min(max(kv_len[b], 0), Tmax);
@@ -813,7 +870,7 @@ __global__ __launch_bounds__(kDecGateThreads) void gate_decode_mask_kernel(
   if (nb > 0) {
     float x[kDecGatePer];
     decode_gate_probs<DG>(q, wq, rope_base, D, kt, bh, h, b * Hkv + g, nb, nkb, scale, qs, part,
-                          sh, x);
+                          sh, prow, x);
 #pragma unroll
     for (int u = 0; u < kDecGatePer; ++u) {
       const int j = tid + kDecGateThreads * u;
