@@ -38,8 +38,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kUnionThreads = 256;
 constexpr int kDecThreads = 256;  // four waves
 constexpr int kDecTile = 64;      // tokens per tile; each wave owns 16 of them
-constexpr int kDecTileTokensPerWg = 256;  // tokens of listed blocks per workgroup chunk
-constexpr int kMaxChunkTiles = 16;        // upper bound of kDecTileTokensPerWg / kDecTile
+// Tokens of listed blocks per workgroup chunk: the largest of these that still
+// gives each of the 256 CUs a workgroup, else the smallest (plan_decode).
+constexpr int kChunkTokens[] = {1024, 512, 256, 128};
+constexpr int kCus = 256;
+constexpr int kMaxChunkTiles = 16;  // kChunkTokens[0] / kDecTile
 constexpr int kCombineThreads = 256;
 
 // ---------------------------------------------------------------------------
@@ -409,9 +412,12 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int Tmax, int D, int list_heads, 
   p.gm = G <= 4 ? 4 : 8;
   p.umax = p.is_union ? (int)std::min<long long>((long long)G * max_k, nbmax) : max_k;
   p.lstride = p.umax;
-  p.chunk = std::max(1, kDecTileTokensPerWg / bs);
-  p.nsplit = std::max(1, (p.umax + p.chunk - 1) / p.chunk);
   const size_t groups = (size_t)B * Hkv;
+  for (int tokens : kChunkTokens) {
+    p.chunk = std::max(1, tokens / bs);
+    p.nsplit = std::max(1, (p.umax + p.chunk - 1) / p.chunk);
+    if (groups * (size_t)p.nsplit >= (size_t)kCus) break;
+  }
   size_t off = p.is_union ? align256(groups * p.umax * sizeof(int32_t)) : 0;
   p.off_ucnt = off;
   off += p.is_union ? align256(groups * sizeof(int32_t)) : 0;

@@ -948,7 +948,9 @@ def test_sparse_decode_parity(case):
 
 def test_sparse_decode_shared_equals_repeated_per_head_lists():
     """Ascending shared lists and the same lists repeated per query head go through
-    the direct and the union path; both visit the same tiles in the same order."""
+    the direct and the union path; both visit the same tiles in the same order (at
+    these sizes both grids are under one workgroup per CU, so both take the smallest
+    chunk of blocks per workgroup)."""
     dw = _decode_case(90, 3, 8, 2, 3000, 128, (3000, 1234, 65), list_heads="kv")
     q, k, v, kv_len = wl.make_decode_inputs(dw)
     idx, cnt = _decode_lists(91, dw, 20)
