@@ -129,12 +129,28 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   const int s = blockIdx.x % nsplit;
   const int bg = blockIdx.x / nsplit;
   const int b = bg / Hkv, g = bg % Hkv;
-  const int U = UNION ? lcnt[bg] : min(max(lcnt[bg], 0), lstride);
   const int e0 = s * chunk;
-  if (e0 >= U) return;  // the combine step reads only chunks below U
-  const int len = min(max(kv_len[b], 0), Tmax);
-  const int nb = len > 0 ? (len - 1) / bs + 1 : 0;
   const int32_t* lrow = list + (size_t)bg * lstride;
+  // The list count, the chunk's entries, the sequence length and the queries are
+  // requested together: none of these loads waits for another.  Entry indices
+  // are clamped into the list row; the count check comes after.
+  const int per = bs / kDecTile;  // tiles per listed block
+  const int e = e0 + lane / per, t = lane % per;
+  const int ev = lrow[min(e, lstride - 1)];
+  const int cnt_raw = lcnt[bg];
+  const int len = min(max(kv_len[b], 0), Tmax);
+  // Q^T as the MFMA B operand: lane l holds head l % 16, dims 8 (l / 16) + 32 kk.
+  const int hs = lane & 15, kg = lane >> 4;
+  bf16x8 qb[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    qb[kk] = *reinterpret_cast<const bf16x8*>(q + ((size_t)bg * G + min(hs, G - 1)) * D +
+                                              8 * kg + 32 * kk);
+  // A chunk at or past the list's end (e0 >= U) finds no tiles and writes an empty
+  // partial, which the combine step never reads; there is no early exit, so that
+  // the loads above are not held back behind the count.
+  const int U = UNION ? cnt_raw : min(max(cnt_raw, 0), lstride);
+  const int nb = len > 0 ? (len - 1) / bs + 1 : 0;
   const uint32_t all_heads = (1u << G) - 1u;
   const __bf16* kbase = kc + (size_t)bg * Tmax * D;
   const __bf16* vbase = vc + (size_t)bg * Tmax * D;
@@ -142,16 +158,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   // Wave 0 turns the chunk's entries into its list of 64-token tiles (entry
   // order, then sub-tile order), in LDS for all waves.
   if (w == 0) {
-    const int per = bs / kDecTile;  // tiles per listed block
-    const int e = e0 + lane / per, t = lane % per;
     int pos = -1;
     uint32_t mask = 0u;
     if (lane < chunk * per && e < U) {
-      const int v = lrow[e];
-      const int j = UNION ? (v & 0xFFFFFF) : v;
+      const int j = UNION ? (ev & 0xFFFFFF) : ev;
       if (j >= 0 && j < nb && j * bs + kDecTile * t < len) {
         pos = j * bs + kDecTile * t;
-        mask = UNION ? ((uint32_t)v >> 24) : all_heads;
+        mask = UNION ? ((uint32_t)ev >> 24) : all_heads;
       }
     }
     const uint64_t valid = __ballot(pos >= 0);
@@ -165,15 +178,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   }
   __syncthreads();
   const int ntiles = t_num;
-
-  // Q^T as the MFMA B operand: lane l holds head l % 16, dims 8 (l / 16) + 32 kk.
-  const int hs = lane & 15, kg = lane >> 4;
-  bf16x8 qb[KK];
+  if (hs >= G) {  // head slots past the group: zero queries
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    qb[kk] = bf16x8{};
-    if (hs < G)
-      qb[kk] = *reinterpret_cast<const bf16x8*>(q + ((size_t)bg * G + hs) * D + 8 * kg + 32 * kk);
+    for (int kk = 0; kk < KK; ++kk) qb[kk] = bf16x8{};
   }
   // P . V lane layout: dims 8 pc .. 8 pc + 7; keys pg + 4 (NR psub + i), i < NR.
   const int pc = lane % C8, pq = lane / C8;
