@@ -765,6 +765,8 @@ DEC_GATE_CASES = {
     "ragged_d64_b64": (3, 4, 2, 64, 700, (700, 1, 0), 64, 32),
     "gqa4_d128_b128": (2, 8, 2, 128, 1000, (1000, 450), 128, 64),
     "llama_40k": (2, 32, 8, 128, 40960, (40960, 12345), 64, 128),
+    "rows_1500_d64_dg32": (2, 4, 1, 64, 96000, (96000, 50001), 64, 32),  # 32 key slots per lane
+    "rows_3125_gqa4": (1, 8, 2, 128, 200000, (199999,), 64, 64),  # 64 key slots per lane
 }
 
 
