@@ -490,10 +490,18 @@ def main(argv=None) -> int:
         tcall2 = lambda: (gcall(), seer.seer_build_mask(gs, w.mode, w.threshold, w.density,
                                                         w.keep_sink, gmk, kv_idx=gidx,
                                                         kv_cnt=gcnt))
+        # The one-call path in passes of two tile rows (128 query blocks) of logits.
+        gws3 = torch.empty((seer.attn_gate_mask_pass_workspace_size(
+            w.batch, w.hq, w.hkv, w.seq, dg, 2),), dtype=torch.uint8, device=dev)
+        pcall = lambda: seer.seer_attn_gate_mask(qd, kd, wq, wk, w.mode, w.threshold, w.density,
+                                                 w.keep_sink, gmk, kv_idx=gidx, kv_cnt=gcnt,
+                                                 workspace=gws3)
         fcall()
         tcall2()
+        pcall()
         f_ms = time_calls(fcall, max(3, args.steps // 2), torch)
         t2_ms = time_calls(tcall2, max(3, args.steps // 2), torch)
+        p_ms = time_calls(pcall, max(3, args.steps // 2), torch)
         result["attn_gate"] = {
             "ms": round(g_ms, 4),
             "gate_dim": dg,
@@ -501,8 +509,11 @@ def main(argv=None) -> int:
             "algorithmic_bytes": g_bytes,
             "gate_to_lists_fused_ms": round(f_ms, 4),
             "gate_then_build_mask_ms": round(t2_ms, 4),
+            "gate_to_lists_passes_of_128_rows_ms": round(p_ms, 4),
+            "logits_workspace_bytes_one_pass_vs_passes": [
+                gws2.numel() - gws.numel(), gws3.numel() - gws.numel()],
         }
-        del wq, wk, gs, gws, gws2, gidx, gcnt
+        del wq, wk, gs, gws, gws2, gws3, gidx, gcnt
 
         # The bench workload's shape with 128-token blocks (TopK at the same density).
         w128 = wl.custom(103, w.batch, w.hq, w.hkv, w.head_dim, w.seq, mode=w.mode,

@@ -5,7 +5,8 @@ include/seer.h); this package only marshals torch tensors into that library.
 """
 
 from .binding import (BLOCK, SEER_MASK_THRESHOLD, SEER_MASK_TOPK, SeerError, load,
-                      attn_gate_decode_keys_workspace_size, attn_gate_mask_workspace_size,
+                      attn_gate_decode_keys_workspace_size, attn_gate_mask_pass_workspace_size,
+                      attn_gate_mask_workspace_size,
                       attn_gate_workspace_size, seer_attn_gate_decode_keys,
                       seer_attn_gate_decode_mask, seer_attn_gate_decode_scores,
                       seer_attn_gate_mask, seer_attn_gate_scores, seer_build_mask_decode, seer_sparse_decode,
@@ -16,7 +17,8 @@ from .binding import (BLOCK, SEER_MASK_THRESHOLD, SEER_MASK_TOPK, SeerError, loa
 
 __all__ = [
     "BLOCK", "SEER_MASK_THRESHOLD", "SEER_MASK_TOPK", "SeerError", "load",
-    "attn_gate_decode_keys_workspace_size", "attn_gate_mask_workspace_size",
+    "attn_gate_decode_keys_workspace_size", "attn_gate_mask_pass_workspace_size",
+    "attn_gate_mask_workspace_size",
     "attn_gate_workspace_size", "seer_attn_gate_decode_keys", "seer_attn_gate_decode_mask",
     "seer_attn_gate_decode_scores",
     "seer_attn_gate_mask",

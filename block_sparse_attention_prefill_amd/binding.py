@@ -26,6 +26,7 @@ EXPORTED = (
     "seer_sparse_prefill_workspace_size", "seer_sparse_prefill", "seer_sparse_prefill_block",
     "seer_pooled_attn_map_workspace_size", "seer_pooled_attn_map", "seer_pooled_target_mse",
     "seer_attn_gate_workspace_size", "seer_attn_gate_scores", "seer_attn_gate_mask_workspace_size",
+    "seer_attn_gate_mask_pass_workspace_size",
     "seer_attn_gate_mask", "seer_attn_gate_decode_keys_workspace_size", "seer_attn_gate_decode_keys",
     "seer_attn_gate_decode_scores", "seer_attn_gate_decode_mask", "seer_build_mask_decode",
     "seer_sparse_decode_workspace_size", "seer_sparse_decode",
@@ -84,6 +85,9 @@ def load() -> ctypes.CDLL:
                                           c_void, c_size, c_void]
     lib.seer_attn_gate_mask_workspace_size.restype = c_size
     lib.seer_attn_gate_mask_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
+    lib.seer_attn_gate_mask_pass_workspace_size.restype = c_size
+    lib.seer_attn_gate_mask_pass_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int,
+                                                            c_int]
     lib.seer_attn_gate_mask.restype = c_int
     lib.seer_attn_gate_mask.argtypes = [c_void, c_void, c_int, c_int, c_int, c_int, c_int,
                                         c_void, c_void, c_int, c_float, c_float, c_int, c_float,
@@ -328,16 +332,24 @@ def attn_gate_mask_workspace_size(b: int, hq: int, hkv: int, t: int, dg: int,
     return load().seer_attn_gate_mask_workspace_size(b, hq, hkv, t, dg, int(bool(with_scores)))
 
 
+def attn_gate_mask_pass_workspace_size(b: int, hq: int, hkv: int, t: int, dg: int,
+                                        pass_tiles: int) -> int:
+    return load().seer_attn_gate_mask_pass_workspace_size(b, hq, hkv, t, dg, int(pass_tiles))
+
+
 def seer_attn_gate_mask(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor, wk: torch.Tensor,
                         mode: int, threshold: float, density: float, keep_sink: bool, max_k: int,
                         scale: Optional[float] = None, rope_base: float = 10000.0,
                         return_scores: bool = False, kv_idx: Optional[torch.Tensor] = None,
                         kv_cnt: Optional[torch.Tensor] = None,
                         scores: Optional[torch.Tensor] = None,
-                        workspace: Optional[torch.Tensor] = None, stream=None):
+                        workspace: Optional[torch.Tensor] = None,
+                        pass_tiles: Optional[int] = None, stream=None):
     """AttnGate scores straight into block lists: (kv_idx [B,Hq,nQB,max_k], kv_cnt
     [B,Hq,nQB], scores [B,Hq,nQB,nQB] or None).  Scores are written only when
-    return_scores is set or a scores buffer is passed."""
+    return_scores is set or a scores buffer is passed.  Without scores, pass_tiles
+    sizes the allocated workspace for passes of that many 64-block tile rows
+    (memory linear in T); the lists are the same."""
     lib = load()
     b, hq, hkv, t, d = _qkv_dims(q, k, k)
     dg = wq.shape[-1]
@@ -354,7 +366,10 @@ def seer_attn_gate_mask(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor, wk: 
         kv_cnt = torch.empty((b, hq, nqb), dtype=torch.int32, device=q.device)
     _need(kv_idx, "kv_idx", torch.int32, (b, hq, nqb, max_k))
     _need(kv_cnt, "kv_cnt", torch.int32, (b, hq, nqb))
-    need = lib.seer_attn_gate_mask_workspace_size(b, hq, hkv, t, dg, int(scores is not None))
+    if scores is None and pass_tiles is not None:
+        need = lib.seer_attn_gate_mask_pass_workspace_size(b, hq, hkv, t, dg, int(pass_tiles))
+    else:
+        need = lib.seer_attn_gate_mask_workspace_size(b, hq, hkv, t, dg, int(scores is not None))
     if workspace is None:
         workspace = _workspace(need, q.device)
     sc = (1.0 / dg ** 0.5) if scale is None else float(scale)

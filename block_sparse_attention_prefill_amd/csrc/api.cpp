@@ -5,6 +5,8 @@
 #include <math.h>
 #include <limits.h>
 
+#include <algorithm>
+
 #include "seer_internal.h"
 
 namespace {
@@ -194,6 +196,15 @@ size_t seer_attn_gate_mask_workspace_size(int B, int Hq, int Hkv, int T, int Dg,
   return gate + (with_scores ? 0 : (size_t)B * Hq * nqb * nqb * sizeof(float));
 }
 
+size_t seer_attn_gate_mask_pass_workspace_size(int B, int Hq, int Hkv, int T, int Dg,
+                                               int pass_tiles) {
+  const size_t gate = seer_attn_gate_workspace_size(B, Hq, Hkv, T, Dg);
+  if (gate == 0 || pass_tiles < 1) return 0;
+  const size_t nqb = (size_t)nqb_of(T);
+  const size_t rows = std::min(nqb, (size_t)64 * (size_t)pass_tiles);
+  return gate + (size_t)B * Hq * rows * nqb * sizeof(float);
+}
+
 int seer_attn_gate_mask(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
                         const float* wq, const float* wk, int Dg, float scale, float rope_base,
                         int mode, float threshold, double density, int keep_sink,
@@ -221,12 +232,23 @@ int seer_attn_gate_mask(const void* q, const void* k, int B, int Hq, int Hkv, in
     const int forced = (keep_sink && nQB > 1) ? 2 : 1;
     if (max_k < forced) return SEER_ERR_CAPACITY;
   }
-  const size_t need = seer_attn_gate_mask_workspace_size(B, Hq, Hkv, T, Dg, scores ? 1 : 0);
-  if (!workspace || workspace_bytes < need || !aligned256(workspace)) return SEER_ERR_WORKSPACE;
+  // Without scores the logits take what the workspace holds past the gate's own
+  // part: all nQB rows per head (one pass), else whole tile rows of 64 (passes).
+  const size_t gate = seer_attn_gate_workspace_size(B, Hq, Hkv, T, Dg);
+  if (!workspace || workspace_bytes < gate || !aligned256(workspace)) return SEER_ERR_WORKSPACE;
+  // Counted from the gate's full size (the logits start at or below it), so the
+  // passes match seer_attn_gate_mask_pass_workspace_size exactly.
+  int pass_rows = nQB;
+  if (!scores) {
+    const size_t row_bytes = (size_t)B * Hq * nQB * sizeof(float);
+    const size_t fit = (workspace_bytes - gate) / row_bytes;
+    if (fit < (size_t)nQB) pass_rows = (int)(fit / 64 * 64);
+    if (pass_rows < 1) return SEER_ERR_WORKSPACE;
+  }
   const hipError_t err = seer::launch_attn_gate_mask(
       q, k, B, Hq, Hkv, T, D, wq, wk, Dg, scale, rope_base, mode, threshold, density,
       keep_sink ? 1 : 0, kv_idx, kv_cnt, max_k, scores, static_cast<float*>(workspace),
-      (hipStream_t)stream);
+      pass_rows, (hipStream_t)stream);
   return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
 }
 

@@ -276,11 +276,15 @@ __global__ __launch_bounds__(64 * kProjWaves) void gate_project_kernel(
 // loads in flight during the first half's MFMAs (half the LDS: more
 // workgroups per CU).
 // Writes the scaled logits (-inf above the diagonal) and, per row, the tile's
-// max and sum of exp(logit - max).
+// max and sum of exp(logit - max).  One launch covers the tile rows it0 ..
+// it0 + (tile rows of npairs pairs) - 1; row i of head bh goes to row
+// bh R + i - 64 it0 of `scores` (R rows per head: the whole map when R = nQB
+// and it0 = 0, else one pass's rows), the pairs to the full-size `part`.
 template <int DG>
 __global__ __launch_bounds__(kScoreThreads) void gate_logits_kernel(
     const float* __restrict__ qt, const float* __restrict__ kt, int Hq, int Hkv, int nqb,
-    float scale, float* __restrict__ scores, float2* __restrict__ part) {
+    float scale, int it0, int npairs, int R, float* __restrict__ scores,
+    float2* __restrict__ part) {
   constexpr int DH = DG / 2;  // dims per half: the tiles go through LDS in two halves
   constexpr int kHalfTile = kTile * (DH + 4);
   constexpr int kSmem = 2 * kHalfTile > kTile * (kTile + 1) ? 2 * kHalfTile : kTile * (kTile + 1);
@@ -290,10 +294,9 @@ __global__ __launch_bounds__(kScoreThreads) void gate_logits_kernel(
   float (*ks)[DH + 4] = reinterpret_cast<float (*)[DH + 4]>(smem + kHalfTile);
   const int tid = threadIdx.x;
   const int ntiles = (nqb + kTile - 1) / kTile;
-  const int npairs = ntiles * (ntiles + 1) / 2;
-  const int pair = blockIdx.x % npairs;
+  const int pair = it0 * (it0 + 1) / 2 + (int)(blockIdx.x % npairs);
   const int bh = blockIdx.x / npairs;  // b * Hq + h
-  int it = 0;
+  int it = it0;
   while ((it + 1) * (it + 2) / 2 <= pair) ++it;
   const int jt = pair - it * (it + 1) / 2;
   const int b = bh / Hq;
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(kScoreThreads) void gate_logits_kernel(
   l += __shfl_xor(l, 1, 64);
   l += __shfl_xor(l, 2, 64);
   if (i < nqb) {
-    float* srow = scores + ((size_t)bh * nqb + i) * nqb + j0 + 16 * qq;
+    float* srow = scores + ((size_t)bh * R + (i - kTile * it0)) * nqb + j0 + 16 * qq;
     if (j0 + 16 * qq + 16 <= nqb && (reinterpret_cast<uintptr_t>(srow) & 15) == 0) {
 #pragma unroll
       for (int c = 0; c < 16; c += 4)
@@ -449,22 +452,26 @@ __global__ __launch_bounds__(64 * kRowWaves) void gate_softmax_kernel(
 // The probabilities are those of gate_softmax_kernel, bit for bit, and the
 // lists those seer_build_mask makes from them (same keys, same count rule,
 // same select); with write_scores the probabilities also go back to the row.
+// A launch takes the rows row0 .. row0 + Rv - 1 of every head (rows = B Hq Rv),
+// their logits at row bh R + i - row0 of `logits` (R >= Rv rows per head).
 template <int NPL>
 __global__ __launch_bounds__(64 * kRowWaves) void gate_softmax_mask_kernel(
-    int rows, int nqb, float* __restrict__ logits, int write_scores,
+    int rows, int nqb, int row0, int Rv, int R, float* __restrict__ logits, int write_scores,
     const float2* __restrict__ part, int mode, float tau, double density, int keep_sink,
     int32_t* __restrict__ idx, int32_t* __restrict__ cnt, int max_k) {
   __shared__ int hist_all[kRowWaves][256];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int row = blockIdx.x * kRowWaves + wv;
-  if (row >= rows) return;
-  const int i = row % nqb;
+  const int prow = blockIdx.x * kRowWaves + wv;  // row of this pass
+  if (prow >= rows) return;
+  const int bh = prow / Rv, il = prow % Rv;
+  const int i = row0 + il;
+  const int row = bh * nqb + i;  // B Hq nQB < 2^31 (checked by the host layer)
   const int n = i + 1;
   const int ntiles = (nqb + kTile - 1) / kTile;
   const int it = i / kTile;
   const float2* pr = part + (size_t)row * ntiles;
-  float* sr = logits + (size_t)row * nqb;
+  float* sr = logits + ((size_t)bh * R + il) * nqb;
   float2 mine = lane <= it ? pr[lane] : make_float2(-INFINITY, 0.f);
   float x[NPL];
 #pragma unroll
@@ -930,12 +937,12 @@ size_t attn_gate_workspace_floats(int B, int Hq, int Hkv, int nqb, int dg) {
 
 namespace {
 
-// Pooling, linear layers + block RoPE, and the causal logit tiles with their
-// per-row (max, sum) pairs.  The scaled logits go to `logits` [B,Hq,nQB,nQB]
-// (causal tiles only); *part_out points at the pairs in the workspace.
+// Pooling and the linear layers + block RoPE (Q~ and K~ at the start of ws);
+// *part_out points at the room for the per-row (max, sum) pairs of the logit
+// tiles in the workspace.
 hipError_t gate_front(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
-                      const float* wq, const float* wk, int dg, float scale, float rope_base,
-                      float* logits, float* ws, float2** part_out, hipStream_t stream) {
+                      const float* wq, const float* wk, int dg, float rope_base, float* ws,
+                      float2** part_out, hipStream_t stream) {
   const int nqb = (T + kTile - 1) / kTile;
   float* qt = ws;
   float* kt = ws + (size_t)B * Hq * nqb * dg;
@@ -963,18 +970,26 @@ hipError_t gate_front(const void* q, const void* k, int B, int Hq, int Hkv, int 
 #undef SEER_GATE_PROJECT
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int ntiles = (nqb + kTile - 1) / kTile;
-  const int npairs = ntiles * (ntiles + 1) / 2;
-  float2* part = reinterpret_cast<float2*>(kt + (size_t)B * Hkv * nqb * dg);
+  *part_out = reinterpret_cast<float2*>(kt + (size_t)B * Hkv * nqb * dg);
+  return hipSuccess;
+}
+
+// The logit tiles of tile rows it0 .. it1 - 1 (R logit rows per head in
+// `logits`, see gate_logits_kernel) and their per-row (max, sum) pairs.
+hipError_t gate_logits(int B, int Hq, int Hkv, int nqb, int dg, float scale, const float* ws,
+                       int it0, int it1, int R, float* logits, float2* part,
+                       hipStream_t stream) {
+  const float* qt = ws;
+  const float* kt = ws + (size_t)B * Hq * nqb * dg;
+  const int npairs = it1 * (it1 + 1) / 2 - it0 * (it0 + 1) / 2;
   const dim3 lgrid((unsigned)((size_t)B * Hq * npairs));
 #define SEER_GATE_LOGITS(DG)                                                                   \
   hipLaunchKernelGGL(gate_logits_kernel<DG>, lgrid, dim3(kScoreThreads), 0, stream, qt, kt,    \
-                     Hq, Hkv, nqb, scale, logits, part)
+                     Hq, Hkv, nqb, scale, it0, npairs, R, logits, part)
   if (dg == 128) SEER_GATE_LOGITS(128);
   else if (dg == 64) SEER_GATE_LOGITS(64);
   else SEER_GATE_LOGITS(32);
 #undef SEER_GATE_LOGITS
-  *part_out = part;
   return hipGetLastError();
 }
 
@@ -986,8 +1001,10 @@ hipError_t launch_attn_gate(const void* q, const void* k, int B, int Hq, int Hkv
   const int nqb = (T + kTile - 1) / kTile;
   if ((size_t)B * Hq * nqb == 0) return hipSuccess;
   float2* part = nullptr;
-  const hipError_t err = gate_front(q, k, B, Hq, Hkv, T, D, wq, wk, dg, scale, rope_base, scores,
-                                    ws, &part, stream);
+  hipError_t err = gate_front(q, k, B, Hq, Hkv, T, D, wq, wk, dg, rope_base, ws, &part, stream);
+  if (err != hipSuccess) return err;
+  const int ntiles = (nqb + kTile - 1) / kTile;
+  err = gate_logits(B, Hq, Hkv, nqb, dg, scale, ws, 0, ntiles, nqb, scores, part, stream);
   if (err != hipSuccess) return err;
   const int rows = B * Hq * nqb;  // < 2^31: the host layer checks B (Hq + Hkv) nQB
   hipLaunchKernelGGL(gate_softmax_kernel, dim3((unsigned)((rows + kRowWaves - 1) / kRowWaves)),
@@ -999,34 +1016,45 @@ hipError_t launch_attn_gate_mask(const void* q, const void* k, int B, int Hq, in
                                  int D, const float* wq, const float* wk, int dg, float scale,
                                  float rope_base, int mode, float threshold, double density,
                                  int keep_sink, int32_t* idx, int32_t* cnt, int max_k,
-                                 float* scores, float* ws, hipStream_t stream) {
+                                 float* scores, float* ws, int pass_rows, hipStream_t stream) {
   const int nqb = (T + kTile - 1) / kTile;
   if ((size_t)B * Hq * nqb == 0) return hipSuccess;
   // Without a scores buffer the logits live past the gate's own workspace, at
   // the next 256-byte boundary (within the 256 bytes of slack the workspace
-  // size adds).
+  // size adds), pass_rows rows per head at a time.
   const size_t off = (attn_gate_workspace_floats(B, Hq, Hkv, nqb, dg) + 63) & ~(size_t)63;
+  const int R = scores ? nqb : pass_rows;  // logit rows per head per pass
   float* logits = scores ? scores : ws + off;
   float2* part = nullptr;
-  hipError_t err = gate_front(q, k, B, Hq, Hkv, T, D, wq, wk, dg, scale, rope_base, logits, ws,
-                              &part, stream);
+  hipError_t err = gate_front(q, k, B, Hq, Hkv, T, D, wq, wk, dg, rope_base, ws, &part, stream);
   if (err != hipSuccess) return err;
-  const int rows = B * Hq * nqb;
-  const dim3 grid((unsigned)((rows + kRowWaves - 1) / kRowWaves));
+  const int ntiles = (nqb + kTile - 1) / kTile;
+  const int tiles_per_pass = R >= nqb ? ntiles : R / kTile;
   const int ws_flag = scores ? 1 : 0;
+  for (int it0 = 0; it0 < ntiles; it0 += tiles_per_pass) {
+    const int it1 = min(it0 + tiles_per_pass, ntiles);
+    err = gate_logits(B, Hq, Hkv, nqb, dg, scale, ws, it0, it1, R, logits, part, stream);
+    if (err != hipSuccess) return err;
+    const int row0 = kTile * it0;
+    const int Rv = min(kTile * it1, nqb) - row0;  // rows of this pass, per head
+    const int rows = B * Hq * Rv;
+    const dim3 grid((unsigned)((rows + kRowWaves - 1) / kRowWaves));
 #define SEER_GATE_MASK(NPL)                                                                    \
   hipLaunchKernelGGL(gate_softmax_mask_kernel<NPL>, grid, dim3(64 * kRowWaves), 0, stream, rows, \
-                     nqb, logits, ws_flag, part, mode, threshold, density, keep_sink, idx, cnt,  \
-                     max_k)
-  if (nqb <= 64) SEER_GATE_MASK(1);
-  else if (nqb <= 64 * 4) SEER_GATE_MASK(4);
-  else if (nqb <= 64 * 8) SEER_GATE_MASK(8);
-  else if (nqb <= 64 * 16) SEER_GATE_MASK(16);
-  else if (nqb <= 64 * 32) SEER_GATE_MASK(32);
-  else if (nqb <= 64 * 64) SEER_GATE_MASK(64);
-  else return hipErrorInvalidValue;  // the host layer rejects nQB > 4096 first
+                     nqb, row0, Rv, R, logits, ws_flag, part, mode, threshold, density,          \
+                     keep_sink, idx, cnt, max_k)
+    if (nqb <= 64) SEER_GATE_MASK(1);
+    else if (nqb <= 64 * 4) SEER_GATE_MASK(4);
+    else if (nqb <= 64 * 8) SEER_GATE_MASK(8);
+    else if (nqb <= 64 * 16) SEER_GATE_MASK(16);
+    else if (nqb <= 64 * 32) SEER_GATE_MASK(32);
+    else if (nqb <= 64 * 64) SEER_GATE_MASK(64);
+    else return hipErrorInvalidValue;  // the host layer rejects nQB > 4096 first
 #undef SEER_GATE_MASK
-  return hipGetLastError();
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 // Decode gate keys workspace (fp32): the pooled cache K [B,Hkv,nKB,2D].

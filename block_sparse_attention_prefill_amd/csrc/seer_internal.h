@@ -53,13 +53,15 @@ hipError_t launch_attn_gate(const void* q, const void* k, int B, int Hq, int Hkv
 
 // Gate scores and block lists in one pass over the logits (nqb <= 4096, checked
 // by the caller).  scores may be null: the logits then live in ws from the
-// first 64-float boundary past attn_gate_workspace_floats(), B*Hq*nqb*nqb
-// more floats.
+// first 64-float boundary past attn_gate_workspace_floats(), pass_rows rows of
+// nqb floats per head (B*Hq*pass_rows*nqb floats), and the rows are produced
+// and selected in passes of pass_rows query blocks; pass_rows is nqb (one pass)
+// or a multiple of 64 below it.  Ignored when scores is given.
 hipError_t launch_attn_gate_mask(const void* q, const void* k, int B, int Hq, int Hkv, int T,
                                  int D, const float* wq, const float* wk, int dg, float scale,
                                  float rope_base, int mode, float threshold, double density,
                                  int keep_sink, int32_t* idx, int32_t* cnt, int max_k,
-                                 float* scores, float* ws, hipStream_t stream);
+                                 float* scores, float* ws, int pass_rows, hipStream_t stream);
 
 // Per-token decode gate (block 64 or 128, nKB = ceil(Tmax / block) <= 4096 and
 // B * max(Hq, Hkv) * nKB < 2^31, checked by the caller).  Keys: kt [B,Hkv,nKB,Dg]

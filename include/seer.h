@@ -218,6 +218,19 @@ int seer_attn_gate_scores(const void* q, const void* k, int B, int Hq, int Hkv, 
 size_t seer_attn_gate_mask_workspace_size(int B, int Hq, int Hkv, int T, int Dg,
                                           int with_scores);
 
+/* Bytes of device workspace for seer_attn_gate_mask without a scores buffer
+ * when the logits are produced and selected in passes of pass_tiles tile rows
+ * (64 query blocks each) instead of all at once: that of seer_attn_gate_scores
+ * plus B * Hq * min(nQB, 64 pass_tiles) * nQB fp32, so the logits take memory
+ * linear in T for a fixed pass.  This is the tiling the rebuttal "SeerAttention:
+ * Learning Intrinsic Sparse Attention in Your LLMs" suggests for the gate when
+ * its quadratic output is too large ("Weakness 2 (Memory complexity)"): the
+ * gate is computed tile by tile like FlashAttention and each row is selected
+ * as soon as its tiles are done (a whole row fits on chip, so no local TopK
+ * and merge are needed).  0 for invalid sizes or pass_tiles < 1. */
+size_t seer_attn_gate_mask_pass_workspace_size(int B, int Hq, int Hkv, int T, int Dg,
+                                               int pass_tiles);
+
 /*
  * AttnGate scores and the block mask in one call: the gate's scores, as
  * seer_attn_gate_scores defines them, go straight into the per-row threshold
@@ -237,8 +250,13 @@ size_t seer_attn_gate_mask_workspace_size(int B, int Hq, int Hkv, int T, int Dg,
  *          capacity rules (SEER_ERR_CAPACITY).
  * scores   device fp32 out [B, Hq, nQB, nQB] (the scores, as
  *          seer_attn_gate_scores writes them), or NULL.
- * workspace device, >= seer_attn_gate_mask_workspace_size(B, Hq, Hkv, T, Dg,
- *          scores != NULL) bytes, 256-byte aligned; overwritten.
+ * workspace device, 256-byte aligned, overwritten.  With scores: >=
+ *          seer_attn_gate_mask_workspace_size(B, Hq, Hkv, T, Dg, 1) bytes.
+ *          Without: >= seer_attn_gate_mask_pass_workspace_size(B, Hq, Hkv, T,
+ *          Dg, 1) bytes; the call then runs as many tile rows per pass as the
+ *          workspace holds (one pass from
+ *          seer_attn_gate_mask_workspace_size(..., 0) bytes on).  The lists do
+ *          not depend on the number of passes.  Too small: SEER_ERR_WORKSPACE.
  */
 int seer_attn_gate_mask(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
                         const float* wq, const float* wk, int Dg, float scale, float rope_base,

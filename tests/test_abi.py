@@ -65,6 +65,17 @@ def test_workspace_sizes():
     assert with_s == seer.attn_gate_workspace_size(1, 32, 8, 32768, 128)
     assert without == with_s + 32 * 512 * 512 * 4
     assert seer.attn_gate_mask_workspace_size(1, 32, 7, 32768, 128, True) == 0
+    # passes of tile rows: one row of tiles is 64 logit rows of nQB per head
+    one = seer.attn_gate_mask_pass_workspace_size(1, 32, 8, 32768, 128, 1)
+    assert one == with_s + 32 * 64 * 512 * 4
+    assert seer.attn_gate_mask_pass_workspace_size(1, 32, 8, 32768, 128, 3) == \
+        with_s + 32 * 192 * 512 * 4
+    assert seer.attn_gate_mask_pass_workspace_size(1, 32, 8, 32768, 128, 8) == without
+    assert seer.attn_gate_mask_pass_workspace_size(1, 32, 8, 32768, 128, 1000) == without
+    assert seer.attn_gate_mask_pass_workspace_size(1, 32, 8, 32768, 128, 0) == 0
+    # a ragged T: the last tile row holds fewer than 64 rows
+    assert seer.attn_gate_mask_pass_workspace_size(1, 4, 2, 64 * 100, 64, 2) == \
+        seer.attn_gate_mask_workspace_size(1, 4, 2, 64 * 100, 64, False)
 
 
 FAKE = 1 << 20  # never dereferenced: every call below fails its host checks first
@@ -198,6 +209,13 @@ def test_attn_gate_mask_rejects_on_host():
     assert call(p16=None) == 1         # lists
     assert call(p7=None) == 1          # weights
     assert call(p2=0) == 0             # empty
+    # without scores the workspace must hold at least one tile row of logits
+    gate = seer.attn_gate_workspace_size(1, 4, 2, 256, 64)
+    one = seer.attn_gate_mask_pass_workspace_size(1, 4, 2, 256, 64, 1)
+    assert one > gate
+    assert call(p19=None, p21=gate) == 4
+    assert call(p19=None, p21=one - 1) == 4
+    assert call(p21=gate - 1) == 4     # with scores the gate's own part is the minimum
 
 
 def test_attn_gate_decode_rejects_on_host():

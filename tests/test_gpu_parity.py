@@ -665,7 +665,8 @@ def test_attn_gate_to_topk_lists():
 @pytest.mark.parametrize("mode", [wl.MODE_TOPK, wl.MODE_THRESHOLD])
 def test_attn_gate_mask_equals_scores_then_mask(case, mode):
     """The fused call returns, bit for bit, the scores of seer_attn_gate_scores and
-    the lists seer_build_mask makes from them, with and without a scores buffer."""
+    the lists seer_build_mask makes from them, with and without a scores buffer, and
+    with the logits produced in passes over tile rows."""
     w, dg = _gate_case(case)
     announce(f"attn gate mask {w.name} dg={dg} mode={mode}")
     q, k, _ = (_dev(t) for t in wl.make_qkv(w))
@@ -682,6 +683,13 @@ def test_attn_gate_mask_equals_scores_then_mask(case, mode):
     assert torch.equal(gs, s)
     assert torch.equal(gc, rc) and torch.equal(gi, ri)
     assert torch.equal(nc, rc) and torch.equal(ni, ri)
+    # The logits in passes of 1 and 3 tile rows (64 query blocks each) from a
+    # workspace sized for that: the same lists.
+    for pt in (1, 3):
+        pi, pc, _ = seer.seer_attn_gate_mask(q, k, wq, wk, mode, thr, density, True, max_k,
+                                             pass_tiles=pt)
+        torch.cuda.synchronize()
+        assert torch.equal(pc, rc) and torch.equal(pi, ri), pt
     if mode == wl.MODE_THRESHOLD:
         announce(f"threshold lists: mean length {float(rc.float().mean()):.2f}, "
                  f"rows at max_k {int((rc == max_k).sum())}")
