@@ -261,6 +261,48 @@ def test_sparse_prefill_shapes_and_lists(b, hq, hkv, t, d, mode):
     assert err <= O_TOL
 
 
+def _sweep_workload(seed):
+    """A seeded random shape and mask rule (ragged T, GQA 1-5, D 64/128, 64- or
+    128-token blocks, TopK or threshold, with or without the sink)."""
+    rng = np.random.default_rng(5000 + seed)
+    hkv = int(rng.integers(1, 4))
+    g = int(rng.choice([1, 2, 4, 5]))
+    topk = bool(rng.integers(0, 2))
+    return wl.custom(
+        200 + seed, int(rng.integers(1, 3)), hkv * g, hkv, int(rng.choice([64, 128])),
+        int(rng.integers(1, 2600)), mode=wl.MODE_TOPK if topk else wl.MODE_THRESHOLD,
+        density=float(rng.uniform(0.05, 0.6)), threshold=float(rng.uniform(0.02, 0.2)),
+        keep_sink=bool(rng.integers(0, 2)),
+        scores=str(rng.choice(["uniform", "local_stripe", "softmax_normal"])),
+        qkv_scale=float(rng.choice([1.0, 0.25])), block=int(rng.choice([64, 128])))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_mask_and_prefill_seeded_sweep(seed):
+    """Seeded random shapes through the GPU mask build and the sparse pass: lists bit
+    for bit against the oracle's, every query block's output against the oracle."""
+    w = _sweep_workload(seed)
+    announce(f"sweep {seed}: b={w.batch} hq={w.hq} hkv={w.hkv} d={w.head_dim} t={w.seq} "
+             f"block={w.block} mode={w.mode} dens={w.density:.2f} thr={w.threshold:.3f} "
+             f"sink={w.keep_sink} scores={w.scores}")
+    q, k, v = wl.make_qkv(w)
+    s = wl.make_scores(w)
+    if w.mode == wl.MODE_TOPK:
+        max_k = seer.topk_budget(w.nqb, w.density, w.keep_sink)
+    else:
+        max_k = max(2, w.nqb // 2)  # threshold rows longer than this keep their best
+    idx, cnt = seer.seer_build_mask(_dev(s), w.mode, w.threshold, w.density, w.keep_sink, max_k)
+    o = seer.seer_sparse_prefill_block(_dev(q), _dev(k), _dev(v), idx, cnt, w.block)
+    torch.cuda.synchronize()
+    o, idx, cnt = o.cpu(), idx.cpu().numpy(), cnt.cpu().numpy()
+    ref_idx, ref_cnt = oracle.build_mask_ref(s.numpy(), w.mode, w.threshold, w.density,
+                                             w.keep_sink, max_k)
+    assert (cnt == ref_cnt).all() and (idx == ref_idx).all()
+    blocks = [(b, h, i) for b in range(w.batch) for h in range(w.hq) for i in range(w.nqb)]
+    ref = oracle.sparse_attention_blocks_ref(q, k, v, idx, cnt, None, blocks, w.block)
+    _check_blocks(o, ref, O_TOL, f"sweep {seed}", w.block)
+
+
 def test_sparse_density_one_matches_dense_causal():
     """Lists holding every causal block: the sparse kernel must reproduce dense
     causal attention (the oracle at density 1 is pinned to SDPA)."""
