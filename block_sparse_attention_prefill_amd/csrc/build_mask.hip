@@ -59,6 +59,14 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
   const float* srow = scores + row * (long long)nkb;
   int32_t* out = idx + row * (long long)max_k;
 
+  // All of the row's loads are issued before any is used (a load under the
+  // per-candidate branch would be waited for one at a time); slots past the
+  // diagonal re-read entry i, so no entry j > i is ever read.
+  float sv[NPL];
+  if (n > 0) {
+#pragma unroll
+    for (int c = 0; c < NPL; ++c) sv[c] = srow[min(64 * c + lane, i)];
+  }
   uint32_t key[NPL];
   int npos = 0;
 #pragma unroll
@@ -69,7 +77,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
       if (j == i || (keep_sink && j == 0)) {
         kj = 0xFFFFFFFFu;
       } else {
-        const float s = srow[j];
+        const float s = sv[c];
         kj = (mode == 1 || s >= tau) ? order_key(s) : 0u;
       }
     }
