@@ -141,22 +141,40 @@ __global__ __launch_bounds__(64 * kWaves) void pooled_target_reg_kernel(
   const float* g = gate ? gate + row * (long long)nqb : nullptr;
   const float4 zero = {0.f, 0.f, 0.f, 0.f};
   float4 x[NC], y[NC];
+  // Every load is issued before any is used and none sits under a per-lane
+  // branch (each would be waited for on its own): chunks past the last full
+  // one re-read it, the partial chunk's entries are re-read from entries <= i,
+  // and selects drop what is not the row's.  No entry j > i is read.
+  const float4* a4 = reinterpret_cast<const float4*>(a);
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  const int clast = max(full - 1, 0);
+  float4 xl[NC], yl[NC];
+  if (full > 0) {
+#pragma unroll
+    for (int u = 0; u < NC; ++u) xl[u] = a4[min(lane + 64 * u, clast)];
+    if (g) {
+#pragma unroll
+      for (int u = 0; u < NC; ++u) yl[u] = g4[min(lane + 64 * u, clast)];
+    }
+  }
+  float xr[3], yr[3] = {0.f, 0.f, 0.f};  // entries 4 full + k of the partial chunk
+#pragma unroll
+  for (int k = 0; k < 3; ++k) xr[k] = a[min(4 * full + k, i)];
+  if (g) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) yr[k] = g[min(4 * full + k, i)];
+  }
 #pragma unroll
   for (int u = 0; u < NC; ++u) {
     const int c = lane + 64 * u;
     x[u] = zero;
     y[u] = zero;
     if (c < full) {
-      x[u] = reinterpret_cast<const float4*>(a)[c];
-      if (g) y[u] = reinterpret_cast<const float4*>(g)[c];
+      x[u] = xl[u];
+      if (g) y[u] = yl[u];
     } else if (c == full && rem) {
-      float xa[4] = {0.f, 0.f, 0.f, 0.f}, ya[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int k = 0; k < rem; ++k) {
-        xa[k] = a[4 * c + k];
-        if (g) ya[k] = g[4 * c + k];
-      }
-      x[u] = {xa[0], xa[1], xa[2], xa[3]};
-      y[u] = {ya[0], ya[1], ya[2], ya[3]};
+      x[u] = {xr[0], rem > 1 ? xr[1] : 0.f, rem > 2 ? xr[2] : 0.f, 0.f};
+      y[u] = {yr[0], rem > 1 ? yr[1] : 0.f, rem > 2 ? yr[2] : 0.f, 0.f};
     }
   }
   float s = 0.f;
