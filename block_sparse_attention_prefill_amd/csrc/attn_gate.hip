@@ -10,7 +10,7 @@
 // are a softmax ("Question 2: (Row-Normalization of Max-Pooled Attention
 // Map)").  Threshold or TopK on these scores (seer_build_mask) gives the mask.
 //
-// Four kernels:
+// Prefill kernels:
 // * gate_pool_kernel: one wave per (batch, head, 64-token block) pools the block
 //   (non-temporal 16-byte loads all in flight, lane shuffles to combine).
 // * gate_project_kernel: one workgroup per (batch, head, 64 blocks) applies the
@@ -22,6 +22,13 @@
 //   tile max and sum of exponentials; gate_softmax_kernel
 //   then combines a row's partials in a fixed order and normalises the row in
 //   place, zeros above the diagonal.
+// * gate_softmax_mask_kernel: the same softmax straight into the row selection of
+//   the mask build (mask_select.h); with a small workspace the logits are made
+//   and selected in passes over tile rows.
+// Decode kernels (one new token per sequence): gate_decode_pool_kernel and
+// gate_project_kernel for the gate keys of every cache block,
+// gate_decode_last_key_kernel for the block a token joins, gate_decode_scores_kernel
+// and gate_decode_mask_kernel for the token's scores (and its block lists).
 #include "mask_select.h"
 
 #include <math.h>
@@ -518,7 +525,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void gate_softmax_mask_kernel(
 // of the cache exactly as above but up to each sequence's own length, and the
 // pooled rows go through gate_project_kernel (K slots only) -- or, to refresh
 // only each sequence's last block (the one a new token joins), one row per
-// (sequence, KV head) through gate_decode_row_kernel.  Scores: the token's q
+// (sequence, KV head) through gate_decode_last_key_kernel.  Scores: the token's q
 // through the Q layer and the rotation at its block index nb - 1, then one
 // workgroup per (sequence, query head) takes the logits over the sequence's
 // blocks and their softmax.
