@@ -11,7 +11,8 @@
 //   list when its query heads share one, else the union of the heads' lists
 //   with a mask of the heads that chose each block (decode_union_kernel), so a
 //   block is read once for the whole group.
-// * decode_attn_kernel splits that list into chunks of a few blocks.  Its
+// * decode_attn_kernel splits that list into chunks of 128 to 1024 listed
+//   tokens, the longest that still gives every CU a workgroup.  Its
 //   workgroup streams the chunk's 64-token tiles (next tile's loads in flight
 //   while the current one is used); each of the four waves owns 16 keys of
 //   every tile and keeps its own online-softmax state, so the loop needs no
