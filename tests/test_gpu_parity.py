@@ -998,6 +998,49 @@ def test_sparse_decode_parity(case):
             assert (got[b] == 0).all()
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_seeded_sweep(seed):
+    """Seeded random decode steps (ragged lengths including empty and one-token
+    sequences, GQA 1-8, D 64/128, 64- or 128-token blocks, lists per query head or
+    per KV head, TopK budgets or thresholds): GPU lists from the decode scores bit
+    for bit against the oracle's, outputs against the oracle."""
+    rng = np.random.default_rng(7000 + seed)
+    hkv = int(rng.integers(1, 4))
+    g = int(rng.choice([1, 2, 4, 5, 8]))
+    b = int(rng.integers(1, 5))
+    tmax = int(rng.integers(1, 3000))
+    lens = [int(x) for x in rng.integers(0, tmax + 1, size=b)]
+    lens[0] = tmax
+    if b > 1:
+        lens[1] = int(rng.choice([0, 1, tmax]))
+    block = int(rng.choice([64, 128]))
+    dw = _decode_case(300 + seed, b, hkv * g, hkv, tmax, int(rng.choice([64, 128])), lens,
+                      block=block, list_heads=str(rng.choice(["q", "kv"])),
+                      budget_tokens=block * int(rng.integers(1, 12)),
+                      keep_sink=bool(rng.integers(0, 2)))
+    mode = wl.MODE_TOPK if rng.integers(0, 2) else wl.MODE_THRESHOLD
+    announce(f"decode sweep {seed}: b={b} hq={dw.hq} hkv={hkv} d={dw.head_dim} tmax={tmax} "
+             f"lens={lens} block={block} lists={dw.list_heads} mode={mode} "
+             f"budget={dw.budget_tokens} sink={dw.keep_sink}")
+    q, k, v, kv_len = wl.make_decode_inputs(dw, tail_nan=True)
+    s = wl.make_decode_scores(dw)
+    thr = 2.0
+    max_k = min(dw.nkb, max(dw.k_blocks, 2)) if mode == wl.MODE_TOPK else max(2, dw.nkb // 3)
+    gi, gc = seer.seer_build_mask_decode(_dev(s), _dev(kv_len), block, mode, thr, dw.k_blocks,
+                                         dw.keep_sink, max_k)
+    ri, rc = oracle.build_mask_decode_ref(s.numpy(), lens, block, mode, thr, dw.k_blocks,
+                                          dw.keep_sink, max_k)
+    gi, gc = gi.cpu().numpy(), gc.cpu().numpy()
+    assert (gc == rc).all() and (gi == ri).all()
+    scale = 1.0 / math.sqrt(dw.head_dim)
+    got = _run_decode(dw, q, k, v, kv_len, gi, gc, scale).float().cpu().numpy()
+    ref = oracle.sparse_decode_ref(q, k, v, lens, gi, gc, scale, block)
+    assert np.isfinite(got).all()
+    err = float(np.abs(got - ref).max())
+    announce(f"decode sweep {seed}: max err {err:.2e}")
+    assert err <= O_TOL
+
+
 def test_sparse_decode_shared_equals_repeated_per_head_lists():
     """Ascending shared lists and the same lists repeated per query head go through
     the direct and the union path; both visit the same tiles in the same order (at
