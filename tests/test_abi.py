@@ -346,3 +346,27 @@ def test_sparse_decode_rejects_on_host():
     assert ws(2, 32, 8, 4096, 128, 32, 64, 64) > ws(2, 32, 8, 4096, 128, 8, 64, 64)
     assert ws(2, 32, 8, 4096, 128, 16, 64, 64) == 0
     assert ws(2, 32, 8, 0, 128, 8, 64, 64) == 0
+
+
+def test_decode_workspace_follows_chunk_rule():
+    """The decode workspace holds one partial per chunk of listed blocks; a chunk is
+    the largest of 1024, 512, 256, 128 tokens that still gives each of the 256 CUs a
+    workgroup (B * Hkv * chunks >= 256), else 128 tokens."""
+    a256 = lambda x: (x + 255) // 256 * 256
+    def expect(b, hq, hkv, tmax, d, lh, max_k, bs):
+        g, groups, nbmax = hq // hkv, b * hkv, (tmax + bs - 1) // bs
+        union = lh == hq and g > 1
+        umax = min(g * max_k, nbmax) if union else max_k
+        for tok in (1024, 512, 256, 128):
+            chunk = max(1, tok // bs)
+            nsplit = max(1, (umax + chunk - 1) // chunk)
+            if groups * nsplit >= 256:
+                break
+        off = a256(groups * umax * 4) + a256(groups * 4) if union else 0
+        return off + a256(groups * nsplit * g * 2 * 4) + a256(groups * nsplit * g * d * 4) + 256
+    for args in [(8, 32, 8, 40960, 128, 8, 64, 64),    # 1024-token chunks, 256 workgroups
+                 (8, 32, 8, 40960, 128, 32, 64, 64),   # union of per-head lists
+                 (1, 32, 8, 40960, 128, 8, 64, 64),    # small grid: 128-token chunks
+                 (2, 8, 2, 3000, 64, 8, 20, 128),      # 128-token blocks
+                 (4, 32, 8, 16384, 128, 8, 32, 64)]:   # 256-token chunks
+        assert seer.sparse_decode_workspace_size(*args) == expect(*args), args
