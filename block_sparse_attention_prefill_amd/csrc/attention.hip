@@ -132,11 +132,14 @@ __device__ __forceinline__ uint32_t lds_u32(const char* p) {
       (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p));
 }
 
+// The LDS-DMA reads M0 at issue, and gfx9 needs one wait state between an SALU
+// write of M0 and an LDS-DMA instruction (the compiler's hazard pass cannot see
+// inside the asm, so the s_nop is written here); M0 is declared clobbered.
 __device__ __forceinline__ void dma16(uint64_t sbase, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(m0)
-               : "memory");
+               : "memory", "m0");
 }
 
 // Per-lane HBM byte offsets of this wave's share of one 64-row tile, the tile
@@ -577,12 +580,13 @@ struct PartIssue {
     offsets(off, kBlk);
     lds0 = lds_u32(ring);
   }
-  // Copy part `p` of the K or V tile whose first row is `g` into ring slot `slot`.
+  // Copy part `p` of the K or V tile whose first row is `g` into the ring slot
+  // starting `slot_off` bytes into the ring.
   template <bool IS_V>
-  __device__ __forceinline__ void issue(const __bf16* g, int nvalid, int p, int slot) const {
+  __device__ __forceinline__ void issue(const __bf16* g, int nvalid, int p, int slot_off) const {
     const uint64_t sb = uniform_u64(g + kPartD * p);
     constexpr uint32_t stride = IS_V ? kPartVSlab : kPartKSlab;
-    const uint32_t lb = lds0 + slot * kPartSlotBytes + kPartCopiesPerWave * wave * stride;
+    const uint32_t lb = lds0 + slot_off + kPartCopiesPerWave * wave * stride;
     if (nvalid >= kBlk) {
 #pragma unroll
       for (int n = 0; n < kPartCopiesPerWave; ++n) dma16(sb, off[n], lb + n * stride);
@@ -701,38 +705,82 @@ __device__ __forceinline__ void pv_part(RowState<D>& st, const bf16x8 (&pb)[4], 
   }
 }
 
-// The sparse pass's loop over one item's list (entries outside [0, i] are
-// skipped; `next(e)` is the first usable list position >= e, `block(e)` its
-// KV block).  The last step reads its slot after the final barrier, so the
-// ring must not be reused without another barrier (the kernel ends here).
-template <int D, typename Next, typename Block>
+// An item's list as a walk over positions x = BS * entry + sub-tile (BS = list
+// block size in 64-token tiles); position x stands for tile BS * list[x / BS] +
+// x % BS and is usable when that entry lies in [0, ib] (ib = the item's own list
+// row) and the tile does not pass the diagonal tile i.  The wave keeps 64
+// consecutive positions in one VGPR (lane L: position base + L, its tile or -1)
+// and their usable-mask from a ballot, so finding the next usable position is a
+// find-first-set on scalar registers and reading its tile a v_readlane: no memory
+// access on the tile loop's path except one window load per 64 positions.  The
+// window load is an ordinary vector load; the compiler waits for it itself, and
+// any copy issued before it is then waited for as well (never fewer).
+template <int BS>
+struct ListWindow {
+  const int32_t* __restrict__ lst;
+  int npos;  // BS * list length
+  int ib, i;
+  int base;  // first position of the window (a multiple of 64), -64 before the first load
+  int win;
+  uint64_t valid;
+  __device__ __forceinline__ void load(int b, int lane) {
+    base = b;
+    const int x = b + lane;
+    int t = -1;
+    if (x < npos) {
+      const int j = lst[x / BS];
+      const int tile = BS * j + x % BS;
+      if (j >= 0 && j <= ib && tile <= i) t = tile;
+    }
+    win = t;
+    valid = __builtin_amdgcn_ballot_w64(t >= 0);
+  }
+  // First usable position >= x, or npos if there is none.  Wave-uniform.
+  __device__ __forceinline__ int next(int x, int lane) {
+    while (x < npos) {
+      if (x >= base + 64) load(x & ~63, lane);
+      const uint64_t m = valid & (~0ull << (x - base));
+      if (m != 0) return base + (int)__builtin_ctzll(m);
+      x = base + 64;
+    }
+    return npos;
+  }
+  // Tile of usable position x (inside the current window).
+  __device__ __forceinline__ int tile(int x) const {
+    return __builtin_amdgcn_readlane(win, x - base);
+  }
+};
+
+// The sparse pass's loop over one item's list (unusable positions are
+// skipped, see ListWindow).  The last step reads its slot after the final
+// barrier, so the ring must not be reused without another barrier (the kernel
+// ends here).
+template <int D, int BS>
 __device__ __forceinline__ void kv_loop_parts(RowState<D>& st, const __bf16* __restrict__ qh,
                                               int q0, const __bf16* __restrict__ kh,
-                                              const __bf16* __restrict__ vh, int T, int i, int n,
-                                              Next next, Block block, char* ring, int lane,
-                                              int wave, float c) {
+                                              const __bf16* __restrict__ vh, int T, int i,
+                                              ListWindow<BS>& lw, char* ring, int lane, int wave,
+                                              float c) {
   constexpr int NP = D / kPartD;           // K (and V) parts per tile
   constexpr int NL = kPartCopiesPerWave;   // this wave's copies per part
-  int e = next(0);
-  if (e >= n) {
-    load_q<D>(st, qh, q0, T, lane, wave);
-    return;
-  }
+  // Q first: its loads overlap the list window's load and the first copies.
+  load_q<D>(st, qh, q0, T, lane, wave);
+  int e = lw.next(0, lane);
+  if (e >= lw.npos) return;
   PartIssue<D> io;
   io.init(ring, wave, lane);
-  int j = block(e);
+  int j = lw.tile(e);
   // Stream parts 0 and 1: K0, K1 for D = 128; K, V for D = 64.
   io.template issue<false>(kh + (size_t)kBlk * j * D, T - kBlk * j, 0, 0);
   if (NP == 2)
-    io.template issue<false>(kh + (size_t)kBlk * j * D, T - kBlk * j, 1, 1);
+    io.template issue<false>(kh + (size_t)kBlk * j * D, T - kBlk * j, 1, kPartSlotBytes);
   else
-    io.template issue<true>(vh + (size_t)kBlk * j * D, T - kBlk * j, 0, 1);
-  load_q<D>(st, qh, q0, T, lane, wave);
+    io.template issue<true>(vh + (size_t)kBlk * j * D, T - kBlk * j, 0, kPartSlotBytes);
   wait_vmcnt<0>();
-  int slot0 = 0;  // ring slot of the current tile's first part
-  auto slot = [&](int p) {  // ring slot of stream part (current tile, p), p <= 5
-    return (slot0 + p) % kPartSlots;
-  };
+  // Ring slots (byte offsets) of stream parts s, s + 1, s + 2 (mod 3), s being
+  // the slot of the current tile's first part.  A tile of NP K and NP V parts
+  // advances s by 2 NP = 1 (D = 128) or 2 (D = 64) modulo 3.
+  int sa = 0, sb = kPartSlotBytes, sc = 2 * kPartSlotBytes;
   while (true) {
     const int cur = j;
     const __bf16* kc = kh + (size_t)kBlk * cur * D;
@@ -742,19 +790,18 @@ __device__ __forceinline__ void kv_loop_parts(RowState<D>& st, const __bf16* __r
     f32x16 s[2];
     bf16x8 pb[4];
     if constexpr (NP == 2) {
-      // Step K0: parts K0 (landing), K1 in flight; request V0.
+      // Step K0: parts K0 (landing, slot a), K1 (slot b) in flight; request V0 (slot c).
       step_barrier<NL>();
-      // The next list entry is needed from step V0 on: its scalar load
-      // overlaps the QK below instead of stalling a step barrier.
-      e = next(e + 1);
-      more = e < n;
-      if (more) j = block(e);
-      qk_part<D>(st, ring + slot(0) * kPartSlotBytes, lane, 0, s);
-      io.template issue<true>(vc, nc, 0, slot(2));
-      // Step K1: K1 landing, V0 in flight; request V1.
+      // The next usable entry is needed from step V0 on.
+      e = lw.next(e + 1, lane);
+      more = e < lw.npos;
+      if (more) j = lw.tile(e);
+      qk_part<D>(st, ring + sa, lane, 0, s);
+      io.template issue<true>(vc, nc, 0, sc);
+      // Step K1: K1 landing, V0 in flight; request V1 (slot a).
       step_barrier<NL>();
-      qk_part<D>(st, ring + slot(1) * kPartSlotBytes, lane, 1, s);
-      io.template issue<true>(vc, nc, 1, slot(3));
+      qk_part<D>(st, ring + sb, lane, 1, s);
+      io.template issue<true>(vc, nc, 1, sa);
       if (cur == i) {  // wave-uniform; the fence keeps it a branch
         compiler_fence();
         mask_diag(s, lane, wave);
@@ -763,37 +810,43 @@ __device__ __forceinline__ void kv_loop_parts(RowState<D>& st, const __bf16* __r
       p_operands<D>(st, s, pb);
       const __bf16* kn = kh + (size_t)kBlk * j * D;
       const int nn = T - kBlk * j;
-      // Step V0: V0 landing, V1 in flight; request K0 of the next tile.
+      // Step V0: V0 landing (slot c), V1 in flight; request K0 of the next tile (slot b).
       step_barrier<NL>();
-      pv_part<D>(st, pb, ring + slot(2) * kPartSlotBytes, lane, 0);
-      if (more) io.template issue<false>(kn, nn, 0, slot(4));
-      // Step V1: V1 landing, K0' in flight if any; request K1'.
+      pv_part<D>(st, pb, ring + sc, lane, 0);
+      if (more) io.template issue<false>(kn, nn, 0, sb);
+      // Step V1: V1 landing (slot a), K0' in flight if any; request K1' (slot c).
       if (more) step_barrier<NL>(); else step_barrier<0>();
-      pv_part<D>(st, pb, ring + slot(3) * kPartSlotBytes, lane, 1);
-      if (more) io.template issue<false>(kn, nn, 1, slot(5));
-      slot0 = slot(4);
+      pv_part<D>(st, pb, ring + sa, lane, 1);
+      if (more) io.template issue<false>(kn, nn, 1, sc);
+      const int t0 = sa;
+      sa = sb;
+      sb = sc;
+      sc = t0;
     } else {
-      e = next(e + 1);
-      more = e < n;
-      if (more) j = block(e);
+      e = lw.next(e + 1, lane);
+      more = e < lw.npos;
+      if (more) j = lw.tile(e);
       const __bf16* kn = kh + (size_t)kBlk * j * D;
       const __bf16* vn = vh + (size_t)kBlk * j * D;
       const int nn = T - kBlk * j;
-      // Step K: K landing, V in flight; request K of the next tile.
+      // Step K: K landing (slot a), V (slot b) in flight; request K of the next tile (slot c).
       step_barrier<NL>();
-      qk_part<D>(st, ring + slot(0) * kPartSlotBytes, lane, 0, s);
-      if (more) io.template issue<false>(kn, nn, 0, slot(2));
+      qk_part<D>(st, ring + sa, lane, 0, s);
+      if (more) io.template issue<false>(kn, nn, 0, sc);
       if (cur == i) {
         compiler_fence();
         mask_diag(s, lane, wave);
       }
       (void)softmax_tile<D, false>(st, s, c);
       p_operands<D>(st, s, pb);
-      // Step V: V landing, K' in flight if any; request V'.
+      // Step V: V landing (slot b), K' in flight if any; request V' (slot a).
       if (more) step_barrier<NL>(); else step_barrier<0>();
-      pv_part<D>(st, pb, ring + slot(1) * kPartSlotBytes, lane, 0);
-      if (more) io.template issue<true>(vn, nn, 0, slot(3));
-      slot0 = slot(2);
+      pv_part<D>(st, pb, ring + sb, lane, 0);
+      if (more) io.template issue<true>(vn, nn, 0, sa);
+      const int t0 = sc;
+      sc = sb;
+      sb = sa;
+      sa = t0;
     }
     if (!more) break;
   }
@@ -830,18 +883,9 @@ __global__ __launch_bounds__(kPairThreads, 3) void sparse_prefill_kernel(
   const size_t lrow = (size_t)bh * rows + ib;
   const int32_t* lst = idx + lrow * max_k;
   const int n = min(max(cnt[lrow], 0), max_k);
-  // Walk positions x = BS * entry + sub-tile; tile BS * lst[entry] + sub.
-  auto next = [&](int x) {  // first position >= x holding a tile in [0, i]
-    while (x < BS * n) {
-      const int j = lst[x / BS];
-      if (j >= 0 && j <= ib && BS * j + x % BS <= i) break;
-      ++x;
-    }
-    return x;
-  };
-  auto block = [&](int x) { return BS * lst[x / BS] + x % BS; };
-  kv_loop_parts<D>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, BS * n, next, block,
-                   ring, lane, wave, c);
+  ListWindow<BS> lw{lst, BS * n, ib, i, -64, -1, 0};
+  kv_loop_parts<D, BS>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, lw, ring, lane,
+                       wave, c);
   (void)store_o<D>(st, o + q_off, kBlk * i, T, lane, wave);
 }
 
