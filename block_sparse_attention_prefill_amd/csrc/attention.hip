@@ -723,17 +723,25 @@ struct ListWindow {
   int base;  // first position of the window (a multiple of 64), -64 before the first load
   int win;
   uint64_t valid;
-  __device__ __forceinline__ void load(int b, int lane) {
+  // issue() requests the window starting at position b (lane L: list entry of
+  // position b + L); finish() turns it into tiles and the usable-mask.  Split so
+  // that other loads can be requested between the two.
+  __device__ __forceinline__ void issue(int b, int lane) {
     base = b;
     const int x = b + lane;
-    int t = -1;
-    if (x < npos) {
-      const int j = lst[x / BS];
-      const int tile = BS * j + x % BS;
-      if (j >= 0 && j <= ib && tile <= i) t = tile;
-    }
-    win = t;
-    valid = __builtin_amdgcn_ballot_w64(t >= 0);
+    win = x < npos ? lst[x / BS] : -1;
+  }
+  __device__ __forceinline__ void finish(int lane) {
+    const int x = base + lane;
+    const int j = win;
+    const int tile = BS * j + x % BS;
+    const bool ok = x < npos && j >= 0 && j <= ib && tile <= i;
+    win = ok ? tile : -1;
+    valid = __builtin_amdgcn_ballot_w64(ok);
+  }
+  __device__ __forceinline__ void load(int b, int lane) {
+    issue(b, lane);
+    finish(lane);
   }
   // First usable position >= x, or npos if there is none.  Wave-uniform.
   __device__ __forceinline__ int next(int x, int lane) {
@@ -759,24 +767,25 @@ template <int D, int BS>
 __device__ __forceinline__ void kv_loop_parts(RowState<D>& st, const __bf16* __restrict__ qh,
                                               int q0, const __bf16* __restrict__ kh,
                                               const __bf16* __restrict__ vh, int T, int i,
-                                              ListWindow<BS>& lw, char* ring, int lane, int wave,
-                                              float c) {
+                                              ListWindow<BS>& lw, int e, int j, char* ring,
+                                              int lane, int wave, float c) {
   constexpr int NP = D / kPartD;           // K (and V) parts per tile
   constexpr int NL = kPartCopiesPerWave;   // this wave's copies per part
-  // Q first: its loads overlap the list window's load and the first copies.
-  load_q<D>(st, qh, q0, T, lane, wave);
-  int e = lw.next(0, lane);
-  if (e >= lw.npos) return;
+  // e = the first usable position, j = its tile (from the work entry).  The
+  // first copies, the Q rows and the list window are all requested before the
+  // one wait, so the item's start costs one memory latency.
   PartIssue<D> io;
   io.init(ring, wave, lane);
-  int j = lw.tile(e);
   // Stream parts 0 and 1: K0, K1 for D = 128; K, V for D = 64.
   io.template issue<false>(kh + (size_t)kBlk * j * D, T - kBlk * j, 0, 0);
   if (NP == 2)
     io.template issue<false>(kh + (size_t)kBlk * j * D, T - kBlk * j, 1, kPartSlotBytes);
   else
     io.template issue<true>(vh + (size_t)kBlk * j * D, T - kBlk * j, 0, kPartSlotBytes);
+  load_q<D>(st, qh, q0, T, lane, wave);
+  lw.issue(e & ~63, lane);
   wait_vmcnt<0>();
+  lw.finish(lane);
   // Ring slots (byte offsets) of stream parts s, s + 1, s + 2 (mod 3), s being
   // the slot of the current tile's first part.  A tile of NP K and NP V parts
   // advances s by 2 NP = 1 (D = 128) or 2 (D = 64) modulo 3.
@@ -861,15 +870,16 @@ __device__ __forceinline__ void kv_loop_parts(RowState<D>& st, const __bf16* __r
 template <int D, int BS>
 __global__ __launch_bounds__(kPairThreads, 3) void sparse_prefill_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    int Hq, int Hkv, int T, int nqb, float c, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ cnt, int max_k, const int32_t* __restrict__ work,
-    __bf16* __restrict__ o) {
+    int Hq, int Hkv, int T, int nqb, float c, const int32_t* __restrict__ idx, int max_k,
+    const int32_t* __restrict__ work, __bf16* __restrict__ o) {
   __shared__ __attribute__((aligned(1024))) char ring[kPartSlots * kPartSlotBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int item = work[blockIdx.x];
+  const int4 w4 = reinterpret_cast<const int4*>(work)[blockIdx.x];
+  const int item = w4.x;
+  if (item < 0) return;  // never written by the schedule (every rank holds an item)
   const int i = item % nqb;   // 64-row query block
   const int bh = item / nqb;  // b * Hq + h
   const int b = bh / Hq;
@@ -882,10 +892,15 @@ __global__ __launch_bounds__(kPairThreads, 3) void sparse_prefill_kernel(
   const int ib = i / BS;                 // this item's list row (and its own block)
   const size_t lrow = (size_t)bh * rows + ib;
   const int32_t* lst = idx + lrow * max_k;
-  const int n = min(max(cnt[lrow], 0), max_k);
-  ListWindow<BS> lw{lst, BS * n, ib, i, -64, -1, 0};
-  kv_loop_parts<D, BS>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, lw, ring, lane,
-                       wave, c);
+  ListWindow<BS> lw{lst, BS * w4.w, ib, i, -64, -1, 0};
+  if (w4.y < lw.npos) {
+    kv_loop_parts<D, BS>(st, q + q_off, kBlk * i, k + kv_off, v + kv_off, T, i, lw, w4.y, w4.z,
+                         ring, lane, wave, c);
+  } else {  // no usable entry: O = 0
+#pragma unroll
+    for (int dt = 0; dt < Cfg<D>::kDTiles; ++dt) st.acc[dt] = f32x16{};
+    st.l = 0.f;
+  }
   (void)store_o<D>(st, o + q_off, kBlk * i, T, lane, wave);
 }
 
@@ -993,11 +1008,11 @@ __global__ __launch_bounds__(kPairThreads * HPW, kPairWgsPerCu) void pooled_map_
 constexpr int kSchedThreads = 1024;
 constexpr int kCostBins = 1024;
 
-// Counting sort of the n candidates `keep` accepts into column `col` of a list
-// with `ng` columns and `cap` rows.  Called by the whole workgroup.
-template <typename Keep, typename Cost, typename Id>
-__device__ void lpt_column(int n, Keep keep, Cost cost, Id id, int32_t* __restrict__ out, int ng,
-                           int col, int cap, int* hist, int* wsum) {
+// Counting sort of the n candidates `keep` accepts by descending cost: the
+// candidate of rank r is handed to put(r, it), and put(r, -1) fills the ranks
+// total .. cap - 1 past the last candidate.  Called by the whole workgroup.
+template <typename Keep, typename Cost, typename Put>
+__device__ void lpt_column(int n, Keep keep, Cost cost, Put put, int cap, int* hist, int* wsum) {
   const int tid = threadIdx.x;
   auto bin_of = [&](int it) { return kCostBins - 1 - min(cost(it), kCostBins - 1); };
   hist[tid] = 0;
@@ -1023,28 +1038,50 @@ __device__ void lpt_column(int n, Keep keep, Cost cost, Id id, int32_t* __restri
   hist[tid] = before + incl - v;  // exclusive offset of this bin
   __syncthreads();
   for (int it = tid; it < n; it += kSchedThreads)
-    if (keep(it)) out[atomicAdd(&hist[bin_of(it)], 1) * ng + col] = id(it);
-  for (int r = total + tid; r < cap; r += kSchedThreads) out[r * ng + col] = -1;
+    if (keep(it)) put(atomicAdd(&hist[bin_of(it)], 1), it);
+  for (int r = total + tid; r < cap; r += kSchedThreads) put(r, -1);
   __syncthreads();  // hist and wsum are reused by the next call
 }
 
+// Each work entry is {item, first usable list position, its tile, list length}
+// (an int4), so that the prefill workgroup can request its first K tile, its Q
+// rows and its list window at once, with no chain of dependent loads.  An item
+// without a usable position gets position = BS * length and tile -1.
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
-    const int32_t* __restrict__ cnt, int Hq, int Hkv, int nqb, int bs, int max_k,
-    int32_t* __restrict__ work) {
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ idx, int Hq, int Hkv, int nqb,
+    int bs, int max_k, int4* __restrict__ work) {
   __shared__ int hist[kCostBins];
   __shared__ int wsum[kSchedThreads / 64];
   const int G = Hq / Hkv;
   const int grp = blockIdx.x;
+  const int ng = gridDim.x;
   const int bh0 = (grp / Hkv) * Hq + (grp % Hkv) * G;  // first head of the group
   const int base = bh0 * nqb;                          // the group's items
   const int rows = (nqb + bs - 1) / bs;                // list rows per head
+  auto row_of = [&](int it) { return (size_t)(bh0 + it / nqb) * rows + (it % nqb) / bs; };
+  auto len_of = [&](int it) { return min(max(cnt[row_of(it)], 0), max_k); };
   lpt_column(
-      G * nqb, [](int) { return true; },
-      [&](int it) {
-        const int c = cnt[(bh0 + it / nqb) * rows + (it % nqb) / bs];
-        return bs * min(max(c, 0), max_k);
+      G * nqb, [](int) { return true; }, [&](int it) { return bs * len_of(it); },
+      [&](int r, int it) {
+        int4 e = {-1, 0, -1, 0};
+        if (it >= 0) {
+          const int n = len_of(it);
+          const int32_t* lst = idx + row_of(it) * (size_t)max_k;
+          const int i = it % nqb, ib = i / bs;
+          int x = 0, tile = -1;
+          for (; x < bs * n; ++x) {  // first usable position (normally x = 0)
+            const int j = lst[x / bs];
+            const int t = bs * j + x % bs;
+            if (j >= 0 && j <= ib && t <= i) {
+              tile = t;
+              break;
+            }
+          }
+          e = {base + it, x, tile, n};
+        }
+        work[(size_t)r * ng + grp] = e;
       },
-      [&](int it) { return base + it; }, work, gridDim.x, grp, G * nqb, hist, wsum);
+      G * nqb, hist, wsum);
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -1056,11 +1093,11 @@ constexpr int kPairVSlots = 1;
 
 template <int D, int BS>
 hipError_t sparse_launch(const void* q, const void* k, const void* v, size_t items, int Hq,
-                         int Hkv, int T, int nqb, float c, const int32_t* idx, const int32_t* cnt,
-                         int max_k, const int32_t* work, void* o, hipStream_t stream) {
+                         int Hkv, int T, int nqb, float c, const int32_t* idx, int max_k,
+                         const int32_t* work, void* o, hipStream_t stream) {
   hipLaunchKernelGGL((sparse_prefill_kernel<D, BS>), dim3((unsigned)items), dim3(kPairThreads), 0,
                      stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, Hq, Hkv, T,
-                     nqb, c, idx, cnt, max_k, work, (__bf16*)o);
+                     nqb, c, idx, max_k, work, (__bf16*)o);
   return hipGetLastError();
 }
 
@@ -1079,7 +1116,8 @@ hipError_t pooled_launch(const void* q, const void* k, const void* v, int B, int
 
 }  // namespace
 
-size_t sparse_work_entries(int B, int Hq, int, int nqb) { return (size_t)B * Hq * nqb; }
+// int32 entries: one int4 {item, first usable position, its tile, length} per item.
+size_t sparse_work_entries(int B, int Hq, int, int nqb) { return (size_t)4 * B * Hq * nqb; }
 
 hipError_t launch_sparse_prefill(const void* q, const void* k, const void* v, int B, int Hq,
                                  int Hkv, int T, int D, float sm_scale, int block,
@@ -1090,18 +1128,18 @@ hipError_t launch_sparse_prefill(const void* q, const void* k, const void* v, in
   if (items == 0) return hipSuccess;
   const float c = sm_scale * kLog2e;
   const int bs = block / kBlk;
-  hipLaunchKernelGGL(schedule_kernel, dim3(B * Hkv), dim3(kSchedThreads), 0, stream, cnt, Hq, Hkv,
-                     nqb, bs, max_k, work);
+  hipLaunchKernelGGL(schedule_kernel, dim3(B * Hkv), dim3(kSchedThreads), 0, stream, cnt, idx,
+                     Hq, Hkv, nqb, bs, max_k, reinterpret_cast<int4*>(work));
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (bs == 2)
-    return D == 128 ? sparse_launch<128, 2>(q, k, v, items, Hq, Hkv, T, nqb, c, idx, cnt, max_k,
+    return D == 128 ? sparse_launch<128, 2>(q, k, v, items, Hq, Hkv, T, nqb, c, idx, max_k,
                                             work, o, stream)
-                    : sparse_launch<64, 2>(q, k, v, items, Hq, Hkv, T, nqb, c, idx, cnt, max_k,
+                    : sparse_launch<64, 2>(q, k, v, items, Hq, Hkv, T, nqb, c, idx, max_k,
                                            work, o, stream);
-  return D == 128 ? sparse_launch<128, 1>(q, k, v, items, Hq, Hkv, T, nqb, c, idx, cnt, max_k,
+  return D == 128 ? sparse_launch<128, 1>(q, k, v, items, Hq, Hkv, T, nqb, c, idx, max_k,
                                           work, o, stream)
-                  : sparse_launch<64, 1>(q, k, v, items, Hq, Hkv, T, nqb, c, idx, cnt, max_k, work,
+                  : sparse_launch<64, 1>(q, k, v, items, Hq, Hkv, T, nqb, c, idx, max_k, work,
                                          o, stream);
 }
 

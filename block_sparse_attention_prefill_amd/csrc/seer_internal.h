@@ -17,7 +17,7 @@ typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef float f32x8 __attribute__((__vector_size__(8 * sizeof(float))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
-// int32 entries of the sparse prefill's work lists (schedule output).
+// int32 entries of the sparse prefill's work list (schedule output: one int4 per item).
 size_t sparse_work_entries(int B, int Hq, int Hkv, int nqb);
 
 hipError_t launch_build_mask(const float* scores, int B, int H, int nqb, int nkb, int mode,

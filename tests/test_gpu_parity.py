@@ -321,10 +321,13 @@ def test_sparse_density_one_matches_dense_causal():
 
 
 @pytest.mark.parametrize("hq,hkv,t,mode", [(32, 8, 4096, "sorted"), (6, 2, 700, "dense"),
+                                           (4, 2, 900, "invalid"),
                                            (3, 3, 1000, "invalid")])
 def test_sparse_schedule_work_list(hq, hkv, t, mode):
     """The work list the schedule leaves in the workspace: column q = b * Hkv + g
-    holds every item of KV group (b, g) exactly once, longest list first."""
+    holds every item of KV group (b, g) exactly once, longest list first, each
+    with its first usable list position, that position's tile and the list
+    length (bit-exact against a scan on the host)."""
     announce(f"schedule work list hq={hq} hkv={hkv} t={t} lists={mode}")
     b, d = 1, 64
     nqb = (t + 63) // 64
@@ -339,15 +342,22 @@ def test_sparse_schedule_work_list(hq, hkv, t, mode):
                              workspace=ws.view(torch.uint8))
     torch.cuda.synchronize()
     ng = b * hkv
-    work = ws.cpu().numpy()[: b * hq * nqb].reshape(G * nqb, ng)
+    work = ws.cpu().numpy()[: 4 * b * hq * nqb].reshape(G * nqb, ng, 4)
     flat_cnt = np.minimum(np.maximum(cnt.reshape(-1), 0), max_k)
+    flat_idx = idx.reshape(-1, max_k)
     for grp in range(ng):
         bb, gg = divmod(grp, hkv)
         lo = (bb * hq + gg * G) * nqb
-        col = work[:, grp]
+        col = work[:, grp, 0]
         assert sorted(col.tolist()) == list(range(lo, lo + G * nqb))
         costs = flat_cnt[col]
         assert (np.diff(costs) <= 0).all(), "items must be longest first"
+        for item, pos, tile, n in work[:, grp]:
+            i = item % nqb
+            lst = flat_idx[item][: flat_cnt[item]]
+            usable = [x for x, j in enumerate(lst) if 0 <= j <= i]
+            assert n == flat_cnt[item]
+            assert (pos, tile) == ((usable[0], lst[usable[0]]) if usable else (len(lst), -1))
 
 
 @pytest.mark.parametrize("d", [128, 64])
