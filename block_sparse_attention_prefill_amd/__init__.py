@@ -13,7 +13,10 @@ from .binding import (BLOCK, SEER_MASK_THRESHOLD, SEER_MASK_TOPK, SeerError, loa
                       sparse_decode_workspace_size,
                       pooled_attn_map_workspace_size, seer_build_mask, seer_pooled_attn_map,
                       seer_pooled_target_mse, seer_sparse_prefill, seer_sparse_prefill_block,
-                      sparse_prefill_workspace_size, topk_budget, version)
+                      sparse_prefill_workspace_size, topk_budget, version,
+                      seer_build_mask_need, seer_validate_lists, list_flags_status,
+                      SEER_LIST_BAD_COUNT, SEER_LIST_BAD_ENTRY, SEER_LIST_REPEAT,
+                      SEER_LIST_UNSORTED, SEER_LIST_CAPACITY)
 
 __all__ = [
     "BLOCK", "SEER_MASK_THRESHOLD", "SEER_MASK_TOPK", "SeerError", "load",
@@ -26,5 +29,7 @@ __all__ = [
     "sparse_decode_workspace_size",
     "pooled_attn_map_workspace_size", "seer_build_mask", "seer_pooled_attn_map",
     "seer_pooled_target_mse", "seer_sparse_prefill", "seer_sparse_prefill_block",
-    "sparse_prefill_workspace_size", "topk_budget", "version",
+    "sparse_prefill_workspace_size", "topk_budget", "version", "seer_build_mask_need",
+    "seer_validate_lists", "list_flags_status", "SEER_LIST_BAD_COUNT", "SEER_LIST_BAD_ENTRY",
+    "SEER_LIST_REPEAT", "SEER_LIST_UNSORTED", "SEER_LIST_CAPACITY",
 ]

@@ -29,8 +29,15 @@ EXPORTED = (
     "seer_attn_gate_mask_pass_workspace_size",
     "seer_attn_gate_mask", "seer_attn_gate_decode_keys_workspace_size", "seer_attn_gate_decode_keys",
     "seer_attn_gate_decode_scores", "seer_attn_gate_decode_mask", "seer_build_mask_decode",
-    "seer_sparse_decode_workspace_size", "seer_sparse_decode",
+    "seer_sparse_decode_workspace_size", "seer_sparse_decode", "seer_build_mask_need",
+    "seer_validate_lists", "seer_list_flags_status",
 )
+
+SEER_LIST_BAD_COUNT = 1
+SEER_LIST_BAD_ENTRY = 2
+SEER_LIST_REPEAT = 4
+SEER_LIST_UNSORTED = 8
+SEER_LIST_CAPACITY = 16
 
 _lib = None
 
@@ -62,6 +69,14 @@ def load() -> ctypes.CDLL:
     lib.seer_build_mask.restype = c_int
     lib.seer_build_mask.argtypes = [c_void, c_int, c_int, c_int, c_int, c_int, c_float, c_double,
                                     c_int, c_void, c_void, c_int, c_void]
+    lib.seer_build_mask_need.restype = c_int
+    lib.seer_build_mask_need.argtypes = [c_void, c_int, c_int, c_int, c_int, c_int, c_float,
+                                         c_double, c_int, c_void, c_void, c_void, c_int, c_void]
+    lib.seer_validate_lists.restype = c_int
+    lib.seer_validate_lists.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int,
+                                        c_void, c_void, c_void]
+    lib.seer_list_flags_status.restype = c_int
+    lib.seer_list_flags_status.argtypes = [c_int]
     lib.seer_sparse_prefill_workspace_size.restype = c_size
     lib.seer_sparse_prefill_workspace_size.argtypes = [c_int, c_int, c_int, c_int]
     lib.seer_sparse_prefill.restype = c_int
@@ -175,6 +190,55 @@ def seer_build_mask(scores: torch.Tensor, mode: int, threshold: float, density: 
         _ptr(scores), b, h, nqb, nkb, int(mode), float(threshold), float(density),
         int(bool(keep_sink)), _ptr(kv_idx), _ptr(kv_cnt), int(max_k), _stream(stream)))
     return kv_idx, kv_cnt
+
+
+def seer_build_mask_need(scores: torch.Tensor, mode: int, threshold: float, density: float,
+                         keep_sink: bool, max_k: int, kv_idx: Optional[torch.Tensor] = None,
+                         kv_cnt: Optional[torch.Tensor] = None,
+                         kv_need: Optional[torch.Tensor] = None, stream=None):
+    """seer_build_mask plus kv_need int32 [B,H,nQB] (blocks selected before any cut
+    to max_k): returns (kv_idx, kv_cnt, kv_need)."""
+    lib = load()
+    b, h, nqb, nkb = scores.shape
+    _need(scores, "scores", torch.float32, (b, h, nqb, nkb))
+    dev = scores.device
+    kv_idx = torch.empty((b, h, nqb, max_k), dtype=torch.int32, device=dev) if kv_idx is None \
+        else kv_idx
+    kv_cnt = torch.empty((b, h, nqb), dtype=torch.int32, device=dev) if kv_cnt is None else kv_cnt
+    kv_need = torch.empty((b, h, nqb), dtype=torch.int32, device=dev) if kv_need is None \
+        else kv_need
+    _need(kv_idx, "kv_idx", torch.int32, (b, h, nqb, max_k))
+    _need(kv_cnt, "kv_cnt", torch.int32, (b, h, nqb))
+    _need(kv_need, "kv_need", torch.int32, (b, h, nqb))
+    _check("seer_build_mask_need", lib.seer_build_mask_need(
+        _ptr(scores), b, h, nqb, nkb, int(mode), float(threshold), float(density),
+        int(bool(keep_sink)), _ptr(kv_idx), _ptr(kv_cnt), _ptr(kv_need), int(max_k),
+        _stream(stream)))
+    return kv_idx, kv_cnt, kv_need
+
+
+def seer_validate_lists(kv_idx: torch.Tensor, kv_cnt: torch.Tensor,
+                        kv_need: Optional[torch.Tensor] = None, row_flags: bool = False,
+                        stream=None):
+    """Flag bits of block lists kv_idx [B,H,nB,max_k] / kv_cnt [B,H,nB]: returns the
+    device int32 [1] OR of all rows, and the per-row flags [B,H,nB] if asked."""
+    lib = load()
+    b, h, nb, max_k = kv_idx.shape
+    _need(kv_idx, "kv_idx", torch.int32, (b, h, nb, max_k))
+    _need(kv_cnt, "kv_cnt", torch.int32, (b, h, nb))
+    if kv_need is not None:
+        _need(kv_need, "kv_need", torch.int32, (b, h, nb))
+    flags = torch.empty((1,), dtype=torch.int32, device=kv_idx.device)
+    rows = torch.empty((b, h, nb), dtype=torch.int32, device=kv_idx.device) if row_flags else None
+    _check("seer_validate_lists", lib.seer_validate_lists(
+        _ptr(kv_idx), _ptr(kv_cnt), _ptr(kv_need), b, h, nb, int(max_k), _ptr(rows),
+        _ptr(flags), _stream(stream)))
+    return (flags, rows) if row_flags else flags
+
+
+def list_flags_status(flags: int) -> int:
+    """The status code a set of list flags amounts to (host only)."""
+    return load().seer_list_flags_status(int(flags))
 
 
 def sparse_prefill_workspace_size(b: int, hq: int, hkv: int, t: int) -> int:

@@ -68,9 +68,13 @@ int seer_topk_budget(int nQB, double density, int keep_sink) {
   return k;
 }
 
-int seer_build_mask(const float* scores, int B, int H, int nQB, int nKB, int mode,
+}  // extern "C"
+
+namespace {
+
+int build_mask_impl(const float* scores, int B, int H, int nQB, int nKB, int mode,
                     float threshold, double density, int keep_sink, int32_t* kv_idx,
-                    int32_t* kv_cnt, int max_k, void* stream) {
+                    int32_t* kv_cnt, int32_t* kv_need, int max_k, void* stream) {
   if (B < 0 || H < 0 || nQB < 0 || nKB < nQB) return SEER_ERR_INVALID_ARG;
   if (nQB > SEER_MAX_QUERY_BLOCKS) return SEER_ERR_UNSUPPORTED;
   if (mode != SEER_MASK_TOPK && mode != SEER_MASK_THRESHOLD) return SEER_ERR_INVALID_ARG;
@@ -88,8 +92,46 @@ int seer_build_mask(const float* scores, int B, int H, int nQB, int nKB, int mod
   }
   const hipError_t err = seer::launch_build_mask(scores, B, H, nQB, nKB, mode, threshold,
                                                  density, keep_sink ? 1 : 0, kv_idx, kv_cnt,
-                                                 max_k, (hipStream_t)stream);
+                                                 kv_need, max_k, (hipStream_t)stream);
   return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int seer_build_mask(const float* scores, int B, int H, int nQB, int nKB, int mode,
+                    float threshold, double density, int keep_sink, int32_t* kv_idx,
+                    int32_t* kv_cnt, int max_k, void* stream) {
+  return build_mask_impl(scores, B, H, nQB, nKB, mode, threshold, density, keep_sink, kv_idx,
+                         kv_cnt, nullptr, max_k, stream);
+}
+
+int seer_build_mask_need(const float* scores, int B, int H, int nQB, int nKB, int mode,
+                         float threshold, double density, int keep_sink, int32_t* kv_idx,
+                         int32_t* kv_cnt, int32_t* kv_need, int max_k, void* stream) {
+  if (!kv_need && (long long)B * H * nQB > 0) return SEER_ERR_INVALID_ARG;
+  return build_mask_impl(scores, B, H, nQB, nKB, mode, threshold, density, keep_sink, kv_idx,
+                         kv_cnt, kv_need, max_k, stream);
+}
+
+int seer_validate_lists(const int32_t* kv_idx, const int32_t* kv_cnt, const int32_t* kv_need,
+                        int B, int H, int nB, int max_k, int32_t* row_flags, int32_t* flags,
+                        void* stream) {
+  if (B < 0 || H < 0 || nB < 0 || max_k < 1) return SEER_ERR_INVALID_ARG;
+  if (!items_fit(B, H, nB)) return SEER_ERR_UNSUPPORTED;
+  if (!flags) return SEER_ERR_INVALID_ARG;
+  const long long rows = (long long)B * H * nB;
+  if (rows > 0 && (!kv_idx || !kv_cnt)) return SEER_ERR_INVALID_ARG;
+  const hipError_t err = seer::launch_validate_lists(kv_idx, kv_cnt, kv_need, rows, nB, max_k,
+                                                     row_flags, flags, (hipStream_t)stream);
+  return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
+}
+
+int seer_list_flags_status(int flags) {
+  if (flags & SEER_LIST_CAPACITY) return SEER_ERR_CAPACITY;
+  if (flags & SEER_LIST_REPEAT) return SEER_ERR_INVALID_ARG;
+  return SEER_OK;
 }
 
 size_t seer_sparse_prefill_workspace_size(int B, int Hq, int Hkv, int T) {

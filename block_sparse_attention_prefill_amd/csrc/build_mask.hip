@@ -41,7 +41,8 @@ template <int NPL>
 __global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
     const float* __restrict__ scores, long long rows, int nqb, int nkb, int mode, float tau,
     double density, int keep_sink, int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
-    int max_k, const int32_t* __restrict__ kv_len, int heads, int block, int k_blocks) {
+    int32_t* __restrict__ need, int max_k, const int32_t* __restrict__ kv_len, int heads,
+    int block, int k_blocks) {
   __shared__ int hist_all[kWavesPerGroup][256];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -96,7 +97,12 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
   }
 
   const int count = wave_select_row<NPL>(key, n, k, npos, lane, hist, out, max_k);
-  if (lane == 0) cnt[row] = count;
+  if (lane == 0) {
+    cnt[row] = count;
+    // The row's size before any cut to max_k: the TopK count, or every forced
+    // and passing block in threshold mode (more than max_k: the row was cut).
+    if (need) need[row] = mode == 1 ? min(k, npos) : npos;
+  }
 }
 
 }  // namespace
@@ -105,15 +111,15 @@ namespace {
 
 hipError_t launch_rows(const float* scores, long long rows, int nqb, int nkb, int row_len,
                        int mode, float threshold, double density, int keep_sink, int32_t* idx,
-                       int32_t* cnt, int max_k, const int32_t* kv_len, int heads, int block,
-                       int k_blocks, hipStream_t stream) {
+                       int32_t* cnt, int32_t* need, int max_k, const int32_t* kv_len, int heads,
+                       int block, int k_blocks, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const dim3 grid((unsigned)((rows + kWavesPerGroup - 1) / kWavesPerGroup));
   const dim3 threads(64 * kWavesPerGroup);
 #define SEER_MASK_LAUNCH(NPL)                                                                  \
   hipLaunchKernelGGL(build_mask_kernel<NPL>, grid, threads, 0, stream, scores, rows, nqb, nkb, \
-                     mode, threshold, density, keep_sink, idx, cnt, max_k, kv_len, heads,      \
-                     block, k_blocks)
+                     mode, threshold, density, keep_sink, idx, cnt, need, max_k, kv_len,       \
+                     heads, block, k_blocks)
   if (row_len <= 64 * 1) SEER_MASK_LAUNCH(1);
   else if (row_len <= 64 * 4) SEER_MASK_LAUNCH(4);
   else if (row_len <= 64 * 8) SEER_MASK_LAUNCH(8);
@@ -129,9 +135,9 @@ hipError_t launch_rows(const float* scores, long long rows, int nqb, int nkb, in
 
 hipError_t launch_build_mask(const float* scores, int B, int H, int nqb, int nkb, int mode,
                              float threshold, double density, int keep_sink, int32_t* idx,
-                             int32_t* cnt, int max_k, hipStream_t stream) {
+                             int32_t* cnt, int32_t* need, int max_k, hipStream_t stream) {
   return launch_rows(scores, (long long)B * H * nqb, nqb, nkb, nqb, mode, threshold, density,
-                     keep_sink, idx, cnt, max_k, nullptr, 1, 64, 0, stream);
+                     keep_sink, idx, cnt, need, max_k, nullptr, 1, 64, 0, stream);
 }
 
 hipError_t launch_build_mask_decode(const float* scores, const int32_t* kv_len, int B, int H,
@@ -139,7 +145,7 @@ hipError_t launch_build_mask_decode(const float* scores, const int32_t* kv_len, 
                                     int keep_sink, int32_t* idx, int32_t* cnt, int max_k,
                                     hipStream_t stream) {
   return launch_rows(scores, (long long)B * H, 1, nkb, nkb, mode, threshold, 1.0, keep_sink, idx,
-                     cnt, max_k, kv_len, H, block, k_blocks, stream);
+                     cnt, nullptr, max_k, kv_len, H, block, k_blocks, stream);
 }
 
 }  // namespace seer

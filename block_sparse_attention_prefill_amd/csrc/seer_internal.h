@@ -20,9 +20,16 @@ typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 // int32 entries of the sparse prefill's work list (schedule output: one int4 per item).
 size_t sparse_work_entries(int B, int Hq, int Hkv, int nqb);
 
+// need may be null (no per-row untruncated counts).
 hipError_t launch_build_mask(const float* scores, int B, int H, int nqb, int nkb, int mode,
                              float threshold, double density, int keep_sink, int32_t* idx,
-                             int32_t* cnt, int max_k, hipStream_t stream);
+                             int32_t* cnt, int32_t* need, int max_k, hipStream_t stream);
+
+// List validation: rows = B*H*nB list rows of max_k entries; need and row_flags
+// may be null; flags (one int) is cleared on the stream first.
+hipError_t launch_validate_lists(const int32_t* idx, const int32_t* cnt, const int32_t* need,
+                                 long long rows, int nrows_per_head, int max_k,
+                                 int32_t* row_flags, int32_t* flags, hipStream_t stream);
 
 // Decode rows: B*H rows of nkb scores; row (b, h) ranks the blocks holding
 // kv_len[b] tokens (block tokens each).

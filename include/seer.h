@@ -106,6 +106,65 @@ int seer_build_mask(const float* scores, int B, int H, int nQB, int nKB, int mod
                     float threshold, double density, int keep_sink, int32_t* kv_idx,
                     int32_t* kv_cnt, int max_k, void* stream);
 
+/*
+ * seer_build_mask that also reports, for every row, how many blocks the rule
+ * selects before any cut to max_k (the capacity signal of threshold mode).
+ *
+ * kv_need device int32 out [B, H, nQB], non-null:
+ *         TopK mode: the row's k_i (equal to kv_cnt, since max_k is at least
+ *         seer_topk_budget);
+ *         threshold mode: the forced blocks plus every other causal block with
+ *         score >= (float)threshold.  kv_need > max_k means the row was cut to
+ *         its forced blocks plus the max_k - |forced| best-ranked passing
+ *         blocks (kv_cnt = max_k): the list differs from what the threshold
+ *         selects, and seer_validate_lists reports it as SEER_LIST_CAPACITY.
+ * Lists, counts, arguments and errors are exactly those of seer_build_mask
+ * (model card "SeerAttention-Llama-3.1-8B-AttnGates", method summary:
+ * threshold or TopK on the soft block scores; the budget is a user knob,
+ * rebuttal "Weakness 1 (How to choose sparsity?)").
+ */
+int seer_build_mask_need(const float* scores, int B, int H, int nQB, int nKB, int mode,
+                         float threshold, double density, int keep_sink, int32_t* kv_idx,
+                         int32_t* kv_cnt, int32_t* kv_need, int max_k, void* stream);
+
+/* Flag bits written by seer_validate_lists (OR-ed per row and over all rows). */
+#define SEER_LIST_BAD_COUNT 1 /* kv_cnt < 0 or > max_k (the calls read it clamped to [0, max_k]) */
+#define SEER_LIST_BAD_ENTRY 2 /* a counted entry outside [0, r] (the calls skip it) */
+#define SEER_LIST_REPEAT 4    /* a block counted twice in one row (it would be accumulated twice) */
+#define SEER_LIST_UNSORTED 8  /* counted entries not strictly ascending (allowed; never written
+                                 by seer_build_mask) */
+#define SEER_LIST_CAPACITY 16 /* kv_need > max_k: a threshold row was cut to max_k */
+
+/*
+ * Checks block lists in the [Seq/Block, TopK] layout of the rebuttal
+ * "SeerAttention: Learning Intrinsic Sparse Attention in Your LLMs", "Weakness 2
+ * (Memory complexity)" against what the sparse prefill requires: row r (of nB
+ * rows per head) may list blocks 0..r, each at most once, among its first
+ * min(max(kv_cnt, 0), max_k) entries.
+ *
+ * kv_idx    device int32 [B, H, nB, max_k]; kv_cnt device int32 [B, H, nB].
+ * kv_need   device int32 [B, H, nB] as written by seer_build_mask_need, or NULL
+ *           (then SEER_LIST_CAPACITY is never set).
+ * row_flags device int32 out [B, H, nB] (the row's flag bits), or NULL.
+ * flags     device int32 out, one element: the OR of every row's flags (the
+ *           call clears it first, on the stream).
+ * Repeats are found in any order for rows r < 8192; in longer rows only when
+ * the repeated entries are adjacent.  Asynchronous on `stream`: read `flags`
+ * after the stream has completed (seer_list_flags_status turns them into a
+ * status).  Errors: SEER_ERR_INVALID_ARG for negative sizes, max_k < 1 or a
+ * NULL kv_idx / kv_cnt / flags; SEER_ERR_UNSUPPORTED if B*H*nB exceeds int range.
+ */
+int seer_validate_lists(const int32_t* kv_idx, const int32_t* kv_cnt, const int32_t* kv_need,
+                        int B, int H, int nB, int max_k, int32_t* row_flags, int32_t* flags,
+                        void* stream);
+
+/* Host only: the status a set of list flags amounts to -- SEER_ERR_CAPACITY if
+ * a row was cut (SEER_LIST_CAPACITY), else SEER_ERR_INVALID_ARG if a block is
+ * repeated (SEER_LIST_REPEAT, the one violation that changes results), else
+ * SEER_OK (counts and entries outside the rules are clamped and skipped by the
+ * calls, and any order is accepted). */
+int seer_list_flags_status(int flags);
+
 /* Bytes of device workspace seer_sparse_prefill needs (work list of the
  * load-balancing schedule).  Returns 0 for invalid sizes. */
 size_t seer_sparse_prefill_workspace_size(int B, int Hq, int Hkv, int T);

@@ -38,7 +38,9 @@ themselves live in ``tests/test_oracle_*.py``.
 """
 
 from .mask import (MODE_THRESHOLD, MODE_TOPK, forced_blocks, topk_count, select_row,
-                   build_mask_ref, mask_rows_ref)
+                   build_mask_ref, mask_rows_ref, row_need, build_mask_need_ref,
+                   validate_row_ref, validate_lists_ref, LIST_BAD_COUNT, LIST_BAD_ENTRY,
+                   LIST_REPEAT, LIST_UNSORTED, LIST_CAPACITY)
 from .attention import (BLOCK, block_probs, allowed_blocks, sparse_attention_ref,
                         sparse_attention_blocks_ref)
 from .pooled import pooled_map_ref, pooled_map_blocks_ref
@@ -49,7 +51,9 @@ from .decode import decode_blocks, select_decode_row, build_mask_decode_ref, spa
 
 __all__ = [
     "MODE_THRESHOLD", "MODE_TOPK", "BLOCK", "forced_blocks", "topk_count", "select_row",
-    "build_mask_ref", "mask_rows_ref", "block_probs", "allowed_blocks",
+    "build_mask_ref", "mask_rows_ref", "row_need", "build_mask_need_ref", "validate_row_ref",
+    "validate_lists_ref", "LIST_BAD_COUNT", "LIST_BAD_ENTRY", "LIST_REPEAT", "LIST_UNSORTED",
+    "LIST_CAPACITY", "block_probs", "allowed_blocks",
     "sparse_attention_ref", "sparse_attention_blocks_ref", "pooled_map_ref",
     "pooled_map_blocks_ref", "pooled_target_ref", "pool_qk", "block_rope", "gate_qk_ref",
     "gate_scores_ref", "rope_at", "decode_gate_scores_ref", "decode_blocks", "select_decode_row", "build_mask_decode_ref",

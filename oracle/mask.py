@@ -26,6 +26,16 @@ Readings where the pages are silent (each also listed in the design notes):
   blocks are cut to the ``max_k - |F_i|`` best by the ranking above.
 * The list of each row is written in ascending block order and padded with -1
   up to ``max_k``; ``cnt`` holds the list length.
+* A row's "need" is the number of blocks the rule selects before any cut to
+  ``max_k``: k_i under TopK, |F_i| plus every passing block under threshold.  A
+  threshold row whose need exceeds ``max_k`` is the capacity overflow the
+  library reports.
+
+List validation (what the sparse calls require of a list, and what a cut
+threshold row looks like) follows the same [Seq/Block, TopK] index layout of
+"Weakness 2 (Memory complexity)": row r of a head may hold blocks 0..r; the
+calls read a count clamped to [0, max_k], skip entries outside [0, r], and
+accept any order, but a block listed twice would be accumulated twice.
 """
 
 from __future__ import annotations
@@ -87,6 +97,74 @@ def select_row(row_scores: np.ndarray, i: int, mode: int, threshold: float,
     else:
         raise ValueError(f"unknown mode {mode}")
     return sorted(chosen)
+
+
+def row_need(row_scores: np.ndarray, i: int, mode: int, threshold: float, density: float,
+             keep_sink: bool) -> int:
+    """Blocks query block i selects before any cut to max_k."""
+    row = np.asarray(row_scores, dtype=np.float32)
+    forced = forced_blocks(i, keep_sink)
+    if mode == MODE_TOPK:
+        return topk_count(i, density, keep_sink)
+    tau = np.float32(threshold)
+    return len(forced) + sum(1 for j in range(i + 1) if j not in forced and bool(row[j] >= tau))
+
+
+def build_mask_need_ref(scores: np.ndarray, mode: int, threshold: float, density: float,
+                        keep_sink: bool, max_k: int):
+    """build_mask_ref plus need [B,H,nQB] int32 (see row_need)."""
+    idx, cnt = build_mask_ref(scores, mode, threshold, density, keep_sink, max_k)
+    scores = np.asarray(scores, dtype=np.float32)
+    bsz, heads, nqb, _ = scores.shape
+    need = np.zeros((bsz, heads, nqb), dtype=np.int32)
+    for b in range(bsz):
+        for h in range(heads):
+            for i in range(nqb):
+                need[b, h, i] = row_need(scores[b, h, i], i, mode, threshold, density, keep_sink)
+    return idx, cnt, need
+
+
+LIST_BAD_COUNT = 1   # cnt < 0 or cnt > max_k
+LIST_BAD_ENTRY = 2   # a counted entry outside [0, r]
+LIST_REPEAT = 4      # a block counted twice in one row
+LIST_UNSORTED = 8    # counted entries not strictly ascending
+LIST_CAPACITY = 16   # need > max_k
+
+
+def validate_row_ref(entries, count: int, r: int, max_k: int, need=None) -> int:
+    """Flag bits of one list row r (entries: the row's max_k stored values)."""
+    f = 0
+    if count < 0 or count > max_k:
+        f |= LIST_BAD_COUNT
+    if need is not None and need > max_k:
+        f |= LIST_CAPACITY
+    n = min(max(count, 0), max_k)
+    seen = set()
+    for x in range(n):
+        e = int(entries[x])
+        if e < 0 or e > r:
+            f |= LIST_BAD_ENTRY
+        elif e in seen:
+            f |= LIST_REPEAT
+        else:
+            seen.add(e)
+        if x > 0 and e <= int(entries[x - 1]):
+            f |= LIST_UNSORTED
+    return f
+
+
+def validate_lists_ref(idx: np.ndarray, cnt: np.ndarray, need, max_k: int):
+    """Per-row flags [B,H,nB] and their OR over all rows."""
+    idx = np.asarray(idx)
+    cnt = np.asarray(cnt)
+    bsz, heads, nb = cnt.shape
+    flags = np.zeros((bsz, heads, nb), dtype=np.int32)
+    for b in range(bsz):
+        for h in range(heads):
+            for r in range(nb):
+                nd = None if need is None else int(np.asarray(need)[b, h, r])
+                flags[b, h, r] = validate_row_ref(idx[b, h, r], int(cnt[b, h, r]), r, max_k, nd)
+    return flags, int(np.bitwise_or.reduce(flags.reshape(-1))) if flags.size else 0
 
 
 def build_mask_ref(scores: np.ndarray, mode: int, threshold: float, density: float,

@@ -103,6 +103,53 @@ def test_build_mask_rejects_on_host(args, status):
     assert seer.load().seer_build_mask(*args) == status
 
 
+def test_build_mask_need_rejects_on_host():
+    lib = seer.load()
+    ok = (FAKE, 1, 1, 4, 4, 1, 0.0, 0.5, 1, FAKE, FAKE, FAKE, 4, None)
+    bad = [((1,), None),            # null kv_need
+           ((5,), 7),               # mode
+           ((4,), 3),               # nKB < nQB
+           ((7,), 0.0),             # density out of range
+           ((12,), 1)]              # max_k below the TopK budget (ceil(0.5 * 4) = 2 + sink)
+    for (pos,), val in bad:
+        a = list(ok)
+        if pos == 1:
+            a[11] = None
+            want = 1
+        else:
+            a[pos] = val
+            want = 3 if pos == 12 else 1
+        assert lib.seer_build_mask_need(*a) == want, (pos, val)
+    a = list(ok)
+    a[3], a[4], a[12] = 4097, 4097, 4097
+    assert lib.seer_build_mask_need(*a) == 2
+    a = list(ok)
+    a[1] = 0
+    a[11] = None
+    assert lib.seer_build_mask_need(*a) == 0  # nothing to do: nothing needed, nothing launched
+
+
+def test_validate_lists_rejects_on_host():
+    lib = seer.load()
+    v = lambda *a: lib.seer_validate_lists(*a)
+    assert v(FAKE, FAKE, None, -1, 1, 4, 4, None, FAKE, None) == 1
+    assert v(FAKE, FAKE, None, 1, 1, -4, 4, None, FAKE, None) == 1
+    assert v(FAKE, FAKE, None, 1, 1, 4, 0, None, FAKE, None) == 1      # max_k < 1
+    assert v(FAKE, FAKE, None, 1, 1, 4, 4, None, None, None) == 1      # no flags output
+    assert v(None, FAKE, None, 1, 1, 4, 4, None, FAKE, None) == 1
+    assert v(FAKE, None, None, 1, 1, 4, 4, None, FAKE, None) == 1
+    assert v(FAKE, FAKE, None, 1 << 20, 1 << 10, 1 << 10, 4, None, FAKE, None) == 2
+
+
+def test_list_flags_status_host_helper():
+    st = seer.list_flags_status
+    assert st(0) == 0
+    assert st(seer.SEER_LIST_UNSORTED | seer.SEER_LIST_BAD_ENTRY | seer.SEER_LIST_BAD_COUNT) == 0
+    assert st(seer.SEER_LIST_REPEAT) == 1
+    assert st(seer.SEER_LIST_CAPACITY | seer.SEER_LIST_REPEAT) == 3
+    assert st(seer.SEER_LIST_CAPACITY) == 3
+
+
 def _prefill(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, Hq=4, Hkv=2, T=128, D=128, scale=0.1, idx=FAKE,
              cnt=FAKE, max_k=2, o=FAKE, ws=FAKE, wsb=1 << 20, stream=None)

@@ -141,6 +141,77 @@ def test_mask_longest_rows_sampled(n, mode, dens, thr, max_k):
         assert (gc[0, 0] == ks).all()
 
 
+@pytest.mark.parametrize("case", ["c2_cut16", "c2_full", "c1_topk", "thr_sink_cut3"])
+def test_build_mask_need_bitexact(case):
+    """kv_need (blocks selected before the cut to max_k) and the lists, bit for bit
+    against the oracle; a threshold row is cut exactly when kv_need > max_k."""
+    if case.startswith("c2"):
+        w = wl.C2
+        max_k = 16 if case == "c2_cut16" else w.nqb
+    elif case == "c1_topk":
+        w = wl.C1
+        max_k = _oracle_max_k(w)
+    else:
+        w = wl.custom(92, 2, 3, 1, 64, 64 * 37 + 5, mode=wl.MODE_THRESHOLD, threshold=0.01,
+                      keep_sink=True, scores="softmax_normal")
+        max_k = 3
+    announce(f"mask need {case} {w.name} max_k={max_k}")
+    s = wl.make_scores(w)
+    idx, cnt, need = seer.seer_build_mask_need(_dev(s), w.mode, w.threshold, w.density,
+                                               w.keep_sink, max_k)
+    torch.cuda.synchronize()
+    ri, rc, rn = oracle.build_mask_need_ref(s.numpy(), w.mode, w.threshold, w.density,
+                                            w.keep_sink, max_k)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+    assert np.array_equal(cnt.cpu().numpy(), rc)
+    assert np.array_equal(need.cpu().numpy(), rn)
+    cut = rn > max_k
+    if case in ("c2_cut16", "thr_sink_cut3"):
+        assert cut.any()
+    if w.mode == wl.MODE_TOPK or case == "c2_full":
+        assert not cut.any()
+    # validation turns the cut rows into SEER_LIST_CAPACITY, and nothing else
+    flags, rows = seer.seer_validate_lists(idx, cnt, need, row_flags=True)
+    torch.cuda.synchronize()
+    rf = rows.cpu().numpy()
+    assert np.array_equal(rf == seer.SEER_LIST_CAPACITY, cut)
+    assert np.array_equal(rf == 0, ~cut)
+    f = int(flags.item())
+    assert f == (seer.SEER_LIST_CAPACITY if cut.any() else 0)
+    assert seer.list_flags_status(f) == (3 if cut.any() else 0)
+
+
+@pytest.mark.parametrize("mode", ["sorted", "unsorted", "invalid", "dense", "repeats"])
+def test_validate_lists_matches_oracle(mode):
+    """Flag bits of every row, bit for bit against the oracle's list rules."""
+    b, h, nqb = 2, 3, 150
+    max_k = 40
+    announce(f"validate lists {mode}")
+    idx, cnt = _random_lists(7 * nqb + len(mode), b, h, nqb, max_k,
+                             "invalid" if mode == "repeats" else mode)
+    rng = np.random.default_rng(5)
+    need = rng.integers(0, max_k + 3, size=(b, h, nqb)).astype(np.int32)
+    if mode == "repeats":  # copy an entry over a later one in some rows (adjacent or not)
+        for (bb, hh, i) in zip(*np.nonzero(cnt >= 3)):
+            if rng.random() < 0.3:
+                n = min(int(cnt[bb, hh, i]), max_k)
+                x, y = sorted(rng.choice(n, size=2, replace=False))
+                idx[bb, hh, i, y] = idx[bb, hh, i, x]
+    flags, rows = seer.seer_validate_lists(_dev(torch.from_numpy(idx)),
+                                           _dev(torch.from_numpy(cnt)),
+                                           _dev(torch.from_numpy(need)), row_flags=True)
+    torch.cuda.synchronize()
+    rf, fall = oracle.validate_lists_ref(idx, cnt, need, max_k)
+    assert np.array_equal(rows.cpu().numpy(), rf)
+    assert int(flags.item()) == fall
+    if mode == "repeats":
+        assert fall & seer.SEER_LIST_REPEAT
+    # without kv_need the capacity bit is never set
+    flags2 = seer.seer_validate_lists(_dev(torch.from_numpy(idx)), _dev(torch.from_numpy(cnt)))
+    torch.cuda.synchronize()
+    assert int(flags2.item()) == fall & ~seer.SEER_LIST_CAPACITY
+
+
 def test_mask_single_block():
     s = torch.full((2, 3, 1, 1), float("nan"))
     w = wl.custom(91, 2, 3, 3, 64, 64, density=0.1)
@@ -183,27 +254,6 @@ def test_sparse_prefill_workloads(wid):
         blocks = [(0, h, i) for h in range(w.hq) for i in range(w.nqb)]
     else:
         blocks = wl.sample_qblocks(w, 8)
-    ref = oracle.sparse_attention_blocks_ref(q, k, v, idx, cnt, None, blocks)
-    _check_blocks(o, ref, O_TOL, w.name)
-
-
-def test_sparse_prefill_128k_sampled():
-    w = wl.C4
-    announce(f"sparse prefill {w.name} (mask built on the GPU)")
-    q, k, v = wl.make_qkv(w)
-    s = wl.make_scores(w)
-    max_k = seer.topk_budget(w.nqb, w.density, w.keep_sink)
-    idx, cnt = seer.seer_build_mask(_dev(s), w.mode, w.threshold, w.density, w.keep_sink, max_k)
-    o = seer.seer_sparse_prefill(_dev(q), _dev(k), _dev(v), idx, cnt)
-    torch.cuda.synchronize()
-    o, idx, cnt = o.cpu(), idx.cpu().numpy(), cnt.cpu().numpy()
-    blocks = wl.sample_qblocks(w, 6)
-    # The lists used by the oracle are the oracle's own; they equal the GPU's
-    # (checked bit for bit), so the GPU lists are only used once verified here.
-    ref_lists = oracle.mask_rows_ref(s.numpy(), blocks, w.mode, w.threshold, w.density,
-                                     w.keep_sink, max_k)
-    for (b, h, i), want in ref_lists.items():
-        assert idx[b, h, i, : cnt[b, h, i]].tolist() == want
     ref = oracle.sparse_attention_blocks_ref(q, k, v, idx, cnt, None, blocks)
     _check_blocks(o, ref, O_TOL, w.name)
 

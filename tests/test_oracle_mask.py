@@ -32,10 +32,12 @@ def _load_golden():
             if in_scores:
                 rows.append([float(x) for x in line.split()])
             elif line.startswith("case"):
-                head, tail = line.split("|")
+                head, tail, needs = line.split("|")
                 _, mode, dens, thr, sink, max_k = head.split()
                 lists = [[int(x) for x in part.split()] for part in tail.split("-")]
-                cases.append((mode, float(dens), float(thr), bool(int(sink)), int(max_k), lists))
+                need = [int(x) for x in needs.split()]
+                cases.append((mode, float(dens), float(thr), bool(int(sink)), int(max_k), lists,
+                              need))
     n = len(rows)
     s = np.zeros((1, 1, n, n), dtype=np.float32)
     for i, r in enumerate(rows):
@@ -46,13 +48,16 @@ def _load_golden():
 def test_hand_worked_example():
     s, cases = _load_golden()
     assert len(cases) == 5
-    for mode, dens, thr, sink, max_k, lists in cases:
+    for mode, dens, thr, sink, max_k, lists, need in cases:
         m = oracle.MODE_TOPK if mode == "topk" else oracle.MODE_THRESHOLD
-        idx, cnt = oracle.build_mask_ref(s, m, thr, dens, sink, max_k)
+        idx, cnt, got_need = oracle.build_mask_need_ref(s, m, thr, dens, sink, max_k)
+        assert got_need[0, 0].tolist() == need, (mode, dens, thr, sink, max_k)
         for i, want in enumerate(lists):
             assert cnt[0, 0, i] == len(want), (mode, i)
             assert idx[0, 0, i, : len(want)].tolist() == want, (mode, dens, thr, sink, max_k, i)
             assert (idx[0, 0, i, len(want):] == -1).all()
+            # a row is cut exactly when its need exceeds max_k
+            assert (cnt[0, 0, i] < need[i]) == (need[i] > max_k)
 
 
 def _better(sc, a, b):
@@ -178,3 +183,40 @@ def test_generators_are_deterministic():
     q1, k1, v1 = wl.make_qkv(wl.C1)
     q2, _, _ = wl.make_qkv(wl.C1)
     assert q1.equal(q2) and not q1.equal(k1)
+
+
+def test_validate_rows_by_hand():
+    """List validation on hand-made rows (flag meanings of the list rules: row r
+    may hold blocks 0..r, counts clamp to [0, max_k], no block twice)."""
+    v = oracle.validate_row_ref
+    assert v([0, 2, 5, -1], 3, 5, 4) == 0
+    assert v([0, 2, 6, -1], 3, 5, 4) == oracle.LIST_BAD_ENTRY          # 6 > r
+    assert v([-3, 2, 5, -1], 3, 5, 4) == oracle.LIST_BAD_ENTRY       # -3 < 0
+    assert v([2, 2, 5, -1], 3, 5, 4) == oracle.LIST_REPEAT | oracle.LIST_UNSORTED
+    assert v([5, 2, 0, -1], 3, 5, 4) == oracle.LIST_UNSORTED           # any order is allowed
+    assert v([5, 2, 5, -1], 3, 5, 4) == oracle.LIST_REPEAT | oracle.LIST_UNSORTED
+    assert v([0, 1, 2, 3], 9, 5, 4) == oracle.LIST_BAD_COUNT           # read as 4 entries
+    assert v([0, 1, 2, 3], -1, 5, 4) == oracle.LIST_BAD_COUNT
+    assert v([0, 1, -1, -1], 2, 5, 4, need=7) == oracle.LIST_CAPACITY
+    assert v([0, 1, -1, -1], 2, 5, 4, need=4) == 0
+    # entries past the count are never looked at
+    assert v([0, 1, 9, 9], 2, 5, 4) == 0
+
+
+def test_validate_built_lists_are_clean():
+    """Lists the selection rule writes carry no flag except capacity, which is
+    set exactly on the cut threshold rows."""
+    w = wl.custom(91, 1, 3, 1, 64, 64 * 40, mode=wl.MODE_THRESHOLD, threshold=0.02,
+                  keep_sink=True, scores="softmax_normal")
+    s = wl.make_scores(w).numpy()
+    for max_k in (w.nqb, 6):
+        idx, cnt, need = oracle.build_mask_need_ref(s, w.mode, w.threshold, w.density,
+                                                    w.keep_sink, max_k)
+        flags, all_flags = oracle.validate_lists_ref(idx, cnt, need, max_k)
+        cut = need > max_k
+        assert ((flags == oracle.LIST_CAPACITY) == cut).all()
+        assert ((flags == 0) == ~cut).all()
+        if max_k == w.nqb:
+            assert all_flags == 0
+        else:
+            assert cut.any() and all_flags == oracle.LIST_CAPACITY
