@@ -15,6 +15,7 @@ from .binding import (BLOCK, SEER_MASK_THRESHOLD, SEER_MASK_TOPK, SeerError, loa
                       seer_pooled_target_mse, seer_sparse_prefill, seer_sparse_prefill_block,
                       sparse_prefill_workspace_size, topk_budget, version,
                       seer_build_mask_need, seer_validate_lists, list_flags_status,
+                      seer_sparse_prefill_noalloc,
                       SEER_LIST_BAD_COUNT, SEER_LIST_BAD_ENTRY, SEER_LIST_REPEAT,
                       SEER_LIST_UNSORTED, SEER_LIST_CAPACITY)
 
@@ -30,6 +31,6 @@ __all__ = [
     "pooled_attn_map_workspace_size", "seer_build_mask", "seer_pooled_attn_map",
     "seer_pooled_target_mse", "seer_sparse_prefill", "seer_sparse_prefill_block",
     "sparse_prefill_workspace_size", "topk_budget", "version", "seer_build_mask_need",
-    "seer_validate_lists", "list_flags_status", "SEER_LIST_BAD_COUNT", "SEER_LIST_BAD_ENTRY",
+    "seer_validate_lists", "list_flags_status", "seer_sparse_prefill_noalloc", "SEER_LIST_BAD_COUNT", "SEER_LIST_BAD_ENTRY",
     "SEER_LIST_REPEAT", "SEER_LIST_UNSORTED", "SEER_LIST_CAPACITY",
 ]

@@ -30,7 +30,7 @@ EXPORTED = (
     "seer_attn_gate_mask", "seer_attn_gate_decode_keys_workspace_size", "seer_attn_gate_decode_keys",
     "seer_attn_gate_decode_scores", "seer_attn_gate_decode_mask", "seer_build_mask_decode",
     "seer_sparse_decode_workspace_size", "seer_sparse_decode", "seer_build_mask_need",
-    "seer_validate_lists", "seer_list_flags_status",
+    "seer_validate_lists", "seer_list_flags_status", "seer_sparse_prefill_noalloc",
 )
 
 SEER_LIST_BAD_COUNT = 1
@@ -75,6 +75,10 @@ def load() -> ctypes.CDLL:
     lib.seer_validate_lists.restype = c_int
     lib.seer_validate_lists.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int,
                                         c_void, c_void, c_void]
+    lib.seer_sparse_prefill_noalloc.restype = c_int
+    lib.seer_sparse_prefill_noalloc.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int,
+                                                c_int, c_float, c_void, c_void, c_int, c_void,
+                                                c_void]
     lib.seer_list_flags_status.restype = c_int
     lib.seer_list_flags_status.argtypes = [c_int]
     lib.seer_sparse_prefill_workspace_size.restype = c_size
@@ -294,6 +298,25 @@ def seer_sparse_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_id
     _check("seer_sparse_prefill", lib.seer_sparse_prefill(
         _ptr(q), _ptr(k), _ptr(v), *dims, _ptr(kv_idx), _ptr(kv_cnt), max_k, _ptr(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def seer_sparse_prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                kv_idx: torch.Tensor, kv_cnt: torch.Tensor, out: torch.Tensor,
+                                sm_scale: Optional[float] = None, stream=None) -> torch.Tensor:
+    """seer_sparse_prefill without a workspace (the library's static scratch holds
+    the work list); `out` is the caller's bf16 [B,Hq,T,D] output."""
+    lib = load()
+    b, hq, hkv, t, d = _qkv_dims(q, k, v)
+    nb = (t + BLOCK - 1) // BLOCK
+    max_k = kv_idx.shape[-1]
+    _need(kv_idx, "kv_idx", torch.int32, (b, hq, nb, max_k))
+    _need(kv_cnt, "kv_cnt", torch.int32, (b, hq, nb))
+    _need(out, "out", torch.bfloat16, (b, hq, t, d))
+    scale = (1.0 / d ** 0.5) if sm_scale is None else float(sm_scale)
+    _check("seer_sparse_prefill_noalloc", lib.seer_sparse_prefill_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), b, hq, hkv, t, d, scale, _ptr(kv_idx), _ptr(kv_cnt),
+        int(max_k), _ptr(out), _stream(stream)))
     return out
 
 

@@ -6,8 +6,19 @@
 #include <limits.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "seer_internal.h"
+
+// Scratch of the no-allocation prefill entry point: the schedule's work list
+// (16 bytes per 64-row item) for up to kNoAllocItems items.  Each GPU the
+// library runs on holds one copy until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in): the
+// device address comes from hipGetSymbolAddress, once per device.
+namespace {
+constexpr long long kNoAllocItems = 1 << 18;
+}
+static __device__ __align__(256) int32_t scratch[4 * kNoAllocItems];
 
 namespace {
 
@@ -35,6 +46,26 @@ int attention_args(const void* q, const void* k, const void* v, const void* o, i
   if (!q || !k || !v || !o) return SEER_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return SEER_ERR_INVALID_ARG;
+  return SEER_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept for later calls.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SEER_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SEER_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SEER_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return SEER_OK;
 }
 
@@ -165,6 +196,24 @@ int seer_sparse_prefill(const void* q, const void* k, const void* v, int B, int 
                         size_t workspace_bytes, void* stream) {
   return seer_sparse_prefill_block(q, k, v, B, Hq, Hkv, T, D, sm_scale, SEER_BLOCK, kv_idx,
                                    kv_cnt, max_k, o, workspace, workspace_bytes, stream);
+}
+
+int seer_sparse_prefill_noalloc(const void* q, const void* k, const void* v, int B, int Hq,
+                                int Hkv, int T, int D, float sm_scale, const int32_t* kv_idx,
+                                const int32_t* kv_cnt, int max_k, void* o, void* stream) {
+  const int st = attention_args(q, k, v, o, B, Hq, Hkv, T, D, sm_scale);
+  if (st != SEER_OK) return st;
+  if (max_k < 1) return SEER_ERR_INVALID_ARG;
+  if ((long long)B * T == 0) return SEER_OK;
+  if (!kv_idx || !kv_cnt) return SEER_ERR_INVALID_ARG;
+  if ((long long)B * Hq * nqb_of(T) > kNoAllocItems) return SEER_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int at = scratch_address(&ws);
+  if (at != SEER_OK) return at;
+  const hipError_t err =
+      seer::launch_sparse_prefill(q, k, v, B, Hq, Hkv, T, D, sm_scale, SEER_BLOCK, kv_idx, kv_cnt,
+                                  max_k, static_cast<int32_t*>(ws), o, (hipStream_t)stream);
+  return err == hipSuccess ? SEER_OK : SEER_ERR_HIP;
 }
 
 size_t seer_pooled_attn_map_workspace_size(int B, int Hq, int T) {

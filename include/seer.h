@@ -208,6 +208,22 @@ int seer_sparse_prefill_block(const void* q, const void* k, const void* v, int B
 
 /* Bytes of device workspace seer_pooled_attn_map needs: the stored per-row
  * block maxima r_ij (fp32, 64 per causal (i, j) tile).  0 for invalid sizes. */
+/*
+ * seer_sparse_prefill for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments minus the workspace, and the same kernels and results.  The
+ * schedule's work list lives in a static device array of the library instead,
+ * sized for B * Hq * nQB <= 262144 items (4 MiB; one copy per GPU, held until
+ * the process ends); larger problems return SEER_ERR_WORKSPACE before any
+ * launch.  Its device address is looked up on the first call made with a
+ * device current (the device of `stream`), so make that device current.  The
+ * call allocates nothing.  Calls that overlap on one GPU (other streams, other
+ * host threads) share the array and race: serialise them.
+ */
+int seer_sparse_prefill_noalloc(const void* q, const void* k, const void* v, int B, int Hq,
+                                int Hkv, int T, int D, float sm_scale, const int32_t* kv_idx,
+                                const int32_t* kv_cnt, int max_k, void* o, void* stream);
+
 size_t seer_pooled_attn_map_workspace_size(int B, int Hq, int T);
 
 /*
