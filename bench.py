@@ -158,6 +158,145 @@ def cpu_baseline(w, q, k, v, scores, max_k, blocks_per_head: int):
     }
 
 
+def clock_during(fn, torch, seconds: float = 2.5, settle: float = 1.5) -> dict:
+    """Shader clock and socket power while fn() runs back to back on the GPU: the
+    calling thread keeps launching fn() for `seconds` while a second thread reads
+    the AMD SMI GPU metrics (current gfx clock of each XCD, socket power) every
+    5 ms; readings from the first `settle` seconds are dropped (the metrics lag
+    the load by up to about a second).  The 2516.6
+    TFLOP/s peak assumes the 2400 MHz peak clock; under a sustained MFMA load the
+    clock settles lower, at the power cap."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:  # pragma: no cover - telemetry is optional
+        return {"error": f"amdsmi unavailable: {e}"}
+    fn()
+    torch.cuda.synchronize()
+    stop = threading.Event()
+    samples = []
+
+    def sample():
+        t0 = time.perf_counter()
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            except Exception:  # pragma: no cover
+                break
+            xs = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and c < 65535]
+            p = m.get("current_socket_power")
+            samples.append((time.perf_counter() - t0, statistics.mean(xs) if xs else None,
+                            float(p) if isinstance(p, (int, float)) else None))
+            time.sleep(0.005)
+
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        fn()
+    launched = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    busy = [x for x in samples if settle <= x[0] <= launched]
+    clocks = [c for _, c, _ in busy if c is not None]
+    powers = [p for _, _, p in busy if p is not None]
+    out = {"samples": len(busy)}
+    if clocks:
+        out["gfx_clock_mhz"] = round(statistics.median(clocks), 1)
+    if powers:
+        out["socket_power_w"] = round(statistics.median(powers), 1)
+    try:
+        out["power_cap_w"] = round(amdsmi.amdsmi_get_power_cap_info(h)["power_cap"] / 1e6, 1)
+    except Exception:  # pragma: no cover
+        pass
+    return out
+
+
+def sparse_config_line(seer, wl, torch, dev, w, args) -> dict:
+    """One workload through seer_build_mask + seer_sparse_prefill: mask and prefill
+    time (mean of per-call events), computed-tile TFLOP/s and fraction of the bf16
+    peak, and the same kernel with every causal block listed (density 1.0)."""
+    log(f"[bench] {w.name}")
+    q, k, v = (t.to(dev) for t in wl.make_qkv(w))
+    sd = wl.make_scores(w).to(dev)
+    max_k = seer.topk_budget(w.nqb, w.density, w.keep_sink) if w.mode == wl.MODE_TOPK else w.nqb
+    idx = torch.empty((w.batch, w.hq, w.nqb, max_k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((w.batch, w.hq, w.nqb), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    ws = torch.empty((seer.sparse_prefill_workspace_size(w.batch, w.hq, w.hkv, w.seq),),
+                     dtype=torch.uint8, device=dev)
+    mask = lambda: seer.seer_build_mask(sd, w.mode, w.threshold, w.density, w.keep_sink, max_k,
+                                        kv_idx=idx, kv_cnt=cnt)
+    pre = lambda: seer.seer_sparse_prefill(q, k, v, idx, cnt, out=out, workspace=ws)
+    mask()
+    pre()
+    n = max(3, args.steps // 2)
+    m_ms = time_calls(mask, n, torch)
+    p_ms = time_calls(pre, n, torch)
+    blocks = int(cnt.sum().item())
+    tf = blocks * tile_flops(w.head_dim) / (p_ms * 1e-3) / 1e12
+    res = {
+        "mask": "topk" if w.mode == wl.MODE_TOPK else "threshold",
+        "density": w.density if w.mode == wl.MODE_TOPK else None,
+        "threshold": w.threshold if w.mode == wl.MODE_THRESHOLD else None,
+        "keep_sink": w.keep_sink, "seq_len": w.seq, "q_heads": w.hq, "kv_heads": w.hkv,
+        "head_dim": w.head_dim, "computed_blocks": blocks,
+        "density_eff": round(blocks / (w.batch * w.hq * w.nqb * (w.nqb + 1) / 2), 5),
+        "mask_build_ms": round(m_ms, 4), "sparse_prefill_ms": round(p_ms, 4),
+        "tflops": round(tf, 3), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+    }
+    del idx
+    idx1 = torch.empty((w.batch, w.hq, w.nqb, w.nqb), dtype=torch.int32, device=dev)
+    seer.seer_build_mask(sd, wl.MODE_TOPK, 0.0, 1.0, w.keep_sink, w.nqb, kv_idx=idx1, kv_cnt=cnt)
+    call1 = lambda: seer.seer_sparse_prefill(q, k, v, idx1, cnt, out=out, workspace=ws)
+    call1()
+    d_ms = time_calls(call1, max(2, args.steps // 5), torch)
+    blocks1 = int(cnt.sum().item())
+    res["density1"] = {
+        "prefill_ms": round(d_ms, 4),
+        "tflops": round(blocks1 * tile_flops(w.head_dim) / (d_ms * 1e-3) / 1e12, 3),
+        "speedup": round(d_ms / p_ms, 3), "ideal_speedup": round(blocks1 / blocks, 3)}
+    del q, k, v, sd, idx1, cnt, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_oracle_extrapolated(w, blocks_per_head: int) -> dict:
+    """The oracle (as is) on `blocks_per_head` seeded sampled query blocks per head
+    of w, and that time scaled by the ratio of computed blocks of the whole
+    workload to those of the sample (an extrapolation, labelled as such)."""
+    import numpy as np
+
+    import oracle
+    from block_sparse_attention_prefill_amd import workloads as wl
+
+    q, k, v = wl.make_qkv(w)
+    scores = wl.make_scores(w).numpy()
+    max_k = oracle.topk_count(w.nqb - 1, w.density, w.keep_sink)
+    rows = wl.sample_qblocks(w, blocks_per_head)
+    t0 = time.perf_counter()
+    lists = oracle.mask_rows_ref(scores, rows, w.mode, w.threshold, w.density, w.keep_sink,
+                                 max_k)
+    idx = np.full((w.batch, w.hq, w.nqb, max_k), -1, np.int32)
+    cnt = np.zeros((w.batch, w.hq, w.nqb), np.int32)
+    for (b, h, i), sel in lists.items():
+        idx[b, h, i, : len(sel)] = sel
+        cnt[b, h, i] = len(sel)
+    oracle.sparse_attention_blocks_ref(q, k, v, idx, cnt, None, rows)
+    dt = time.perf_counter() - t0
+    sample_blocks = int(cnt.sum())
+    total_blocks = sum(oracle.topk_count(i, w.density, w.keep_sink) for i in range(w.nqb)) \
+        * w.batch * w.hq
+    return {"sample": f"{len(rows)} seeded query blocks ({blocks_per_head} per head)",
+            "sample_s": round(dt, 2), "sample_blocks": sample_blocks,
+            "tflops": round(sample_blocks * tile_flops(w.head_dim) / dt / 1e12, 6),
+            "extrapolated_full_s": round(dt * total_blocks / sample_blocks, 1),
+            "extrapolation": "sample time x (computed blocks of the workload / of the sample)"}
+
+
 def decode_bench(seer, wl, torch, dev, args):
     import dataclasses
     import numpy as np
@@ -395,6 +534,14 @@ def main(argv=None) -> int:
         },
     }
 
+    # Shader clock and socket power during sustained prefill calls (not timed).
+    log("[bench] clock during sustained prefill")
+    clk = clock_during(prefill, torch)
+    result["clock_during_prefill"] = clk
+    if "gfx_clock_mhz" in clk:
+        peak_at = PEAK_BF16_TFLOPS * clk["gfx_clock_mhz"] / 2400.0
+        result["roofline"]["frac_at_measured_clock"] = round(achieved / peak_at, 4)
+
     if not args.no_extras:
         # The prefill call with L2 and the 256 MB MALL flushed before each call (a
         # 1 GiB read), so that K/V start in HBM: median, min and max.
@@ -540,6 +687,11 @@ def main(argv=None) -> int:
         }
         del s128, idx128, cnt128
 
+        # The other sparse workloads at their stated shapes: 8k with threshold 2e-3
+        # lists, and 128k with TopK 0.17 lists.
+        result["c2_t8192_threshold"] = sparse_config_line(seer, wl, torch, dev, wl.C2, args)
+        result["c4_t131072_topk0.17"] = sparse_config_line(seer, wl, torch, dev, wl.C4, args)
+
         # Decode: one new token per sequence over a 40k-token cache, 4K-token budget
         # (90 % sparsity), lists per KV group and per query head.  HBM-bound: the
         # algorithmic bytes are the K and V rows of each KV group's selected blocks
@@ -549,6 +701,11 @@ def main(argv=None) -> int:
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, scores, max_k, args.cpu_blocks_per_head)
+        if not args.no_extras and "c4_t131072_topk0.17" in result:
+            log("[bench] CPU oracle on the 128k workload's sampled blocks")
+            del q, k, v, scores
+            result["c4_t131072_topk0.17"]["cpu_oracle"] = cpu_oracle_extrapolated(
+                wl.C4, wl.C4.sample_qblocks)
 
     print(json.dumps(result), flush=True)
     return 0

@@ -1065,12 +1065,13 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
       [&](int r, int it) {
         int4 e = {-1, 0, -1, 0};
         if (it >= 0) {
-          const int n = len_of(it);
           const int32_t* lst = idx + row_of(it) * (size_t)max_k;
+          const int j0 = lst[0];  // requested with the count (max_k >= 1)
+          const int n = len_of(it);
           const int i = it % nqb, ib = i / bs;
           int x = 0, tile = -1;
           for (; x < bs * n; ++x) {  // first usable position (normally x = 0)
-            const int j = lst[x / bs];
+            const int j = x < bs ? j0 : lst[x / bs];
             const int t = bs * j + x % bs;
             if (j >= 0 && j <= ib && t <= i) {
               tile = t;

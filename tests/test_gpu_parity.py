@@ -1058,6 +1058,37 @@ def test_sparse_decode_parity(case):
             assert (got[b] == 0).all()
 
 
+def test_sparse_decode_workspace_reuse():
+    """One workspace reused across decode calls of different shapes (per-head and
+    per-KV-head lists, several chunks per KV group): every call equals the same call
+    on a fresh workspace bit for bit (nothing from an earlier call leaks in)."""
+    cases = [("gqa4_d128_long", dict(batch=3, hq=8, hkv=2, tmax=9000, d=128,
+                                     kv_lens=(9000, 4000, 1), block=64, list_heads="q"), 60),
+             ("gqa4_d128_kv", dict(batch=2, hq=8, hkv=2, tmax=9000, d=128,
+                                   kv_lens=(8000, 9000), block=64, list_heads="kv"), 100),
+             ("gqa2_d64_b128", dict(batch=1, hq=4, hkv=2, tmax=3000, d=64, kv_lens=(2999,),
+                                    block=128, list_heads="q"), 20)]
+    big = max(seer.sparse_decode_workspace_size(c["batch"], c["hq"], c["hkv"], c["tmax"], c["d"],
+                                                c["hq"] if c["list_heads"] == "q" else c["hkv"],
+                                                mk, c["block"]) for _, c, mk in cases)
+    ws = torch.full((big,), 0x7F, dtype=torch.uint8, device="cuda")  # garbage to start from
+    for rep in range(2):
+        for n, (name, c, max_k) in enumerate(cases):
+            announce(f"decode workspace reuse {name} rep {rep}")
+            dw = _decode_case(120 + n, **c)
+            q, k, v, kv_len = wl.make_decode_inputs(dw)
+            idx, cnt = _decode_lists(dw.wid + rep, dw, max_k)
+            args = (_dev(q), _dev(k), _dev(v), _dev(kv_len), _dev(torch.from_numpy(idx)),
+                    _dev(torch.from_numpy(cnt)), dw.block)
+            fresh = seer.seer_sparse_decode(*args)
+            reused = seer.seer_sparse_decode(*args, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(fresh.view(torch.int16), reused.view(torch.int16)), name
+            ref = oracle.sparse_decode_ref(q, k, v, dw.kv_lens, idx, cnt,
+                                           1.0 / math.sqrt(dw.head_dim), dw.block)
+            assert float(np.abs(reused.float().cpu().numpy() - ref).max()) <= O_TOL
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_decode_seeded_sweep(seed):
     """Seeded random decode steps (ragged lengths including empty and one-token
