@@ -10,18 +10,24 @@
 // are a softmax ("Question 2: (Row-Normalization of Max-Pooled Attention
 // Map)").  Threshold or TopK on these scores (seer_build_mask) gives the mask.
 //
-// Prefill kernels:
+// Prefill kernels, up to 2048 query blocks (rows whose logits fit in LDS):
+// * gate_pool_project_kernel: the pooling pass over Q and K; K~ (linear layer
+//   and block RoPE on the fp32 matrix cores) for every block, the pooled Q means.
+// * gate_qproj_kernel: Q~ from the pooled Q means.
+// * gate_rows_kernel: per group of 16 query blocks, the causal logits Q~ K~^T
+//   (fp32 matrix cores) into LDS, the exact row softmax, the score rows written
+//   once; the fused variant selects each row's block list from the same values.
+// RoPE angles are formed and reduced in fp64 so that far block positions keep
+// their accuracy.
+// Longer rows (the logits go through HBM):
 // * gate_pool_kernel: one wave per (batch, head, 64-token block) pools the block
 //   (non-temporal 16-byte loads all in flight, lane shuffles to combine).
 // * gate_project_kernel: one workgroup per (batch, head, 64 blocks) applies the
-//   head's linear layer on the fp32 matrix cores (v_mfma_f32_32x32x2f32, fp32
-//   operands and accumulation) and the block RoPE, whose angles are formed and
-//   reduced in fp64 so that far block positions keep their accuracy.
+//   head's linear layer (v_mfma_f32_32x32x2f32) and the block RoPE.
 // * gate_logits_kernel: one workgroup per causal 64 x 64 tile of block pairs
-//   (Q~ K~^T on the fp32 matrix cores) writes the scaled logits and each row's
-//   tile max and sum of exponentials; gate_softmax_kernel
-//   then combines a row's partials in a fixed order and normalises the row in
-//   place, zeros above the diagonal.
+//   writes the scaled logits and each row's tile max and sum of exponentials;
+//   gate_softmax_kernel then combines a row's partials in a fixed order and
+//   normalises the row in place, zeros above the diagonal.
 // * gate_softmax_mask_kernel: the same softmax straight into the row selection of
 //   the mask build (mask_select.h); with a small workspace the logits are made
 //   and selected in passes over tile rows.
@@ -122,17 +128,32 @@ __global__ __launch_bounds__(64 * kPoolWaves) void gate_pool_kernel(
 }
 
 // Rotary pair (x1, x2) at block position pos with frequency inv_freq: the angle
-// is formed and reduced mod 2 pi in fp64, sin and cos of the reduced angle are
-// fp32.
+// is formed and reduced mod 2 pi in fp64 (the multiple of 2 pi taken off is the
+// nearest integer to the angle times 1 / (2 pi); near a half turn either
+// neighbour leaves |r| <= pi + a few ulp, which sin and cos take as accurately),
+// sin and cos of the reduced angle are fp32.
 __device__ __forceinline__ void rope_rotate(double inv_freq, int pos, float x1, float x2,
                                             float& y1, float& y2) {
   const double two_pi = 6.283185307179586476925287;
+  const double inv_two_pi = 0.159154943091895335768883763;
   const double ang = (double)pos * inv_freq;
-  const float r = (float)(ang - two_pi * rint(ang / two_pi));
+  const float r = (float)(ang - two_pi * rint(ang * inv_two_pi));
   float sn, cs;
   sincosf(r, &sn, &cs);
   y1 = x1 * cs - x2 * sn;
   y2 = x2 * cs + x1 * sn;
+}
+
+// Rotary frequencies rope_base^(-2e/Dg), e < Dg/2, formed on the host in fp64
+// and passed by value (a kernel argument): no per-lane pow on the device.
+struct RopeFreqs {
+  double f[64];
+};
+
+RopeFreqs rope_freqs(float rope_base, int dg) {
+  RopeFreqs r{};
+  for (int e = 0; e < dg / 2 && e < 64; ++e) r.f[e] = pow((double)rope_base, -2.0 * e / (double)dg);
+  return r;
 }
 
 // Linear layer + block RoPE on the fp32 matrix cores.  One workgroup (two
@@ -518,6 +539,527 @@ __global__ __launch_bounds__(64 * kRowWaves) void gate_softmax_mask_kernel(
   const int count = rowsel::wave_select_row<NPL>(key, n, k, npos, lane, hist_all[wv],
                                                  idx + (size_t)row * max_k, max_k);
   if (lane == 0) cnt[row] = count;
+}
+
+// ---------------------------------------------------------------------------
+// Prefill gate for nQB <= kRowsMaxBlocks: three kernels, the logits never leave
+// the chip.
+//
+// gate_pool_project_kernel: the pooling pass over Q and K (the HBM-bound part).
+// K workgroups (first in the grid) take 16 consecutive blocks of one KV head,
+// 2 per wave, pooled into LDS; then the 16 rows go through the head's linear
+// layer on v_mfma_f32_16x16x4f32 (fp32 operands and accumulation) and the block
+// RoPE: wave w computes RoPE tile pair w % P (16-column tiles holding columns e
+// and e + Dg/2 in the same lane) over input-dim slice w / P, the slices summed
+// in order through LDS.  At MFMA step s, lane group kg = lane / 16 feeds dim
+// 16 (s / 4) + 4 kg + s % 4 of its row (one 16-byte LDS read per 4 steps) and
+// the weight row of the same dim (any assignment of dims to k-slots works as
+// long as both operands use it).  Q workgroups take 8 blocks, one per wave, and
+// write the means (the linear layer is gate_qproj_kernel's): a short chain per
+// workgroup keeps the pass's tail short.
+constexpr int kPPWaves = 8;
+constexpr int kPPRows = 16;   // pooled rows (blocks) per workgroup
+constexpr int kPoolSplit = 2;  // loads of a block issued in this many batches
+
+// Pools block i of one head's rows src [T, D] into dst (Q: the D means; K: the
+// D maxima then the D minima).  Lanes L < D / 8 write; a block at or past nqb
+// gives zeros.
+template <int D>
+__device__ __forceinline__ void pool_block_lds(const __bf16* __restrict__ src, int T, int i,
+                                               int nqb, bool is_q, int lane, float* dst) {
+  constexpr int C = D / 8;   // chunks per row
+  constexpr int R = 64 / C;  // rows read together by the wave
+  constexpr int kPerLane = kTile / R;
+  const int ch = lane % C, rg = lane / C;
+  float a[8], m[8];
+  if (i >= nqb) {
+    if (rg == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dst[8 * ch + e] = 0.f;
+        if (!is_q) dst[D + 8 * ch + e] = 0.f;
+      }
+    }
+    return;
+  }
+  const int r0 = kTile * i, r1 = min(r0 + kTile, T);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = is_q ? 0.f : -INFINITY;
+    m[e] = INFINITY;
+  }
+  // kPoolSplit batches of kPerLane / kPoolSplit loads, all of a batch in flight at once.
+  constexpr int H = kPerLane / kPoolSplit;
+#pragma unroll 1
+  for (int h = 0; h < kPoolSplit; ++h) {
+    bf16x8 x[H];
+#pragma unroll
+    for (int u = 0; u < H; ++u) {
+      // Rows past a short last block re-read its last row (not used): the loads
+      // stay unconditional, so none waits on another.  Read once: non-temporal,
+      // so they do not displace reused data in L2.
+      const int r = min(r0 + rg + R * (H * h + u), r1 - 1);
+      x[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const bf16x8*>(src + (size_t)r * D + 8 * ch));
+    }
+#pragma unroll
+    for (int u = 0; u < H; ++u) {
+      if (r0 + rg + R * (H * h + u) >= r1) continue;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = (float)x[u][e];
+        if (is_q) {
+          a[e] += v;
+        } else {
+          a[e] = fmaxf(a[e], v);
+          m[e] = fminf(m[e], v);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = C; off < 64; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float ao = __shfl_xor(a[e], off, 64);
+      const float mo = __shfl_xor(m[e], off, 64);
+      a[e] = is_q ? a[e] + ao : fmaxf(a[e], ao);
+      m[e] = fminf(m[e], mo);
+    }
+  if (rg == 0) {
+    if (is_q) {
+      const float inv = 1.0f / (float)(r1 - r0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[8 * ch + e] = a[e] * inv;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dst[8 * ch + e] = a[e];
+        dst[D + 8 * ch + e] = m[e];
+      }
+    }
+  }
+}
+
+// Occupancy floor (waves per SIMD, at most 80 registers a lane): three
+// 8-wave workgroups per CU keep enough pooling loads in flight.
+constexpr int kPPWavesPerEU = 6;
+template <int D, int DG>
+__global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(kPPWavesPerEU)))
+void gate_pool_project_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, int B, int Hq, int Hkv, int T,
+    int nqb, const float* __restrict__ wk, RopeFreqs freqs, float* __restrict__ pq,
+    float* __restrict__ kt) {
+  constexpr int LDR = 2 * D + 4;  // padded LDS row (floats), room for a K row
+  __shared__ __attribute__((aligned(16))) float prow[kPPRows][LDR];
+  __shared__ float part[kPPWaves][2][4][64];  // each wave's share of the 16 x 2 x 16 products
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int ng = (nqb + kPPRows - 1) / kPPRows;
+  // B (Hq + Hkv) nQB < 2^31 (checked by the host layer): 32-bit unit arithmetic.
+  const int kunits = B * Hkv * ng;
+  if ((int)blockIdx.x >= kunits) {
+    // Q: kPPWaves blocks per workgroup, one per wave, means to pq (the rows
+    // kernel applies the linear layer).
+    const int u = (int)blockIdx.x - kunits;
+    const int nq8 = (nqb + kPPWaves - 1) / kPPWaves;
+    const int bh = u / nq8, i = kPPWaves * (u % nq8) + wv;
+    if (i < nqb)
+      pool_block_lds<D>(q + (size_t)bh * T * D, T, i, nqb, true, lane,
+                        pq + ((size_t)bh * nqb + i) * D);
+    return;
+  }
+  const int g = (int)blockIdx.x % ng, bh = (int)blockIdx.x / ng;  // bh = b * Hkv + head
+  const int head = bh % Hkv;
+  const int din = 2 * D;
+  const __bf16* src = k + (size_t)bh * T * D;
+#pragma unroll 1
+  for (int t = 0; t < kPPRows / kPPWaves; ++t) {
+    const int r = (kPPRows / kPPWaves) * wv + t;
+    pool_block_lds<D>(src, T, kPPRows * g + r, nqb, false, lane, &prow[r][0]);
+  }
+  __syncthreads();
+  // Wave w: RoPE tile pair w % P (tiles w % P and w % P + Dg/32, columns e and
+  // e + Dg/2), input dims of slice w / P of S (16-dim groups tb .. te - 1), the
+  // weights of CB groups requested together.  The S slices' products are summed
+  // in slice order through LDS.
+  constexpr int P = DG / 32;
+  constexpr int S = kPPWaves / P;
+  constexpr int CB = 4;  // 16-dim groups whose weights are requested together
+  const int pr = wv % P, ps = wv / P;
+  const float* w = wk + (size_t)head * din * DG;
+  const int r = lane & 15, kg = lane >> 4;
+  const int col0 = 16 * pr + r, col1 = col0 + DG / 2;
+  const int nt = din / 16;
+  const int tb = ps * nt / S, te = (ps + 1) * nt / S;
+  f32x4 acc0 = {}, acc1 = {};
+  // Groups past the slice's end (a short last batch) re-read its last group
+  // and enter with zero rows: straight-line loads, none waiting on another.
+#pragma unroll 1
+  for (int t0 = tb; t0 < te; t0 += CB) {
+    float wr[CB][8];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const int t = min(t0 + c, te - 1);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const float* wrow = w + (size_t)(16 * t + 4 * kg + qq) * DG;
+        wr[c][qq] = wrow[col0];
+        wr[c][4 + qq] = wrow[col1];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const int t = min(t0 + c, te - 1);
+      f32x4 av = *reinterpret_cast<const f32x4*>(&prow[r][16 * t + 4 * kg]);
+      if (t0 + c >= te) av = f32x4{};
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[qq], wr[c][qq], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[qq], wr[c][4 + qq], acc1, 0, 0, 0);
+      }
+    }
+  }
+  // acc[v]: row 4 kg + v of the group, column col0 (acc0) or col1 (acc1).
+  if constexpr (S > 1) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      part[wv][0][v][lane] = acc0[v];
+      part[wv][1][v][lane] = acc1[v];
+    }
+    __syncthreads();
+    if (ps != 0) return;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      acc0[v] = part[pr][0][v][lane];
+      acc1[v] = part[pr][1][v][lane];
+    }
+#pragma unroll 1
+    for (int s2 = 1; s2 < S; ++s2)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        acc0[v] += part[pr + P * s2][0][v][lane];
+        acc1[v] += part[pr + P * s2][1][v][lane];
+      }
+  }
+  float* out = kt + (size_t)bh * nqb * DG;
+  const double inv_freq = freqs.f[col0];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int i = kPPRows * g + 4 * kg + v;
+    float y1, y2;
+    rope_rotate(inv_freq, i, acc0[v], acc1[v], y1, y2);
+    if (i < nqb) {
+      out[(size_t)i * DG + col0] = y1;
+      out[(size_t)i * DG + col1] = y2;
+    }
+  }
+}
+
+// gate_qproj_kernel: Q~ = rope(Qp Wq[h]) for 64 pooled query rows (four groups
+// of 16) of one (batch, head) per workgroup of 8 waves.  The head's weights go
+// through LDS in two halves of 64 dims, all their 16-byte loads (and the rows')
+// in flight at once; wave w computes RoPE tile pair w % P (columns e and
+// e + Dg/2) for the row groups w / P, w / P + 8 / P, ... on
+// v_mfma_f32_16x16x4f32 (dims assigned to k-slots as in
+// gate_pool_project_kernel), each weight read from LDS feeding every row group
+// it serves, then the block RoPE.  With D = 64 the second half re-reads the
+// first (unused); rows past nQB re-read the last row (not written).
+constexpr int kQPRows = 64;
+constexpr int kQPThreads = 512;
+
+template <int DG>
+__global__ __launch_bounds__(kQPThreads) void gate_qproj_kernel(const float* __restrict__ pq,
+                                                                const float* __restrict__ wq,
+                                                                int D, int Hq, int nqb,
+                                                                RopeFreqs freqs,
+                                                                float* __restrict__ qt) {
+  constexpr int NW = kQPThreads / 64;
+  constexpr int WLD = DG + 4;                      // padded weight row in LDS (floats)
+  constexpr int WPT = 64 * DG / 4 / kQPThreads;    // 16-byte weight loads per thread and half
+  constexpr int P = DG / 32;                       // RoPE tile pairs
+  constexpr int NRG = kQPRows / 16;                // row groups
+  constexpr int RPW = P * NRG >= NW ? P * NRG / NW : 1;  // row groups per wave
+  constexpr int RGS = NW / P;                      // row-group stride between a wave's groups
+  __shared__ __attribute__((aligned(16))) float wl[64 * WLD];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int r = lane & 15, kg = lane >> 4;
+  const int pr = wv % P, rg0 = wv / P;
+  const bool active = rg0 < NRG;
+  const int nblk = (nqb + kQPRows - 1) / kQPRows;
+  const int bh = (int)blockIdx.x / nblk;  // b * Hq + h
+  const int row0 = kQPRows * ((int)blockIdx.x % nblk);
+  const float* w = wq + (size_t)(bh % Hq) * D * DG;
+  const int nh = D / 64;
+  f32x4 wst[2][WPT], av[RPW][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int u = 0; u < WPT; ++u) {
+      const int x = threadIdx.x + kQPThreads * u;
+      const int row = 64 * min(h, nh - 1) + x / (DG / 4);
+      wst[h][u] = *reinterpret_cast<const f32x4*>(w + (size_t)row * DG + 4 * (x % (DG / 4)));
+    }
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int rg = min(rg0 + RGS * j, NRG - 1);
+    const float* arow = pq + ((size_t)bh * nqb + min(row0 + 16 * rg + r, nqb - 1)) * D;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      av[j][t] = *reinterpret_cast<const f32x4*>(arow + 16 * min(t, D / 16 - 1) + 4 * kg);
+  }
+  const int col0 = 16 * pr + r, col1 = col0 + DG / 2;
+  f32x4 acc0[RPW], acc1[RPW];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) acc0[j] = acc1[j] = f32x4{};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h > 0) __syncthreads();  // every wave is done with the first half
+#pragma unroll
+    for (int u = 0; u < WPT; ++u) {
+      const int x = threadIdx.x + kQPThreads * u;
+      *reinterpret_cast<f32x4*>(wl + (x / (DG / 4)) * WLD + 4 * (x % (DG / 4))) = wst[h][u];
+    }
+    __syncthreads();
+    if (h < nh && active) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const float* wrow = wl + (16 * t + 4 * kg + qq) * WLD;
+          const float b0 = wrow[col0], b1 = wrow[col1];
+#pragma unroll
+          for (int j = 0; j < RPW; ++j) {
+            acc0[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j][4 * h + t][qq], b0, acc0[j], 0, 0, 0);
+            acc1[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j][4 * h + t][qq], b1, acc1[j], 0, 0, 0);
+          }
+        }
+    }
+  }
+  if (!active) return;
+  // acc[j][v]: row row0 + 16 rg + 4 kg + v, column col0 (acc0) or col1 (acc1).
+  float* out = qt + (size_t)bh * nqb * DG;
+  const double inv_freq = freqs.f[col0];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int rg = rg0 + RGS * j;
+    if (rg >= NRG) break;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = row0 + 16 * rg + 4 * kg + v;
+      float y1, y2;
+      rope_rotate(inv_freq, i, acc0[j][v], acc1[j][v], y1, y2);
+      if (i < nqb) {
+        out[(size_t)i * DG + col0] = y1;
+        out[(size_t)i * DG + col1] = y2;
+      }
+    }
+  }
+}
+
+// gate_rows_kernel: the Q~ rows, logits, softmax (and with MASK the block
+// selection) of one group of 16 query blocks of one (batch, head).  Workgroups
+// go heaviest group first (group g has g + 1 tiles of 16 x 16 logits), more of
+// them than fit at once, so that light groups fill in behind heavy ones and
+// one group's softmax overlaps another's matrix work.
+// * Q~ rows (from gate_qproj_kernel) into LDS.
+// * Logits: the waves take the tiles round robin, Q~ K~^T on
+//   v_mfma_f32_16x16x4f32 (Q~ from LDS, the next tile's K~ rows loading during
+//   the current tile's MFMAs), and write the scaled logits (-inf above the
+//   diagonal) into LDS.
+// * Softmax: one wave per row takes the exact row max, the sum of exponentials
+//   and the probabilities in registers; the score row is written once (zeros
+//   above the diagonal) and, with MASK, selected as in gate_softmax_mask_kernel
+//   (same keys, count rule and select).  Both variants share the softmax code,
+//   so the fused lists are those of the scores, bit for bit.
+constexpr int kRowGroup = 16;         // query blocks per row group
+constexpr int kRowsWaves = 4;
+constexpr int kRowsMaxBlocks = 2048;  // LDS: 16 nQB fp32 logits per workgroup
+
+// Wave-wide max and sum with the same value in every lane.  Within each row of
+// 16 lanes, DPP moves pair every lane with a partner holding the same partial
+// (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror): both add the
+// same two operands, in either order, which is exact for a commutative
+// operation.  The four row results are then combined in one fixed order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_lanes(float v, int r) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+}
+
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(fmaxf(row_lanes(v, 0), row_lanes(v, 1)), fmaxf(row_lanes(v, 2), row_lanes(v, 3)));
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return (row_lanes(v, 0) + row_lanes(v, 1)) + (row_lanes(v, 2) + row_lanes(v, 3));
+}
+
+// Dynamic LDS of gate_rows_kernel: the Q~ rows of a group, then the logits
+// (16 x 16 G fp32).
+size_t gate_rows_lds_bytes(int nqb, int dg) {
+  const int G = (nqb + kRowGroup - 1) / kRowGroup;
+  return (kRowGroup * (size_t)(dg + 4) + (size_t)kRowGroup * kRowGroup * G) * sizeof(float);
+}
+
+template <int DG, int NPL, bool MASK>
+__global__ __launch_bounds__(64 * kRowsWaves) void gate_rows_kernel(
+    const float* __restrict__ qt, const float* __restrict__ kt, int BHq, int Hq, int Hkv,
+    int nqb, float scale,
+    float* __restrict__ scores, int mode, float tau, double density, int keep_sink,
+    int32_t* __restrict__ idx, int32_t* __restrict__ cnt, int max_k) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  __shared__ int hist_all[MASK ? kRowsWaves : 1][256];
+  constexpr int NV = DG / 16;     // 16-byte operand reads per lane and row
+  constexpr int QLD = DG + 4;     // padded Q~ row in LDS (floats)
+  float* qs = smem;                    // Q~ rows of the group [16][QLD]
+  float* lg = smem + kRowGroup * QLD;  // logits [16][16 (g + 1)]
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int r = lane & 15, kg = lane >> 4;
+  const int G = (nqb + kRowGroup - 1) / kRowGroup;
+  const int bh = (int)(blockIdx.x % BHq);  // b * Hq + h
+  const int g = G - 1 - (int)(blockIdx.x / BHq);
+  const int b = bh / Hq;
+  const int kvh = b * Hkv + (bh % Hq) / (Hq / Hkv);
+  const int ntile = g + 1;
+  const int width = kRowGroup * ntile;  // logit row length in LDS
+
+  {
+    // The group's Q~ rows into LDS; rows past nQB re-read the last row (their
+    // logits are never read).
+    constexpr int C4 = DG / 4;
+#pragma unroll
+    for (int x = threadIdx.x; x < kRowGroup * C4; x += 64 * kRowsWaves) {
+      const int row = min(kRowGroup * g + x / C4, nqb - 1);
+      *reinterpret_cast<f32x4*>(qs + (x / C4) * QLD + 4 * (x % C4)) =
+          *reinterpret_cast<const f32x4*>(qt + ((size_t)bh * nqb + row) * DG + 4 * (x % C4));
+    }
+    __syncthreads();
+  }
+
+  // Logits: lane (r, kg) feeds dims 16 t + 4 kg .. + 3 of row r of both
+  // operands at MFMA steps 4 t .. 4 t + 3.  K~ rows past nQB (the last group's
+  // diagonal tile) re-read the last row: those logits are all above the
+  // diagonal, and the loads stay unconditional.
+  const float* krow = kt + (size_t)kvh * nqb * DG + 4 * kg;
+  auto load_k = [&](int ct, f32x4 (&v)[NV]) {
+    const float* src = krow + (size_t)min(kRowGroup * ct + r, nqb - 1) * DG;
+#pragma unroll
+    for (int t = 0; t < NV; ++t) v[t] = *reinterpret_cast<const f32x4*>(src + 16 * t);
+  };
+  const float* qa = qs + r * QLD + 4 * kg;
+  auto tile = [&](int ct, const f32x4 (&bk)[NV]) {
+    f32x4 acc = {};
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(qa + 16 * t);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[qq], bk[t][qq], acc, 0, 0, 0);
+    }
+    // acc[v]: row 4 kg + v of the group, column 16 ct + r.
+    const int j = kRowGroup * ct + r;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int lr = 4 * kg + v;
+      lg[lr * width + j] = (j <= kRowGroup * g + lr) ? acc[v] * scale : -INFINITY;
+    }
+  };
+  // Tiles in pairs with two buffers: no branch between a prefetch and its use
+  // (one would let the compiler sink the load to the use), and the scheduling
+  // barriers keep the loads ahead of the MFMAs they overlap.  A tile index past
+  // the last re-reads the last tile's rows, so every wait counts exactly the
+  // loads of the tile after it.
+  f32x4 b0[NV], b1[NV];
+  int ct = wv;
+  load_k(min(ct, ntile - 1), b0);
+#pragma unroll 1
+  for (; ct + kRowsWaves < ntile; ct += 2 * kRowsWaves) {
+    load_k(ct + kRowsWaves, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    tile(ct, b0);
+    load_k(min(ct + 2 * kRowsWaves, ntile - 1), b0);
+    __builtin_amdgcn_sched_barrier(0);
+    tile(ct + kRowsWaves, b1);
+  }
+  if (ct < ntile) tile(ct, b0);
+  __syncthreads();
+
+#pragma unroll 1
+  for (int lr = wv; lr < kRowGroup; lr += kRowsWaves) {
+    const int i = kRowGroup * g + lr;
+    if (i >= nqb) break;
+    const float* src = lg + lr * width;
+    float x[NPL];
+    float m = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < NPL; ++c) {
+      const int j = 64 * c + lane;
+      x[c] = j <= i ? src[j] : -INFINITY;
+      m = fmaxf(m, x[c]);
+    }
+    m = wave_max_f(m);
+    float l = 0.f;
+#pragma unroll
+    for (int c = 0; c < NPL; ++c) {
+      x[c] = (64 * c + lane <= i) ? expf(x[c] - m) : 0.f;
+      l += x[c];
+    }
+    l = wave_sum_f(l);
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int c = 0; c < NPL; ++c) x[c] *= inv;
+    const size_t row = (size_t)bh * nqb + i;
+    if (scores) {
+      // Written once, read by the caller later: non-temporal, so the stream of
+      // score rows does not push the K~ rows out of L2.
+      float* sr = scores + row * nqb;
+#pragma unroll
+      for (int c = 0; c < NPL; ++c)
+        if (64 * c + lane < nqb) __builtin_nontemporal_store(x[c], sr + 64 * c + lane);
+    }
+    if constexpr (MASK) {
+      const int n = i + 1;
+      uint32_t key[NPL];
+      int npos = 0;
+#pragma unroll
+      for (int c = 0; c < NPL; ++c) {
+        const int j = 64 * c + lane;
+        uint32_t kj = 0u;
+        if (j < n) {
+          if (j == i || (keep_sink && j == 0))
+            kj = 0xFFFFFFFFu;
+          else
+            kj = (mode == 1 || x[c] >= tau) ? rowsel::order_key(x[c]) : 0u;
+        }
+        key[c] = kj;
+        npos += kj != 0u;
+      }
+      npos = rowsel::wave_sum(npos);
+      int kk;
+      if (mode == 1) {
+        const int forced = (i == 0) ? 1 : (keep_sink ? 2 : 1);
+        kk = min(i + 1, max(forced, (int)ceil(density * (double)(i + 1))));
+      } else {
+        kk = min(npos, max_k);
+      }
+      const int count = rowsel::wave_select_row<NPL>(key, n, kk, npos, lane, hist_all[wv],
+                                                     idx + row * max_k, max_k);
+      if (lane == 0) cnt[row] = count;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1000,6 +1542,90 @@ hipError_t gate_logits(int B, int Hq, int Hkv, int nqb, int dg, float scale, con
   return hipGetLastError();
 }
 
+// The one-pass gate's front (nQB <= kRowsMaxBlocks), two kernels: K~
+// [B,Hkv,nQB,Dg] at the start of ws, then the pooled Q [B,Hq,nQB,D], then Q~
+// [B,Hq,nQB,Dg].
+hipError_t gate_pool_project(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
+                             const float* wq, const float* wk, int dg, float rope_base,
+                             float* ws, hipStream_t stream) {
+  const int nqb = (T + kTile - 1) / kTile;
+  float* kt = ws;
+  float* pq = ws + (size_t)B * Hkv * nqb * dg;
+  const size_t ng = (nqb + kPPRows - 1) / kPPRows, nq8 = (nqb + kPPWaves - 1) / kPPWaves;
+  const dim3 grid((unsigned)((size_t)B * Hkv * ng + (size_t)B * Hq * nq8));
+  const RopeFreqs freqs = rope_freqs(rope_base, dg);
+#define SEER_GATE_PP(DD, DG)                                                                   \
+  hipLaunchKernelGGL((gate_pool_project_kernel<DD, DG>), grid, dim3(64 * kPPWaves), 0, stream, \
+                     (const __bf16*)q, (const __bf16*)k, B, Hq, Hkv, T, nqb, wk, freqs, pq, kt)
+  if (D == 128) {
+    if (dg == 128) SEER_GATE_PP(128, 128);
+    else if (dg == 64) SEER_GATE_PP(128, 64);
+    else SEER_GATE_PP(128, 32);
+  } else {
+    if (dg == 128) SEER_GATE_PP(64, 128);
+    else if (dg == 64) SEER_GATE_PP(64, 64);
+    else SEER_GATE_PP(64, 32);
+  }
+#undef SEER_GATE_PP
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  float* qt = pq + (size_t)B * Hq * nqb * D;
+  const dim3 qgrid((unsigned)((size_t)B * Hq * ((nqb + kQPRows - 1) / kQPRows)));
+#define SEER_GATE_QP(DG)                                                                      \
+  hipLaunchKernelGGL(gate_qproj_kernel<DG>, qgrid, dim3(kQPThreads), 0, stream, pq, wq, D, Hq, \
+                     nqb, freqs, qt)
+  if (dg == 128) SEER_GATE_QP(128);
+  else if (dg == 64) SEER_GATE_QP(64);
+  else SEER_GATE_QP(32);
+#undef SEER_GATE_QP
+  return hipGetLastError();
+}
+
+template <int DG, int NPL, bool MASK>
+hipError_t gate_rows_launch(int B, int Hq, int Hkv, int nqb, int D, float scale, const float* ws,
+                            float* scores, int mode, float tau, double density, int keep_sink,
+                            int32_t* idx, int32_t* cnt, int max_k, hipStream_t stream) {
+  const float* kt = ws;
+  const float* qt = ws + (size_t)B * Hkv * nqb * DG + (size_t)B * Hq * nqb * D;
+  const int G = (nqb + kRowGroup - 1) / kRowGroup;
+  const size_t lds = gate_rows_lds_bytes(nqb, DG);
+  auto kern = gate_rows_kernel<DG, NPL, MASK>;
+  if (lds > 65536) {
+    const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)lds);
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)((size_t)B * Hq * G)), dim3(64 * kRowsWaves), lds,
+                     stream, qt, kt, B * Hq, Hq, Hkv, nqb, scale, scores, mode, tau, density,
+                     keep_sink, idx, cnt, max_k);
+  return hipGetLastError();
+}
+
+template <bool MASK>
+hipError_t gate_rows(int B, int Hq, int Hkv, int nqb, int D, int dg, float scale, const float* ws,
+                     float* scores, int mode, float tau, double density, int keep_sink,
+                     int32_t* idx, int32_t* cnt, int max_k, hipStream_t stream) {
+#define SEER_GATE_ROWS_CALL(DG, NPL)                                                       \
+  return gate_rows_launch<DG, NPL, MASK>(B, Hq, Hkv, nqb, D, scale, ws, scores, mode, tau, \
+                                         density, keep_sink, idx, cnt, max_k, stream)
+#define SEER_GATE_ROWS_NPL(DG)                     \
+  do {                                             \
+    if (nqb <= 64) SEER_GATE_ROWS_CALL(DG, 1);     \
+    if (nqb <= 64 * 4) SEER_GATE_ROWS_CALL(DG, 4); \
+    if (nqb <= 64 * 8) SEER_GATE_ROWS_CALL(DG, 8); \
+    if (nqb <= 64 * 16) SEER_GATE_ROWS_CALL(DG, 16); \
+    SEER_GATE_ROWS_CALL(DG, 32);                   \
+  } while (0)
+  static_assert(kRowsMaxBlocks == 64 * 32, "NPL ladder covers kRowsMaxBlocks");
+  if (nqb > kRowsMaxBlocks) return hipErrorInvalidValue;
+  if (dg == 128) SEER_GATE_ROWS_NPL(128);
+  if (dg == 64) SEER_GATE_ROWS_NPL(64);
+  SEER_GATE_ROWS_NPL(32);
+#undef SEER_GATE_ROWS_NPL
+#undef SEER_GATE_ROWS_CALL
+}
+
 }  // namespace
 
 hipError_t launch_attn_gate(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
@@ -1007,6 +1633,12 @@ hipError_t launch_attn_gate(const void* q, const void* k, int B, int Hq, int Hkv
                             float rope_base, float* scores, float* ws, hipStream_t stream) {
   const int nqb = (T + kTile - 1) / kTile;
   if ((size_t)B * Hq * nqb == 0) return hipSuccess;
+  if (nqb <= kRowsMaxBlocks) {
+    hipError_t err = gate_pool_project(q, k, B, Hq, Hkv, T, D, wq, wk, dg, rope_base, ws, stream);
+    if (err != hipSuccess) return err;
+    return gate_rows<false>(B, Hq, Hkv, nqb, D, dg, scale, ws, scores, 0, 0.f, 0.0, 0, nullptr,
+                            nullptr, 1, stream);
+  }
   float2* part = nullptr;
   hipError_t err = gate_front(q, k, B, Hq, Hkv, T, D, wq, wk, dg, rope_base, ws, &part, stream);
   if (err != hipSuccess) return err;
@@ -1026,6 +1658,12 @@ hipError_t launch_attn_gate_mask(const void* q, const void* k, int B, int Hq, in
                                  float* scores, float* ws, int pass_rows, hipStream_t stream) {
   const int nqb = (T + kTile - 1) / kTile;
   if ((size_t)B * Hq * nqb == 0) return hipSuccess;
+  if (nqb <= kRowsMaxBlocks) {  // the logits stay on chip: no passes, no logits buffer
+    hipError_t err = gate_pool_project(q, k, B, Hq, Hkv, T, D, wq, wk, dg, rope_base, ws, stream);
+    if (err != hipSuccess) return err;
+    return gate_rows<true>(B, Hq, Hkv, nqb, D, dg, scale, ws, scores, mode, threshold, density,
+                           keep_sink, idx, cnt, max_k, stream);
+  }
   // Without a scores buffer the logits live past the gate's own workspace, at
   // the next 256-byte boundary (within the 256 bytes of slack the workspace
   // size adds), pass_rows rows per head at a time.

@@ -697,10 +697,12 @@ def _gate_case(case):
         return wl.custom(82, 1, 6, 3, 64, 2000), 128
     if case == "far128k":  # block positions up to 2047: RoPE angles of ~2000 rad
         return wl.custom(86, 1, 2, 1, 64, 131072), 64
+    if case == "rows4096":  # 4096 query blocks: rows longer than one workgroup's LDS holds
+        return wl.custom(87, 1, 1, 1, 64, 262144), 32
     return wl.custom(83, 1, 32, 8, 128, 8192, qkv_scale=1.0 / math.sqrt(128.0)), 128
 
 
-@pytest.mark.parametrize("case", ["tiny", "ragged", "d64", "far128k", "llama8k"])
+@pytest.mark.parametrize("case", ["tiny", "ragged", "d64", "far128k", "rows4096", "llama8k"])
 def test_attn_gate_scores(case):
     w, dg = _gate_case(case)
     announce(f"attn gate scores {w.name} dg={dg}")
@@ -763,7 +765,7 @@ def test_attn_gate_to_topk_lists():
     assert exact > 0.9 * (exact + ambiguous)
 
 
-@pytest.mark.parametrize("case", ["tiny", "ragged", "d64", "far128k", "llama8k"])
+@pytest.mark.parametrize("case", ["tiny", "ragged", "d64", "far128k", "rows4096", "llama8k"])
 @pytest.mark.parametrize("mode", [wl.MODE_TOPK, wl.MODE_THRESHOLD])
 def test_attn_gate_mask_equals_scores_then_mask(case, mode):
     """The fused call returns, bit for bit, the scores of seer_attn_gate_scores and
