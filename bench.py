@@ -400,8 +400,9 @@ def decode_bench(seer, wl, torch, dev, args):
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first: the power controller settles within about 0.1 s")
     ap.add_argument("--workload", type=int, default=3, help="workload id (default 3: 32k, density 0.1)")
     ap.add_argument("--cpu-blocks-per-head", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
