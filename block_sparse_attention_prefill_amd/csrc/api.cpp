@@ -27,7 +27,9 @@ constexpr int kVersion = 100;  // 0.1.0
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
-int nqb_of(int T) { return (T + SEER_BLOCK - 1) / SEER_BLOCK; }
+// In 64 bits: callers pass T before it is range-checked, and T + 63 overflows
+// int for T near INT_MAX; the quotient always fits.
+int nqb_of(int T) { return (int)(((long long)T + SEER_BLOCK - 1) / SEER_BLOCK); }
 
 // Sizes must keep every flattened index inside int32 / size_t arithmetic the
 // kernels use: item ids (B*H*nQB) are int, element offsets are size_t.
