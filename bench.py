@@ -88,6 +88,22 @@ def time_calls(fn, n: int, torch, flush=None):
     return statistics.mean(a.elapsed_time(b) for a, b in evs)
 
 
+def settle(fn, torch, seconds: float = 0.1, max_calls: int = 400) -> None:
+    """Untimed calls of fn for about `seconds` of GPU time, so that the calls timed
+    next run at the clock the socket power controller holds under this load (it
+    moves the clock for a few tens of ms after the load changes)."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    fn()
+    b.record()
+    torch.cuda.synchronize()
+    one = max(a.elapsed_time(b) * 1e-3, 1e-6)
+    for _ in range(min(max_calls, int(seconds / one))):
+        fn()
+    torch.cuda.synchronize()
+
+
 def call_stats(fn, n: int, torch, flush=None) -> dict:
     """Median, min and max duration (ms) of fn() over n calls, timed as in
     time_calls."""
@@ -232,9 +248,11 @@ def sparse_config_line(seer, wl, torch, dev, w, args) -> dict:
                                         kv_idx=idx, kv_cnt=cnt)
     pre = lambda: seer.seer_sparse_prefill(q, k, v, idx, cnt, out=out, workspace=ws)
     mask()
-    pre()
+    settle(pre, torch)
     n = max(3, args.steps // 2)
+    settle(mask, torch)
     m_ms = time_calls(mask, n, torch)
+    settle(pre, torch)
     p_ms = time_calls(pre, n, torch)
     blocks = int(cnt.sum().item())
     tf = blocks * tile_flops(w.head_dim) / (p_ms * 1e-3) / 1e12
@@ -252,7 +270,7 @@ def sparse_config_line(seer, wl, torch, dev, w, args) -> dict:
     idx1 = torch.empty((w.batch, w.hq, w.nqb, w.nqb), dtype=torch.int32, device=dev)
     seer.seer_build_mask(sd, wl.MODE_TOPK, 0.0, 1.0, w.keep_sink, w.nqb, kv_idx=idx1, kv_cnt=cnt)
     call1 = lambda: seer.seer_sparse_prefill(q, k, v, idx1, cnt, out=out, workspace=ws)
-    call1()
+    settle(call1, torch)
     d_ms = time_calls(call1, max(2, args.steps // 5), torch)
     blocks1 = int(cnt.sum().item())
     res["density1"] = {
@@ -558,10 +576,9 @@ def main(argv=None) -> int:
         cnt1 = torch.empty((w.batch, w.hq, w.nqb), dtype=torch.int32, device=dev)
         seer.seer_build_mask(sd, wl.MODE_TOPK, 0.0, 1.0, w.keep_sink, w.nqb, kv_idx=idx1,
                              kv_cnt=cnt1)
-        seer.seer_sparse_prefill(qd, kd, vd, idx1, cnt1, out=out, workspace=ws)
-        n1 = max(2, args.steps // 5)
-        dense_ms = time_calls(lambda: seer.seer_sparse_prefill(qd, kd, vd, idx1, cnt1, out=out,
-                                                               workspace=ws), n1, torch)
+        dense = lambda: seer.seer_sparse_prefill(qd, kd, vd, idx1, cnt1, out=out, workspace=ws)
+        settle(dense, torch)
+        dense_ms = time_calls(dense, max(2, args.steps // 5), torch)
         blocks1 = int(cnt1.sum().item())
         result["density1"] = {
             "prefill_ms": round(dense_ms, 4),
@@ -580,7 +597,7 @@ def main(argv=None) -> int:
         ws5 = torch.empty((seer.pooled_attn_map_workspace_size(w5.batch, w5.hq, w5.seq),),
                           dtype=torch.uint8, device=dev)
         call = lambda: seer.seer_pooled_attn_map(q5, k5, v5, out=o5, amap=a5, workspace=ws5)
-        call()
+        settle(call, torch)
         pm_ms = time_calls(call, max(2, args.steps // 5), torch)
         tiles = w5.batch * w5.hq * w5.nqb * (w5.nqb + 1) // 2
         result["pooled_map"] = {
@@ -601,7 +618,7 @@ def main(argv=None) -> int:
         lossd = torch.empty((1,), dtype=torch.float32, device=dev)
         tcall = lambda: seer.seer_pooled_target_mse(a5, gate, target=tgt, row_sse=rsse,
                                                     loss=lossd)
-        tcall()
+        settle(tcall, torch)
         tg_ms = time_calls(tcall, max(3, args.steps // 2), torch)
         rows = w5.batch * w5.hq * w5.nqb
         tg_bytes = 4 * (2 * tiles + rows * w5.nqb + rows + 1)
@@ -622,7 +639,7 @@ def main(argv=None) -> int:
         gws = torch.empty((seer.load().seer_attn_gate_workspace_size(
             w.batch, w.hq, w.hkv, w.seq, dg),), dtype=torch.uint8, device=dev)
         gcall = lambda: seer.seer_attn_gate_scores(qd, kd, wq, wk, scores=gs, workspace=gws)
-        gcall()
+        settle(gcall, torch)
         g_ms = time_calls(gcall, max(3, args.steps // 2), torch)
         g_bytes = 2 * (qd.numel() + kd.numel()) + 4 * gs.numel()
         # The same gate straight into the bench's TopK lists in one call (no score
@@ -644,11 +661,11 @@ def main(argv=None) -> int:
         pcall = lambda: seer.seer_attn_gate_mask(qd, kd, wq, wk, w.mode, w.threshold, w.density,
                                                  w.keep_sink, gmk, kv_idx=gidx, kv_cnt=gcnt,
                                                  workspace=gws3)
-        fcall()
-        tcall2()
-        pcall()
+        settle(fcall, torch)
         f_ms = time_calls(fcall, max(3, args.steps // 2), torch)
+        settle(tcall2, torch)
         t2_ms = time_calls(tcall2, max(3, args.steps // 2), torch)
+        settle(pcall, torch)
         p_ms = time_calls(pcall, max(3, args.steps // 2), torch)
         result["attn_gate"] = {
             "ms": round(g_ms, 4),
@@ -674,7 +691,7 @@ def main(argv=None) -> int:
                                               w128.keep_sink, mk128)
         call128 = lambda: seer.seer_sparse_prefill_block(qd, kd, vd, idx128, cnt128, 128, out=out,
                                                          workspace=ws)
-        call128()
+        settle(call128, torch)
         b128_ms = time_calls(call128, max(3, args.steps // 2), torch)
         # 64-token tiles computed: a listed 128-block gives both of its tiles to each
         # 64-row half, except the diagonal block, whose upper tile the first half skips.
