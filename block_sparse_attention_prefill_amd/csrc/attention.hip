@@ -999,14 +999,20 @@ __global__ __launch_bounds__(kPairThreads * HPW, kPairWgsPerCu) void pooled_map_
 
 // ---------------------------------------------------------------------------
 // Schedule (longest-processing-time first): one workgroup per KV group (b, g)
-// counting-sorts that group's G * nQB items by descending list length; the
-// rank-r item of group q goes to position r * NG + q of the work list (NG =
-// B * Hkv).  Workgroups are dispatched in position order, so long rows start
-// first everywhere; and since the hardware deals workgroup L to XCD L % 8,
-// every item of a group lands on the same XCD whenever NG is a multiple of 8
-// (its K/V then stays in that XCD's L2).
+// counting-sorts that group's N = G * nQB items by descending list length.
+// The groups run in P phases of GP = NG / P groups (NG = B * Hkv): the rank-r
+// item of group q goes to position (q / GP) * GP * N + r * GP + q % GP of the
+// work list.  Workgroups are dispatched in position order, so the groups of one
+// phase run together, and within a phase long rows start first everywhere.
+// Since the hardware deals workgroup L to XCD L % 8, every item of a group
+// lands on the XCDs x with x % GP = q % GP whenever NG is a multiple of 8 (one
+// XCD per group with one phase: its K/V then stays in that XCD's L2).  P > 1
+// when the K and V of all groups exceed kActiveKvBytes: a phase's K/V then
+// stays in the 256 MB memory-side cache while it runs, instead of every group's
+// K/V competing for it (128k tokens, 8 KV groups: 64 MB per group, 8 phases).
 constexpr int kSchedThreads = 1024;
 constexpr int kCostBins = 1024;
+constexpr double kActiveKvBytes = 64.0 * 1024 * 1024;
 
 // Counting sort of the n candidates `keep` accepts by descending cost: the
 // candidate of rank r is handed to put(r, it), and put(r, -1) fills the ranks
@@ -1049,7 +1055,7 @@ __device__ void lpt_column(int n, Keep keep, Cost cost, Put put, int cap, int* h
 // without a usable position gets position = BS * length and tile -1.
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ idx, int Hq, int Hkv, int nqb,
-    int bs, int max_k, int4* __restrict__ work) {
+    int bs, int max_k, int phases, int4* __restrict__ work) {
   __shared__ int hist[kCostBins];
   __shared__ int wsum[kSchedThreads / 64];
   const int G = Hq / Hkv;
@@ -1058,6 +1064,9 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
   const int bh0 = (grp / Hkv) * Hq + (grp % Hkv) * G;  // first head of the group
   const int base = bh0 * nqb;                          // the group's items
   const int rows = (nqb + bs - 1) / bs;                // list rows per head
+  const int gp = ng / phases;                          // groups per phase
+  const int ql = grp % gp;                             // the group's column in its phase
+  const size_t pbase = (size_t)(grp / gp) * gp * G * nqb;  // first position of its phase
   auto row_of = [&](int it) { return (size_t)(bh0 + it / nqb) * rows + (it % nqb) / bs; };
   auto len_of = [&](int it) { return min(max(cnt[row_of(it)], 0), max_k); };
   lpt_column(
@@ -1080,7 +1089,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
           }
           e = {base + it, x, tile, n};
         }
-        work[(size_t)r * ng + grp] = e;
+        work[pbase + (size_t)r * gp + ql] = e;
       },
       G * nqb, hist, wsum);
 }
@@ -1115,6 +1124,21 @@ hipError_t pooled_launch(const void* q, const void* k, const void* v, int B, int
   return hipGetLastError();
 }
 
+// Phases of the schedule for NG groups whose K and V take kv_bytes: the fewest
+// (doubling from 1) that bring a phase's K/V to kActiveKvBytes, keeping each
+// phase's groups an even share of the 8 XCDs (GP a multiple or a divisor of 8);
+// 1 when NG is not a multiple of 8 (groups are not pinned to XCDs then).
+int kv_phases(int ng, double kv_bytes) {
+  int p = 1;
+  if (ng % kXcds != 0) return p;
+  while (kv_bytes / p > kActiveKvBytes && ng % (2 * p) == 0) {
+    const int gp = ng / (2 * p);
+    if (gp % kXcds != 0 && kXcds % gp != 0) break;
+    p *= 2;
+  }
+  return p;
+}
+
 }  // namespace
 
 // int32 entries: one int4 {item, first usable position, its tile, length} per item.
@@ -1130,7 +1154,8 @@ hipError_t launch_sparse_prefill(const void* q, const void* k, const void* v, in
   const float c = sm_scale * kLog2e;
   const int bs = block / kBlk;
   hipLaunchKernelGGL(schedule_kernel, dim3(B * Hkv), dim3(kSchedThreads), 0, stream, cnt, idx,
-                     Hq, Hkv, nqb, bs, max_k, reinterpret_cast<int4*>(work));
+                     Hq, Hkv, nqb, bs, max_k, kv_phases(B * Hkv, 4.0 * B * Hkv * (double)T * D),
+                     reinterpret_cast<int4*>(work));
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (bs == 2)

@@ -370,15 +370,34 @@ def test_sparse_density_one_matches_dense_causal():
     assert float(np.abs(o.double().numpy() - ref).max()) <= O_TOL
 
 
-@pytest.mark.parametrize("hq,hkv,t,mode", [(32, 8, 4096, "sorted"), (6, 2, 700, "dense"),
-                                           (4, 2, 900, "invalid"),
-                                           (3, 3, 1000, "invalid")])
-def test_sparse_schedule_work_list(hq, hkv, t, mode):
-    """The work list the schedule leaves in the workspace: column q = b * Hkv + g
-    holds every item of KV group (b, g) exactly once, longest list first, each
-    with its first usable list position, that position's tile and the list
-    length (bit-exact against a scan on the host)."""
-    announce(f"schedule work list hq={hq} hkv={hkv} t={t} lists={mode}")
+def _schedule_phases(ng, kv_bytes, active=64 * 1024 * 1024):
+    """The phase count the schedule uses: doubling from 1 while a phase's K/V
+    exceeds 64 MiB, each phase keeping an even share of the 8 XCDs."""
+    p = 1
+    if ng % 8:
+        return p
+    while kv_bytes / p > active and ng % (2 * p) == 0:
+        gp = ng // (2 * p)
+        if gp % 8 and 8 % gp:
+            break
+        p *= 2
+    return p
+
+
+@pytest.mark.parametrize("hq,hkv,t,mode,phases", [(32, 8, 4096, "sorted", 1),
+                                                  (6, 2, 700, "dense", 1),
+                                                  (4, 2, 900, "invalid", 1),
+                                                  (3, 3, 1000, "invalid", 1),
+                                                  (16, 8, 40000, "sorted", 2),
+                                                  (8, 8, 140000, "invalid", 8)])
+def test_sparse_schedule_work_list(hq, hkv, t, mode, phases):
+    """The work list the schedule leaves in the workspace: KV group q = b * Hkv + g
+    runs in phase q / GP (GP = NG / P groups per phase), and its rank-r item sits
+    at position (q / GP) * GP * N + r * GP + q % GP (N = G * nQB); the group's
+    column holds each of its items exactly once, longest list first, each with its
+    first usable list position, that position's tile and the list length
+    (bit-exact against a scan on the host)."""
+    announce(f"schedule work list hq={hq} hkv={hkv} t={t} lists={mode} phases={phases}")
     b, d = 1, 64
     nqb = (t + 63) // 64
     G = hq // hkv
@@ -392,17 +411,21 @@ def test_sparse_schedule_work_list(hq, hkv, t, mode):
                              workspace=ws.view(torch.uint8))
     torch.cuda.synchronize()
     ng = b * hkv
-    work = ws.cpu().numpy()[: 4 * b * hq * nqb].reshape(G * nqb, ng, 4)
+    assert _schedule_phases(ng, 4.0 * b * hkv * t * d) == phases
+    n_items = G * nqb
+    gp = ng // phases
+    work = ws.cpu().numpy()[: 4 * b * hq * nqb].reshape(-1, 4)
     flat_cnt = np.minimum(np.maximum(cnt.reshape(-1), 0), max_k)
     flat_idx = idx.reshape(-1, max_k)
     for grp in range(ng):
         bb, gg = divmod(grp, hkv)
         lo = (bb * hq + gg * G) * nqb
-        col = work[:, grp, 0]
-        assert sorted(col.tolist()) == list(range(lo, lo + G * nqb))
+        rows = (grp // gp) * gp * n_items + np.arange(n_items) * gp + grp % gp
+        col = work[rows, 0]
+        assert sorted(col.tolist()) == list(range(lo, lo + n_items))
         costs = flat_cnt[col]
         assert (np.diff(costs) <= 0).all(), "items must be longest first"
-        for item, pos, tile, n in work[:, grp]:
+        for item, pos, tile, n in work[rows]:
             i = item % nqb
             lst = flat_idx[item][: flat_cnt[item]]
             usable = [x for x, j in enumerate(lst) if 0 <= j <= i]
