@@ -859,15 +859,19 @@ __global__ __launch_bounds__(kQPThreads) void gate_qproj_kernel(const float* __r
 }
 
 // gate_rows_kernel: the Q~ rows, logits, softmax (and with MASK the block
-// selection) of one group of 16 query blocks of one (batch, head).  Workgroups
-// go heaviest group first (group g has g + 1 tiles of 16 x 16 logits), more of
-// them than fit at once, so that light groups fill in behind heavy ones and
-// one group's softmax overlaps another's matrix work.
-// * Q~ rows (from gate_qproj_kernel) into LDS.
+// selection) of one group of 16 query blocks of one (batch, head).  Group g has
+// g + 1 tiles of 16 x 16 logits.  Workgroups take the groups in blocks of 8
+// weight ranks, heaviest block first, alternately heaviest-first and
+// lightest-first within a block, so that the workgroups resident together on a
+// CU (dealt out in launch order) carry about equal work, and one group's softmax
+// overlaps another's matrix work.  Only the logits take LDS and the registers
+// stay within 128, so four workgroups fit on a CU at 512 query blocks (all of
+// them at once for 32 heads).
+// * Q~ operands (from gate_qproj_kernel) in registers, loaded once.
 // * Logits: the waves take the tiles round robin, Q~ K~^T on
-//   v_mfma_f32_16x16x4f32 (Q~ from LDS, the next tile's K~ rows loading during
-//   the current tile's MFMAs), and write the scaled logits (-inf above the
-//   diagonal) into LDS.
+//   v_mfma_f32_16x16x4f32 (the next tile's K~ rows loading during the current
+//   tile's MFMAs), and write the scaled logits (-inf above the diagonal) into
+//   LDS.
 // * Softmax: one wave per row takes the exact row max, the sum of exponentials
 //   and the probabilities in registers; the score row is written once (zeros
 //   above the diagonal) and, with MASK, selected as in gate_softmax_mask_kernel
@@ -906,15 +910,15 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return (row_lanes(v, 0) + row_lanes(v, 1)) + (row_lanes(v, 2) + row_lanes(v, 3));
 }
 
-// Dynamic LDS of gate_rows_kernel: the Q~ rows of a group, then the logits
-// (16 x 16 G fp32).
+// Dynamic LDS of gate_rows_kernel: the logits of a group (16 x 16 G fp32).
 size_t gate_rows_lds_bytes(int nqb, int dg) {
   const int G = (nqb + kRowGroup - 1) / kRowGroup;
-  return (kRowGroup * (size_t)(dg + 4) + (size_t)kRowGroup * kRowGroup * G) * sizeof(float);
+  (void)dg;
+  return (size_t)kRowGroup * kRowGroup * G * sizeof(float);
 }
 
 template <int DG, int NPL, bool MASK>
-__global__ __launch_bounds__(64 * kRowsWaves) void gate_rows_kernel(
+__global__ __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu(4))) void gate_rows_kernel(
     const float* __restrict__ qt, const float* __restrict__ kt, int BHq, int Hq, int Hkv,
     int nqb, float scale,
     float* __restrict__ scores, int mode, float tau, double density, int keep_sink,
@@ -922,31 +926,32 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gate_rows_kernel(
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ int hist_all[MASK ? kRowsWaves : 1][256];
   constexpr int NV = DG / 16;     // 16-byte operand reads per lane and row
-  constexpr int QLD = DG + 4;     // padded Q~ row in LDS (floats)
-  float* qs = smem;                    // Q~ rows of the group [16][QLD]
-  float* lg = smem + kRowGroup * QLD;  // logits [16][16 (g + 1)]
+  float* lg = smem;  // logits [16][16 (g + 1)]
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int r = lane & 15, kg = lane >> 4;
   const int G = (nqb + kRowGroup - 1) / kRowGroup;
   const int bh = (int)(blockIdx.x % BHq);  // b * Hq + h
-  const int g = G - 1 - (int)(blockIdx.x / BHq);
+  int g;
+  {
+    const int j = (int)(blockIdx.x / BHq);  // weight rank: 0 is the heaviest group
+    const int lo = j / 8 * 8, hi = min(G, lo + 8);
+    const int jj = ((j / 8) & 1) ? hi - 1 - (j - lo) : j;
+    g = G - 1 - jj;
+  }
   const int b = bh / Hq;
   const int kvh = b * Hkv + (bh % Hq) / (Hq / Hkv);
   const int ntile = g + 1;
   const int width = kRowGroup * ntile;  // logit row length in LDS
 
+  // This lane's Q~ operands (row r of the group, dims 16 t + 4 kg .. + 3), held in
+  // registers for every tile; rows past nQB re-read the last row (their logits are
+  // never read).
+  f32x4 qv[NV];
   {
-    // The group's Q~ rows into LDS; rows past nQB re-read the last row (their
-    // logits are never read).
-    constexpr int C4 = DG / 4;
+    const float* qrow = qt + ((size_t)bh * nqb + min(kRowGroup * g + r, nqb - 1)) * DG + 4 * kg;
 #pragma unroll
-    for (int x = threadIdx.x; x < kRowGroup * C4; x += 64 * kRowsWaves) {
-      const int row = min(kRowGroup * g + x / C4, nqb - 1);
-      *reinterpret_cast<f32x4*>(qs + (x / C4) * QLD + 4 * (x % C4)) =
-          *reinterpret_cast<const f32x4*>(qt + ((size_t)bh * nqb + row) * DG + 4 * (x % C4));
-    }
-    __syncthreads();
+    for (int t = 0; t < NV; ++t) qv[t] = *reinterpret_cast<const f32x4*>(qrow + 16 * t);
   }
 
   // Logits: lane (r, kg) feeds dims 16 t + 4 kg .. + 3 of row r of both
@@ -959,15 +964,13 @@ __global__ __launch_bounds__(64 * kRowsWaves) void gate_rows_kernel(
 #pragma unroll
     for (int t = 0; t < NV; ++t) v[t] = *reinterpret_cast<const f32x4*>(src + 16 * t);
   };
-  const float* qa = qs + r * QLD + 4 * kg;
   auto tile = [&](int ct, const f32x4 (&bk)[NV]) {
     f32x4 acc = {};
 #pragma unroll
     for (int t = 0; t < NV; ++t) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(qa + 16 * t);
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[qq], bk[t][qq], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[t][qq], bk[t][qq], acc, 0, 0, 0);
     }
     // acc[v]: row 4 kg + v of the group, column 16 ct + r.
     const int j = kRowGroup * ct + r;
