@@ -29,20 +29,38 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+// Lane moves within rows of 16 lanes (DPP, no LDS round trip).  dpp_row<CTRL>
+// reads 0 where the source lane lies outside the row.
+template <int CTRL>
+__device__ __forceinline__ int dpp_row(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
 }
 
-// Inclusive prefix sum over the wave (lane order).
+// Sum over the wave, the same in every lane: pair, quad, half-row and row sums
+// by DPP moves (quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror,
+// row_mirror), then the four row sums read from lanes 0, 16, 32, 48.
+__device__ __forceinline__ int wave_sum(int v) {
+  v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+  v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
+  v += __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
+// Inclusive prefix sum over the wave (lane order): within each row of 16 lanes
+// by row_shr 1, 2, 4, 8, then each row adds the totals of the rows before it
+// (lanes 15, 31, 47).
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(v, off, 64);
-    if (lane >= off) v += y;
-  }
-  return v;
+  v += dpp_row<0x111>(v);
+  v += dpp_row<0x112>(v);
+  v += dpp_row<0x114>(v);
+  v += dpp_row<0x118>(v);
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
 }
 
 // Number of set bits of `mask` below this lane.
@@ -98,9 +116,9 @@ __device__ __forceinline__ int wave_select_row(const uint32_t (&key)[NPL], int n
       }
       const uint64_t who = __ballot(sel_bin >= 0);
       const int src = __builtin_ctzll(who);
-      sel_bin = __shfl(sel_bin, src, 64);
-      sel_above = __shfl(sel_above, src, 64);
-      sel_cnt = __shfl(sel_cnt, src, 64);
+      sel_bin = __builtin_amdgcn_readlane(sel_bin, src);
+      sel_above = __builtin_amdgcn_readlane(sel_above, src);
+      sel_cnt = __builtin_amdgcn_readlane(sel_cnt, src);
       prefix |= (uint32_t)sel_bin << shift;
       mask |= 0xFFu << shift;
       remaining -= sel_above;
