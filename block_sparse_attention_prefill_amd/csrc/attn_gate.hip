@@ -11,12 +11,12 @@
 // Map)").  Threshold or TopK on these scores (seer_build_mask) gives the mask.
 //
 // Prefill kernels, up to 2048 query blocks (rows whose logits fit in LDS):
-// * gate_pool_project_kernel: the pooling pass over Q and K; K~ (linear layer
-//   and block RoPE on the fp32 matrix cores) for every block, the pooled Q means.
-// * gate_qproj_kernel: Q~ from the pooled Q means.
-// * gate_rows_kernel: per group of 16 query blocks, the causal logits Q~ K~^T
-//   (fp32 matrix cores) into LDS, the exact row softmax, the score rows written
-//   once; the fused variant selects each row's block list from the same values.
+// * gate_pool_project_kernel: the pooling pass over K; K~ (linear layer and
+//   block RoPE on the fp32 matrix cores) for every block.
+// * gate_rows_kernel: per group of 16 query blocks, the Q pooling, linear layer
+//   and block RoPE, the causal logits Q~ K~^T (fp32 matrix cores) into LDS, the
+//   exact row softmax, the score rows written once; the fused variant selects
+//   each row's block list from the same values.
 // RoPE angles are formed and reduced in fp64 so that far block positions keep
 // their accuracy.
 // Longer rows (the logits go through HBM):
@@ -545,21 +545,19 @@ __global__ __launch_bounds__(64 * kRowWaves) void gate_softmax_mask_kernel(
 // Prefill gate for nQB <= kRowsMaxBlocks: three kernels, the logits never leave
 // the chip.
 //
-// gate_pool_project_kernel: the pooling pass over Q and K (the HBM-bound part).
-// K workgroups (first in the grid) take 16 consecutive blocks of one KV head,
-// 2 per wave, pooled into LDS; then the 16 rows go through the head's linear
+// gate_pool_project_kernel: the pooling pass over K.  A workgroup takes 16
+// consecutive blocks of one KV head, 2 per wave, pooled into LDS; then the 16
+// rows go through the head's linear
 // layer on v_mfma_f32_16x16x4f32 (fp32 operands and accumulation) and the block
 // RoPE: wave w computes RoPE tile pair w % P (16-column tiles holding columns e
 // and e + Dg/2 in the same lane) over input-dim slice w / P, the slices summed
 // in order through LDS.  At MFMA step s, lane group kg = lane / 16 feeds dim
 // 16 (s / 4) + 4 kg + s % 4 of its row (one 16-byte LDS read per 4 steps) and
 // the weight row of the same dim (any assignment of dims to k-slots works as
-// long as both operands use it).  Q workgroups take 8 blocks, one per wave, and
-// write the means (the linear layer is gate_qproj_kernel's): a short chain per
-// workgroup keeps the pass's tail short.
+// long as both operands use it).  Q is pooled and projected by gate_rows_kernel,
+// per group of 16 query blocks.
 constexpr int kPPWaves = 8;
 constexpr int kPPRows = 16;   // pooled rows (blocks) per workgroup
-constexpr int kPoolSplit = 2;  // loads of a block issued in this many batches
 
 // Pools block i of one head's rows src [T, D] into dst (Q: the D means; K: the
 // D maxima then the D minima).  Lanes L < D / 8 write; a block at or past nqb
@@ -588,23 +586,22 @@ __device__ __forceinline__ void pool_block_lds(const __bf16* __restrict__ src, i
     a[e] = is_q ? 0.f : -INFINITY;
     m[e] = INFINITY;
   }
-  // kPoolSplit batches of kPerLane / kPoolSplit loads, all of a batch in flight at once.
-  constexpr int H = kPerLane / kPoolSplit;
-#pragma unroll 1
-  for (int h = 0; h < kPoolSplit; ++h) {
+  // All of the block's loads in flight at once.
+  {
+    constexpr int H = kPerLane;
     bf16x8 x[H];
 #pragma unroll
     for (int u = 0; u < H; ++u) {
       // Rows past a short last block re-read its last row (not used): the loads
       // stay unconditional, so none waits on another.  Read once: non-temporal,
       // so they do not displace reused data in L2.
-      const int r = min(r0 + rg + R * (H * h + u), r1 - 1);
+      const int r = min(r0 + rg + R * u, r1 - 1);
       x[u] = __builtin_nontemporal_load(
           reinterpret_cast<const bf16x8*>(src + (size_t)r * D + 8 * ch));
     }
 #pragma unroll
     for (int u = 0; u < H; ++u) {
-      if (r0 + rg + R * (H * h + u) >= r1) continue;
+      if (r0 + rg + R * u >= r1) continue;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float v = (float)x[u][e];
@@ -641,34 +638,16 @@ __device__ __forceinline__ void pool_block_lds(const __bf16* __restrict__ src, i
   }
 }
 
-// Occupancy floor (waves per SIMD, at most 80 registers a lane): three
-// 8-wave workgroups per CU keep enough pooling loads in flight.
-constexpr int kPPWavesPerEU = 6;
 template <int D, int DG>
-__global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(kPPWavesPerEU)))
-void gate_pool_project_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, int B, int Hq, int Hkv, int T,
-    int nqb, const float* __restrict__ wk, RopeFreqs freqs, float* __restrict__ pq,
-    float* __restrict__ kt) {
+__global__ __launch_bounds__(64 * kPPWaves) void gate_pool_project_kernel(
+    const __bf16* __restrict__ k, int Hkv, int T, int nqb, const float* __restrict__ wk,
+    RopeFreqs freqs, float* __restrict__ kt) {
   constexpr int LDR = 2 * D + 4;  // padded LDS row (floats), room for a K row
   __shared__ __attribute__((aligned(16))) float prow[kPPRows][LDR];
   __shared__ float part[kPPWaves][2][4][64];  // each wave's share of the 16 x 2 x 16 products
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int ng = (nqb + kPPRows - 1) / kPPRows;
-  // B (Hq + Hkv) nQB < 2^31 (checked by the host layer): 32-bit unit arithmetic.
-  const int kunits = B * Hkv * ng;
-  if ((int)blockIdx.x >= kunits) {
-    // Q: kPPWaves blocks per workgroup, one per wave, means to pq (the rows
-    // kernel applies the linear layer).
-    const int u = (int)blockIdx.x - kunits;
-    const int nq8 = (nqb + kPPWaves - 1) / kPPWaves;
-    const int bh = u / nq8, i = kPPWaves * (u % nq8) + wv;
-    if (i < nqb)
-      pool_block_lds<D>(q + (size_t)bh * T * D, T, i, nqb, true, lane,
-                        pq + ((size_t)bh * nqb + i) * D);
-    return;
-  }
   const int g = (int)blockIdx.x % ng, bh = (int)blockIdx.x / ng;  // bh = b * Hkv + head
   const int head = bh % Hkv;
   const int din = 2 * D;
@@ -756,108 +735,6 @@ void gate_pool_project_kernel(
   }
 }
 
-// gate_qproj_kernel: Q~ = rope(Qp Wq[h]) for 64 pooled query rows (four groups
-// of 16) of one (batch, head) per workgroup of 8 waves.  The head's weights go
-// through LDS in two halves of 64 dims, all their 16-byte loads (and the rows')
-// in flight at once; wave w computes RoPE tile pair w % P (columns e and
-// e + Dg/2) for the row groups w / P, w / P + 8 / P, ... on
-// v_mfma_f32_16x16x4f32 (dims assigned to k-slots as in
-// gate_pool_project_kernel), each weight read from LDS feeding every row group
-// it serves, then the block RoPE.  With D = 64 the second half re-reads the
-// first (unused); rows past nQB re-read the last row (not written).
-constexpr int kQPRows = 64;
-constexpr int kQPThreads = 512;
-
-template <int DG>
-__global__ __launch_bounds__(kQPThreads) void gate_qproj_kernel(const float* __restrict__ pq,
-                                                                const float* __restrict__ wq,
-                                                                int D, int Hq, int nqb,
-                                                                RopeFreqs freqs,
-                                                                float* __restrict__ qt) {
-  constexpr int NW = kQPThreads / 64;
-  constexpr int WLD = DG + 4;                      // padded weight row in LDS (floats)
-  constexpr int WPT = 64 * DG / 4 / kQPThreads;    // 16-byte weight loads per thread and half
-  constexpr int P = DG / 32;                       // RoPE tile pairs
-  constexpr int NRG = kQPRows / 16;                // row groups
-  constexpr int RPW = P * NRG >= NW ? P * NRG / NW : 1;  // row groups per wave
-  constexpr int RGS = NW / P;                      // row-group stride between a wave's groups
-  __shared__ __attribute__((aligned(16))) float wl[64 * WLD];
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int r = lane & 15, kg = lane >> 4;
-  const int pr = wv % P, rg0 = wv / P;
-  const bool active = rg0 < NRG;
-  const int nblk = (nqb + kQPRows - 1) / kQPRows;
-  const int bh = (int)blockIdx.x / nblk;  // b * Hq + h
-  const int row0 = kQPRows * ((int)blockIdx.x % nblk);
-  const float* w = wq + (size_t)(bh % Hq) * D * DG;
-  const int nh = D / 64;
-  f32x4 wst[2][WPT], av[RPW][8];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int u = 0; u < WPT; ++u) {
-      const int x = threadIdx.x + kQPThreads * u;
-      const int row = 64 * min(h, nh - 1) + x / (DG / 4);
-      wst[h][u] = *reinterpret_cast<const f32x4*>(w + (size_t)row * DG + 4 * (x % (DG / 4)));
-    }
-#pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    const int rg = min(rg0 + RGS * j, NRG - 1);
-    const float* arow = pq + ((size_t)bh * nqb + min(row0 + 16 * rg + r, nqb - 1)) * D;
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-      av[j][t] = *reinterpret_cast<const f32x4*>(arow + 16 * min(t, D / 16 - 1) + 4 * kg);
-  }
-  const int col0 = 16 * pr + r, col1 = col0 + DG / 2;
-  f32x4 acc0[RPW], acc1[RPW];
-#pragma unroll
-  for (int j = 0; j < RPW; ++j) acc0[j] = acc1[j] = f32x4{};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (h > 0) __syncthreads();  // every wave is done with the first half
-#pragma unroll
-    for (int u = 0; u < WPT; ++u) {
-      const int x = threadIdx.x + kQPThreads * u;
-      *reinterpret_cast<f32x4*>(wl + (x / (DG / 4)) * WLD + 4 * (x % (DG / 4))) = wst[h][u];
-    }
-    __syncthreads();
-    if (h < nh && active) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const float* wrow = wl + (16 * t + 4 * kg + qq) * WLD;
-          const float b0 = wrow[col0], b1 = wrow[col1];
-#pragma unroll
-          for (int j = 0; j < RPW; ++j) {
-            acc0[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j][4 * h + t][qq], b0, acc0[j], 0, 0, 0);
-            acc1[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j][4 * h + t][qq], b1, acc1[j], 0, 0, 0);
-          }
-        }
-    }
-  }
-  if (!active) return;
-  // acc[j][v]: row row0 + 16 rg + 4 kg + v, column col0 (acc0) or col1 (acc1).
-  float* out = qt + (size_t)bh * nqb * DG;
-  const double inv_freq = freqs.f[col0];
-#pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    const int rg = rg0 + RGS * j;
-    if (rg >= NRG) break;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int i = row0 + 16 * rg + 4 * kg + v;
-      float y1, y2;
-      rope_rotate(inv_freq, i, acc0[j][v], acc1[j][v], y1, y2);
-      if (i < nqb) {
-        out[(size_t)i * DG + col0] = y1;
-        out[(size_t)i * DG + col1] = y2;
-      }
-    }
-  }
-}
-
 // gate_rows_kernel: the Q~ rows, logits, softmax (and with MASK the block
 // selection) of one group of 16 query blocks of one (batch, head).  Group g has
 // g + 1 tiles of 16 x 16 logits.  Workgroups take the groups in blocks of 8
@@ -867,7 +744,11 @@ __global__ __launch_bounds__(kQPThreads) void gate_qproj_kernel(const float* __r
 // overlaps another's matrix work.  Only the logits take LDS and the registers
 // stay within 128, so four workgroups fit on a CU at 512 query blocks (all of
 // them at once for 32 heads).
-// * Q~ operands (from gate_qproj_kernel) in registers, loaded once.
+// * Q~ rows: the group's 16 query blocks are pooled (means) into LDS, go through
+//   the head's linear layer on v_mfma_f32_16x16x4f32 (wave w < Dg/32 takes RoPE
+//   tile pair w, columns e and e + Dg/2, over all D input dims, dims assigned to
+//   k-slots as in gate_pool_project_kernel) and the block RoPE, and each lane then
+//   holds its Q~ operands in registers.
 // * Logits: the waves take the tiles round robin, Q~ K~^T on
 //   v_mfma_f32_16x16x4f32 (the next tile's K~ rows loading during the current
 //   tile's MFMAs), and write the scaled logits (-inf above the diagonal) into
@@ -910,23 +791,26 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return (row_lanes(v, 0) + row_lanes(v, 1)) + (row_lanes(v, 2) + row_lanes(v, 3));
 }
 
-// Dynamic LDS of gate_rows_kernel: the logits of a group (16 x 16 G fp32).
-size_t gate_rows_lds_bytes(int nqb, int dg) {
+// Dynamic LDS of gate_rows_kernel: first the pooled Q rows [16][D + 4] and the
+// Q~ rows [16][Dg + 4], then, in the same space, the logits of the group
+// (16 x 16 G fp32).
+size_t gate_rows_lds_bytes(int nqb, int d, int dg) {
   const int G = (nqb + kRowGroup - 1) / kRowGroup;
-  (void)dg;
-  return (size_t)kRowGroup * kRowGroup * G * sizeof(float);
+  const size_t logits = (size_t)kRowGroup * kRowGroup * G;
+  const size_t qrows = (size_t)kRowGroup * (d + 4) + (size_t)kRowGroup * (dg + 4);
+  return (logits > qrows ? logits : qrows) * sizeof(float);
 }
 
-template <int DG, int NPL, bool MASK>
+template <int D, int DG, int NPL, bool MASK>
 __global__ __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu(4))) void gate_rows_kernel(
-    const float* __restrict__ qt, const float* __restrict__ kt, int BHq, int Hq, int Hkv,
-    int nqb, float scale,
+    const __bf16* __restrict__ q, int T, const float* __restrict__ wq, RopeFreqs freqs,
+    const float* __restrict__ kt, int BHq, int Hq, int Hkv, int nqb, float scale,
     float* __restrict__ scores, int mode, float tau, double density, int keep_sink,
     int32_t* __restrict__ idx, int32_t* __restrict__ cnt, int max_k) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ int hist_all[MASK ? kRowsWaves : 1][256];
   constexpr int NV = DG / 16;     // 16-byte operand reads per lane and row
-  float* lg = smem;  // logits [16][16 (g + 1)]
+  float* lg = smem;  // logits [16][16 (g + 1)], once the Q~ operands are in registers
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int r = lane & 15, kg = lane >> 4;
@@ -944,15 +828,69 @@ __global__ __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu
   const int ntile = g + 1;
   const int width = kRowGroup * ntile;  // logit row length in LDS
 
-  // This lane's Q~ operands (row r of the group, dims 16 t + 4 kg .. + 3), held in
-  // registers for every tile; rows past nQB re-read the last row (their logits are
-  // never read).
-  f32x4 qv[NV];
-  {
-    const float* qrow = qt + ((size_t)bh * nqb + min(kRowGroup * g + r, nqb - 1)) * DG + 4 * kg;
-#pragma unroll
-    for (int t = 0; t < NV; ++t) qv[t] = *reinterpret_cast<const f32x4*>(qrow + 16 * t);
+  // Q~ of the group: pooled means (blocks past nQB give zero rows, whose logits
+  // are never read), the linear layer and the block RoPE, into LDS.
+  constexpr int LDQ = D + 4, LDT = DG + 4;  // padded LDS rows (floats)
+  float* prow = smem;                 // pooled Q means [16][LDQ]
+  float* qs = smem + kRowGroup * LDQ;  // Q~ rows [16][LDT]
+#pragma unroll 1
+  for (int t = 0; t < kRowGroup / kRowsWaves; ++t) {
+    const int rr = (kRowGroup / kRowsWaves) * wv + t;
+    pool_block_lds<D>(q + (size_t)bh * T * D, T, kRowGroup * g + rr, nqb, true, lane,
+                      prow + rr * LDQ);
   }
+  __syncthreads();
+  if (wv < DG / 32) {
+    // RoPE tile pair wv: columns col0 and col0 + Dg/2, all D input dims, the
+    // weights of CB 16-dim groups requested together.
+    constexpr int NT = D / 16;
+    constexpr int CB = 4;
+    const float* w = wq + (size_t)(bh % Hq) * D * DG;
+    const int col0 = 16 * wv + r, col1 = col0 + DG / 2;
+    f32x4 acc0 = {}, acc1 = {};
+#pragma unroll 1
+    for (int t0 = 0; t0 < NT; t0 += CB) {
+      float wr[CB][8];
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const int t = min(t0 + c, NT - 1);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const float* wrow = w + (size_t)(16 * t + 4 * kg + qq) * DG;
+          wr[c][qq] = wrow[col0];
+          wr[c][4 + qq] = wrow[col1];
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const int t = min(t0 + c, NT - 1);
+        f32x4 av = *reinterpret_cast<const f32x4*>(prow + r * LDQ + 16 * t + 4 * kg);
+        if (t0 + c >= NT) av = f32x4{};
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[qq], wr[c][qq], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[qq], wr[c][4 + qq], acc1, 0, 0, 0);
+        }
+      }
+    }
+    // acc[v]: row 4 kg + v of the group, column col0 (acc0) or col1 (acc1).
+    const double inv_freq = freqs.f[col0];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float y1, y2;
+      rope_rotate(inv_freq, kRowGroup * g + 4 * kg + v, acc0[v], acc1[v], y1, y2);
+      qs[(4 * kg + v) * LDT + col0] = y1;
+      qs[(4 * kg + v) * LDT + col1] = y2;
+    }
+  }
+  __syncthreads();
+  // This lane's Q~ operands (row r of the group, dims 16 t + 4 kg .. + 3), held in
+  // registers for every tile.
+  f32x4 qv[NV];
+#pragma unroll
+  for (int t = 0; t < NV; ++t)
+    qv[t] = *reinterpret_cast<const f32x4*>(qs + r * LDT + 16 * t + 4 * kg);
+  __syncthreads();  // the logits below reuse this LDS
 
   // Logits: lane (r, kg) feeds dims 16 t + 4 kg .. + 3 of row r of both
   // operands at MFMA steps 4 t .. 4 t + 3.  K~ rows past nQB (the last group's
@@ -1548,18 +1486,16 @@ hipError_t gate_logits(int B, int Hq, int Hkv, int nqb, int dg, float scale, con
 // The one-pass gate's front (nQB <= kRowsMaxBlocks), two kernels: K~
 // [B,Hkv,nQB,Dg] at the start of ws, then the pooled Q [B,Hq,nQB,D], then Q~
 // [B,Hq,nQB,Dg].
-hipError_t gate_pool_project(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
-                             const float* wq, const float* wk, int dg, float rope_base,
-                             float* ws, hipStream_t stream) {
+hipError_t gate_pool_keys(const void* k, int B, int Hkv, int T, int D, const float* wk, int dg,
+                          float rope_base, float* ws, hipStream_t stream) {
   const int nqb = (T + kTile - 1) / kTile;
   float* kt = ws;
-  float* pq = ws + (size_t)B * Hkv * nqb * dg;
-  const size_t ng = (nqb + kPPRows - 1) / kPPRows, nq8 = (nqb + kPPWaves - 1) / kPPWaves;
-  const dim3 grid((unsigned)((size_t)B * Hkv * ng + (size_t)B * Hq * nq8));
+  const size_t ng = (nqb + kPPRows - 1) / kPPRows;
+  const dim3 grid((unsigned)((size_t)B * Hkv * ng));
   const RopeFreqs freqs = rope_freqs(rope_base, dg);
 #define SEER_GATE_PP(DD, DG)                                                                   \
   hipLaunchKernelGGL((gate_pool_project_kernel<DD, DG>), grid, dim3(64 * kPPWaves), 0, stream, \
-                     (const __bf16*)q, (const __bf16*)k, B, Hq, Hkv, T, nqb, wk, freqs, pq, kt)
+                     (const __bf16*)k, Hkv, T, nqb, wk, freqs, kt)
   if (D == 128) {
     if (dg == 128) SEER_GATE_PP(128, 128);
     else if (dg == 64) SEER_GATE_PP(128, 64);
@@ -1570,29 +1506,18 @@ hipError_t gate_pool_project(const void* q, const void* k, int B, int Hq, int Hk
     else SEER_GATE_PP(64, 32);
   }
 #undef SEER_GATE_PP
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  float* qt = pq + (size_t)B * Hq * nqb * D;
-  const dim3 qgrid((unsigned)((size_t)B * Hq * ((nqb + kQPRows - 1) / kQPRows)));
-#define SEER_GATE_QP(DG)                                                                      \
-  hipLaunchKernelGGL(gate_qproj_kernel<DG>, qgrid, dim3(kQPThreads), 0, stream, pq, wq, D, Hq, \
-                     nqb, freqs, qt)
-  if (dg == 128) SEER_GATE_QP(128);
-  else if (dg == 64) SEER_GATE_QP(64);
-  else SEER_GATE_QP(32);
-#undef SEER_GATE_QP
   return hipGetLastError();
 }
 
-template <int DG, int NPL, bool MASK>
-hipError_t gate_rows_launch(int B, int Hq, int Hkv, int nqb, int D, float scale, const float* ws,
+template <int D, int DG, int NPL, bool MASK>
+hipError_t gate_rows_launch(const void* q, int T, const float* wq, const RopeFreqs& freqs, int B,
+                            int Hq, int Hkv, int nqb, float scale, const float* ws,
                             float* scores, int mode, float tau, double density, int keep_sink,
                             int32_t* idx, int32_t* cnt, int max_k, hipStream_t stream) {
   const float* kt = ws;
-  const float* qt = ws + (size_t)B * Hkv * nqb * DG + (size_t)B * Hq * nqb * D;
   const int G = (nqb + kRowGroup - 1) / kRowGroup;
-  const size_t lds = gate_rows_lds_bytes(nqb, DG);
-  auto kern = gate_rows_kernel<DG, NPL, MASK>;
+  const size_t lds = gate_rows_lds_bytes(nqb, D, DG);
+  auto kern = gate_rows_kernel<D, DG, NPL, MASK>;
   if (lds > 65536) {
     const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1600,31 +1525,39 @@ hipError_t gate_rows_launch(int B, int Hq, int Hkv, int nqb, int D, float scale,
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)((size_t)B * Hq * G)), dim3(64 * kRowsWaves), lds,
-                     stream, qt, kt, B * Hq, Hq, Hkv, nqb, scale, scores, mode, tau, density,
-                     keep_sink, idx, cnt, max_k);
+                     stream, (const __bf16*)q, T, wq, freqs, kt, B * Hq, Hq, Hkv, nqb, scale,
+                     scores, mode, tau, density, keep_sink, idx, cnt, max_k);
   return hipGetLastError();
 }
 
 template <bool MASK>
-hipError_t gate_rows(int B, int Hq, int Hkv, int nqb, int D, int dg, float scale, const float* ws,
-                     float* scores, int mode, float tau, double density, int keep_sink,
-                     int32_t* idx, int32_t* cnt, int max_k, hipStream_t stream) {
-#define SEER_GATE_ROWS_CALL(DG, NPL)                                                       \
-  return gate_rows_launch<DG, NPL, MASK>(B, Hq, Hkv, nqb, D, scale, ws, scores, mode, tau, \
-                                         density, keep_sink, idx, cnt, max_k, stream)
-#define SEER_GATE_ROWS_NPL(DG)                     \
-  do {                                             \
-    if (nqb <= 64) SEER_GATE_ROWS_CALL(DG, 1);     \
-    if (nqb <= 64 * 4) SEER_GATE_ROWS_CALL(DG, 4); \
-    if (nqb <= 64 * 8) SEER_GATE_ROWS_CALL(DG, 8); \
-    if (nqb <= 64 * 16) SEER_GATE_ROWS_CALL(DG, 16); \
-    SEER_GATE_ROWS_CALL(DG, 32);                   \
+hipError_t gate_rows(const void* q, int T, int D, const float* wq, float rope_base, int B, int Hq,
+                     int Hkv, int nqb, int dg, float scale, const float* ws, float* scores,
+                     int mode, float tau, double density, int keep_sink, int32_t* idx,
+                     int32_t* cnt, int max_k, hipStream_t stream) {
+  const RopeFreqs freqs = rope_freqs(rope_base, dg);
+#define SEER_GATE_ROWS_CALL(DD, DG, NPL)                                                      \
+  return gate_rows_launch<DD, DG, NPL, MASK>(q, T, wq, freqs, B, Hq, Hkv, nqb, scale, ws,    \
+                                             scores, mode, tau, density, keep_sink, idx, cnt, \
+                                             max_k, stream)
+#define SEER_GATE_ROWS_NPL(DD, DG)                     \
+  do {                                                 \
+    if (nqb <= 64) SEER_GATE_ROWS_CALL(DD, DG, 1);     \
+    if (nqb <= 64 * 4) SEER_GATE_ROWS_CALL(DD, DG, 4); \
+    if (nqb <= 64 * 8) SEER_GATE_ROWS_CALL(DD, DG, 8); \
+    if (nqb <= 64 * 16) SEER_GATE_ROWS_CALL(DD, DG, 16); \
+    SEER_GATE_ROWS_CALL(DD, DG, 32);                   \
   } while (0)
   static_assert(kRowsMaxBlocks == 64 * 32, "NPL ladder covers kRowsMaxBlocks");
   if (nqb > kRowsMaxBlocks) return hipErrorInvalidValue;
-  if (dg == 128) SEER_GATE_ROWS_NPL(128);
-  if (dg == 64) SEER_GATE_ROWS_NPL(64);
-  SEER_GATE_ROWS_NPL(32);
+  if (D == 128) {
+    if (dg == 128) SEER_GATE_ROWS_NPL(128, 128);
+    if (dg == 64) SEER_GATE_ROWS_NPL(128, 64);
+    SEER_GATE_ROWS_NPL(128, 32);
+  }
+  if (dg == 128) SEER_GATE_ROWS_NPL(64, 128);
+  if (dg == 64) SEER_GATE_ROWS_NPL(64, 64);
+  SEER_GATE_ROWS_NPL(64, 32);
 #undef SEER_GATE_ROWS_NPL
 #undef SEER_GATE_ROWS_CALL
 }
@@ -1637,9 +1570,10 @@ hipError_t launch_attn_gate(const void* q, const void* k, int B, int Hq, int Hkv
   const int nqb = (T + kTile - 1) / kTile;
   if ((size_t)B * Hq * nqb == 0) return hipSuccess;
   if (nqb <= kRowsMaxBlocks) {
-    hipError_t err = gate_pool_project(q, k, B, Hq, Hkv, T, D, wq, wk, dg, rope_base, ws, stream);
+    hipError_t err = gate_pool_keys(k, B, Hkv, T, D, wk, dg, rope_base, ws, stream);
     if (err != hipSuccess) return err;
-    return gate_rows<false>(B, Hq, Hkv, nqb, D, dg, scale, ws, scores, 0, 0.f, 0.0, 0, nullptr,
+    return gate_rows<false>(q, T, D, wq, rope_base, B, Hq, Hkv, nqb, dg, scale, ws, scores, 0,
+                            0.f, 0.0, 0, nullptr,
                             nullptr, 1, stream);
   }
   float2* part = nullptr;
@@ -1662,10 +1596,10 @@ hipError_t launch_attn_gate_mask(const void* q, const void* k, int B, int Hq, in
   const int nqb = (T + kTile - 1) / kTile;
   if ((size_t)B * Hq * nqb == 0) return hipSuccess;
   if (nqb <= kRowsMaxBlocks) {  // the logits stay on chip: no passes, no logits buffer
-    hipError_t err = gate_pool_project(q, k, B, Hq, Hkv, T, D, wq, wk, dg, rope_base, ws, stream);
+    hipError_t err = gate_pool_keys(k, B, Hkv, T, D, wk, dg, rope_base, ws, stream);
     if (err != hipSuccess) return err;
-    return gate_rows<true>(B, Hq, Hkv, nqb, D, dg, scale, ws, scores, mode, threshold, density,
-                           keep_sink, idx, cnt, max_k, stream);
+    return gate_rows<true>(q, T, D, wq, rope_base, B, Hq, Hkv, nqb, dg, scale, ws, scores, mode,
+                           threshold, density, keep_sink, idx, cnt, max_k, stream);
   }
   // Without a scores buffer the logits live past the gate's own workspace, at
   // the next 256-byte boundary (within the 256 bytes of slack the workspace
