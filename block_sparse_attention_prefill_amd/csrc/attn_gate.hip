@@ -11,12 +11,14 @@
 // Map)").  Threshold or TopK on these scores (seer_build_mask) gives the mask.
 //
 // Prefill kernels, up to 2048 query blocks (rows whose logits fit in LDS):
-// * gate_pool_project_kernel: the pooling pass over K; K~ (linear layer and
-//   block RoPE on the fp32 matrix cores) for every block.
-// * gate_rows_kernel: per group of 16 query blocks, the Q pooling, linear layer
-//   and block RoPE, the causal logits Q~ K~^T (fp32 matrix cores) into LDS, the
-//   exact row softmax, the score rows written once; the fused variant selects
-//   each row's block list from the same values.
+// * gate_pool_project_kernel: the pooling pass over K, K~ (linear layer and
+//   block RoPE on the fp32 matrix cores) for every block, and the Q means of the
+//   heavier half of the query groups.
+// * gate_rows_kernel: per group of 16 query blocks, the Q pooling (lighter
+//   half) or the means from the pass above, the linear layer and block RoPE, the
+//   causal logits Q~ K~^T (fp32 matrix cores) into LDS, the exact row softmax,
+//   the score rows written once; the fused variant selects each row's block list
+//   from the same values.
 // RoPE angles are formed and reduced in fp64 so that far block positions keep
 // their accuracy.
 // Longer rows (the logits go through HBM):
@@ -545,24 +547,26 @@ __global__ __launch_bounds__(64 * kRowWaves) void gate_softmax_mask_kernel(
 // Prefill gate for nQB <= kRowsMaxBlocks: three kernels, the logits never leave
 // the chip.
 //
-// gate_pool_project_kernel: the pooling pass over K.  A workgroup takes 16
-// consecutive blocks of one KV head, 2 per wave, pooled into LDS; then the 16
-// rows go through the head's linear
+// gate_pool_project_kernel: the pooling pass over K and part of Q.  A K
+// workgroup (first in the grid) takes 16 consecutive blocks of one KV head, 2
+// per wave, pooled into LDS; then the 16 rows go through the head's linear
 // layer on v_mfma_f32_16x16x4f32 (fp32 operands and accumulation) and the block
 // RoPE: wave w computes RoPE tile pair w % P (16-column tiles holding columns e
 // and e + Dg/2 in the same lane) over input-dim slice w / P, the slices summed
 // in order through LDS.  At MFMA step s, lane group kg = lane / 16 feeds dim
 // 16 (s / 4) + 4 kg + s % 4 of its row (one 16-byte LDS read per 4 steps) and
 // the weight row of the same dim (any assignment of dims to k-slots works as
-// long as both operands use it).  Q is pooled and projected by gate_rows_kernel,
-// per group of 16 query blocks.
+// long as both operands use it).  Q workgroups take 8 query blocks at or past
+// qsplit (the heavier groups), one per wave, and write the means; the rest of Q
+// is pooled by gate_rows_kernel, and all of it projected there.
 constexpr int kPPWaves = 8;
 constexpr int kPPRows = 16;   // pooled rows (blocks) per workgroup
 
 // Pools block i of one head's rows src [T, D] into dst (Q: the D means; K: the
-// D maxima then the D minima).  Lanes L < D / 8 write; a block at or past nqb
-// gives zeros.
-template <int D>
+// D maxima then the D minima), its loads issued in SPLIT batches.  Lanes
+// L < D / 8 write; a block at or past nqb gives zeros.  The sums run over the
+// rows in the same order for any SPLIT.
+template <int D, int SPLIT>
 __device__ __forceinline__ void pool_block_lds(const __bf16* __restrict__ src, int T, int i,
                                                int nqb, bool is_q, int lane, float* dst) {
   constexpr int C = D / 8;   // chunks per row
@@ -586,22 +590,23 @@ __device__ __forceinline__ void pool_block_lds(const __bf16* __restrict__ src, i
     a[e] = is_q ? 0.f : -INFINITY;
     m[e] = INFINITY;
   }
-  // All of the block's loads in flight at once.
-  {
-    constexpr int H = kPerLane;
+  // SPLIT batches of kPerLane / SPLIT loads, all of a batch in flight at once.
+  constexpr int H = kPerLane / SPLIT;
+#pragma unroll 1
+  for (int h = 0; h < SPLIT; ++h) {
     bf16x8 x[H];
 #pragma unroll
     for (int u = 0; u < H; ++u) {
       // Rows past a short last block re-read its last row (not used): the loads
       // stay unconditional, so none waits on another.  Read once: non-temporal,
       // so they do not displace reused data in L2.
-      const int r = min(r0 + rg + R * u, r1 - 1);
+      const int r = min(r0 + rg + R * (H * h + u), r1 - 1);
       x[u] = __builtin_nontemporal_load(
           reinterpret_cast<const bf16x8*>(src + (size_t)r * D + 8 * ch));
     }
 #pragma unroll
     for (int u = 0; u < H; ++u) {
-      if (r0 + rg + R * u >= r1) continue;
+      if (r0 + rg + R * (H * h + u) >= r1) continue;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float v = (float)x[u][e];
@@ -639,15 +644,28 @@ __device__ __forceinline__ void pool_block_lds(const __bf16* __restrict__ src, i
 }
 
 template <int D, int DG>
-__global__ __launch_bounds__(64 * kPPWaves) void gate_pool_project_kernel(
-    const __bf16* __restrict__ k, int Hkv, int T, int nqb, const float* __restrict__ wk,
-    RopeFreqs freqs, float* __restrict__ kt) {
+__global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(6)))
+void gate_pool_project_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, int B, int Hkv, int T, int nqb,
+    int qsplit, const float* __restrict__ wk, RopeFreqs freqs, float* __restrict__ pq,
+    float* __restrict__ kt) {
   constexpr int LDR = 2 * D + 4;  // padded LDS row (floats), room for a K row
   __shared__ __attribute__((aligned(16))) float prow[kPPRows][LDR];
   __shared__ float part[kPPWaves][2][4][64];  // each wave's share of the 16 x 2 x 16 products
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int ng = (nqb + kPPRows - 1) / kPPRows;
+  const int kunits = B * Hkv * ng;
+  if ((int)blockIdx.x >= kunits) {
+    // Q: kPPWaves blocks at or past qsplit per workgroup, one per wave, means to pq.
+    const int u = (int)blockIdx.x - kunits;
+    const int nq8 = (nqb - qsplit + kPPWaves - 1) / kPPWaves;
+    const int bh = u / nq8, i = qsplit + kPPWaves * (u % nq8) + wv;
+    if (i < nqb)
+      pool_block_lds<D, 2>(q + (size_t)bh * T * D, T, i, nqb, true, lane,
+                           pq + ((size_t)bh * nqb + i) * D);
+    return;
+  }
   const int g = (int)blockIdx.x % ng, bh = (int)blockIdx.x / ng;  // bh = b * Hkv + head
   const int head = bh % Hkv;
   const int din = 2 * D;
@@ -655,7 +673,7 @@ __global__ __launch_bounds__(64 * kPPWaves) void gate_pool_project_kernel(
 #pragma unroll 1
   for (int t = 0; t < kPPRows / kPPWaves; ++t) {
     const int r = (kPPRows / kPPWaves) * wv + t;
-    pool_block_lds<D>(src, T, kPPRows * g + r, nqb, false, lane, &prow[r][0]);
+    pool_block_lds<D, 2>(src, T, kPPRows * g + r, nqb, false, lane, &prow[r][0]);
   }
   __syncthreads();
   // Wave w: RoPE tile pair w % P (tiles w % P and w % P + Dg/32, columns e and
@@ -744,7 +762,8 @@ __global__ __launch_bounds__(64 * kPPWaves) void gate_pool_project_kernel(
 // overlaps another's matrix work.  Only the logits take LDS and the registers
 // stay within 128, so four workgroups fit on a CU at 512 query blocks (all of
 // them at once for 32 heads).
-// * Q~ rows: the group's 16 query blocks are pooled (means) into LDS, go through
+// * Q~ rows: the group's 16 query blocks are pooled (means) into LDS (or, for the
+//   heavier groups, their means are copied from gate_pool_project_kernel), go through
 //   the head's linear layer on v_mfma_f32_16x16x4f32 (wave w < Dg/32 takes RoPE
 //   tile pair w, columns e and e + Dg/2, over all D input dims, dims assigned to
 //   k-slots as in gate_pool_project_kernel) and the block RoPE, and each lane then
@@ -760,7 +779,8 @@ __global__ __launch_bounds__(64 * kPPWaves) void gate_pool_project_kernel(
 //   so the fused lists are those of the scores, bit for bit.
 constexpr int kRowGroup = 16;         // query blocks per row group
 constexpr int kRowsWaves = 4;
-constexpr int kRowsMaxBlocks = 2048;  // LDS: 16 nQB fp32 logits per workgroup
+constexpr int kRowsMaxBlocks = 2048;
+constexpr int kGateSplitNum = 1, kGateSplitDen = 2;  // share of groups pooled in the rows kernel  // LDS: 16 nQB fp32 logits per workgroup
 
 // Wave-wide max and sum with the same value in every lane.  Within each row of
 // 16 lanes, DPP moves pair every lane with a partner holding the same partial
@@ -803,7 +823,8 @@ size_t gate_rows_lds_bytes(int nqb, int d, int dg) {
 
 template <int D, int DG, int NPL, bool MASK>
 __global__ __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu(4))) void gate_rows_kernel(
-    const __bf16* __restrict__ q, int T, const float* __restrict__ wq, RopeFreqs freqs,
+    const __bf16* __restrict__ q, int T, const float* __restrict__ pq, int qsplit,
+    const float* __restrict__ wq, RopeFreqs freqs,
     const float* __restrict__ kt, int BHq, int Hq, int Hkv, int nqb, float scale,
     float* __restrict__ scores, int mode, float tau, double density, int keep_sink,
     int32_t* __restrict__ idx, int32_t* __restrict__ cnt, int max_k) {
@@ -833,11 +854,22 @@ __global__ __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu
   constexpr int LDQ = D + 4, LDT = DG + 4;  // padded LDS rows (floats)
   float* prow = smem;                 // pooled Q means [16][LDQ]
   float* qs = smem + kRowGroup * LDQ;  // Q~ rows [16][LDT]
+  if (kRowGroup * g >= qsplit) {
+    // Pooled by gate_pool_project_kernel: copy the means.
+    constexpr int C4 = D / 4;
+    for (int x = threadIdx.x; x < kRowGroup * C4; x += 64 * kRowsWaves) {
+      const int rr = x / C4, i = min(kRowGroup * g + rr, nqb - 1);
+      f32x4 v = *reinterpret_cast<const f32x4*>(pq + ((size_t)bh * nqb + i) * D + 4 * (x % C4));
+      if (kRowGroup * g + rr >= nqb) v = f32x4{};
+      *reinterpret_cast<f32x4*>(prow + rr * LDQ + 4 * (x % C4)) = v;
+    }
+  } else {
 #pragma unroll 1
-  for (int t = 0; t < kRowGroup / kRowsWaves; ++t) {
-    const int rr = (kRowGroup / kRowsWaves) * wv + t;
-    pool_block_lds<D>(q + (size_t)bh * T * D, T, kRowGroup * g + rr, nqb, true, lane,
-                      prow + rr * LDQ);
+    for (int t = 0; t < kRowGroup / kRowsWaves; ++t) {
+      const int rr = (kRowGroup / kRowsWaves) * wv + t;
+      pool_block_lds<D, 1>(q + (size_t)bh * T * D, T, kRowGroup * g + rr, nqb, true, lane,
+                           prow + rr * LDQ);
+    }
   }
   __syncthreads();
   if (wv < DG / 32) {
@@ -1486,16 +1518,20 @@ hipError_t gate_logits(int B, int Hq, int Hkv, int nqb, int dg, float scale, con
 // The one-pass gate's front (nQB <= kRowsMaxBlocks), two kernels: K~
 // [B,Hkv,nQB,Dg] at the start of ws, then the pooled Q [B,Hq,nQB,D], then Q~
 // [B,Hq,nQB,Dg].
-hipError_t gate_pool_keys(const void* k, int B, int Hkv, int T, int D, const float* wk, int dg,
-                          float rope_base, float* ws, hipStream_t stream) {
+hipError_t gate_pool_keys(const void* q, const void* k, int B, int Hq, int Hkv, int T, int D,
+                          const float* wk, int dg, float rope_base, int qsplit, float* ws,
+                          hipStream_t stream) {
   const int nqb = (T + kTile - 1) / kTile;
   float* kt = ws;
+  float* pq = ws + (size_t)B * Hkv * nqb * dg;
   const size_t ng = (nqb + kPPRows - 1) / kPPRows;
-  const dim3 grid((unsigned)((size_t)B * Hkv * ng));
+  const size_t nq8 = (nqb - qsplit + kPPWaves - 1) / kPPWaves;
+  const dim3 grid((unsigned)((size_t)B * Hkv * ng + (size_t)B * Hq * nq8));
   const RopeFreqs freqs = rope_freqs(rope_base, dg);
 #define SEER_GATE_PP(DD, DG)                                                                   \
   hipLaunchKernelGGL((gate_pool_project_kernel<DD, DG>), grid, dim3(64 * kPPWaves), 0, stream, \
-                     (const __bf16*)k, Hkv, T, nqb, wk, freqs, kt)
+                     (const __bf16*)q, (const __bf16*)k, B, Hkv, T, nqb, qsplit, wk, freqs, \
+                     pq, kt)
   if (D == 128) {
     if (dg == 128) SEER_GATE_PP(128, 128);
     else if (dg == 64) SEER_GATE_PP(128, 64);
@@ -1509,12 +1545,21 @@ hipError_t gate_pool_keys(const void* k, int B, int Hkv, int T, int D, const flo
   return hipGetLastError();
 }
 
+// First query block whose Q the pooling kernel pools (the heavier groups, at or
+// past it, then start their logits at once while the others pool).
+int gate_qsplit(int nqb) {
+  const int G = (nqb + kRowGroup - 1) / kRowGroup;
+  return kRowGroup * (G * kGateSplitNum / kGateSplitDen);
+}
+
 template <int D, int DG, int NPL, bool MASK>
-hipError_t gate_rows_launch(const void* q, int T, const float* wq, const RopeFreqs& freqs, int B,
-                            int Hq, int Hkv, int nqb, float scale, const float* ws,
+hipError_t gate_rows_launch(const void* q, int T, int qsplit, const float* wq,
+                            const RopeFreqs& freqs, int B, int Hq, int Hkv, int nqb, float scale,
+                            const float* ws,
                             float* scores, int mode, float tau, double density, int keep_sink,
                             int32_t* idx, int32_t* cnt, int max_k, hipStream_t stream) {
   const float* kt = ws;
+  const float* pq = ws + (size_t)B * Hkv * nqb * DG;
   const int G = (nqb + kRowGroup - 1) / kRowGroup;
   const size_t lds = gate_rows_lds_bytes(nqb, D, DG);
   auto kern = gate_rows_kernel<D, DG, NPL, MASK>;
@@ -1525,19 +1570,21 @@ hipError_t gate_rows_launch(const void* q, int T, const float* wq, const RopeFre
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)((size_t)B * Hq * G)), dim3(64 * kRowsWaves), lds,
-                     stream, (const __bf16*)q, T, wq, freqs, kt, B * Hq, Hq, Hkv, nqb, scale,
+                     stream, (const __bf16*)q, T, pq, qsplit, wq, freqs, kt, B * Hq, Hq, Hkv,
+                     nqb, scale,
                      scores, mode, tau, density, keep_sink, idx, cnt, max_k);
   return hipGetLastError();
 }
 
 template <bool MASK>
-hipError_t gate_rows(const void* q, int T, int D, const float* wq, float rope_base, int B, int Hq,
-                     int Hkv, int nqb, int dg, float scale, const float* ws, float* scores,
+hipError_t gate_rows(const void* q, int T, int D, int qsplit, const float* wq, float rope_base,
+                     int B, int Hq, int Hkv, int nqb, int dg, float scale, const float* ws,
+                     float* scores,
                      int mode, float tau, double density, int keep_sink, int32_t* idx,
                      int32_t* cnt, int max_k, hipStream_t stream) {
   const RopeFreqs freqs = rope_freqs(rope_base, dg);
 #define SEER_GATE_ROWS_CALL(DD, DG, NPL)                                                      \
-  return gate_rows_launch<DD, DG, NPL, MASK>(q, T, wq, freqs, B, Hq, Hkv, nqb, scale, ws,    \
+  return gate_rows_launch<DD, DG, NPL, MASK>(q, T, qsplit, wq, freqs, B, Hq, Hkv, nqb, scale, ws, \
                                              scores, mode, tau, density, keep_sink, idx, cnt, \
                                              max_k, stream)
 #define SEER_GATE_ROWS_NPL(DD, DG)                     \
@@ -1570,9 +1617,10 @@ hipError_t launch_attn_gate(const void* q, const void* k, int B, int Hq, int Hkv
   const int nqb = (T + kTile - 1) / kTile;
   if ((size_t)B * Hq * nqb == 0) return hipSuccess;
   if (nqb <= kRowsMaxBlocks) {
-    hipError_t err = gate_pool_keys(k, B, Hkv, T, D, wk, dg, rope_base, ws, stream);
+    const int qsplit = gate_qsplit(nqb);
+    hipError_t err = gate_pool_keys(q, k, B, Hq, Hkv, T, D, wk, dg, rope_base, qsplit, ws, stream);
     if (err != hipSuccess) return err;
-    return gate_rows<false>(q, T, D, wq, rope_base, B, Hq, Hkv, nqb, dg, scale, ws, scores, 0,
+    return gate_rows<false>(q, T, D, qsplit, wq, rope_base, B, Hq, Hkv, nqb, dg, scale, ws, scores, 0,
                             0.f, 0.0, 0, nullptr,
                             nullptr, 1, stream);
   }
@@ -1596,9 +1644,10 @@ hipError_t launch_attn_gate_mask(const void* q, const void* k, int B, int Hq, in
   const int nqb = (T + kTile - 1) / kTile;
   if ((size_t)B * Hq * nqb == 0) return hipSuccess;
   if (nqb <= kRowsMaxBlocks) {  // the logits stay on chip: no passes, no logits buffer
-    hipError_t err = gate_pool_keys(k, B, Hkv, T, D, wk, dg, rope_base, ws, stream);
+    const int qsplit = gate_qsplit(nqb);
+    hipError_t err = gate_pool_keys(q, k, B, Hq, Hkv, T, D, wk, dg, rope_base, qsplit, ws, stream);
     if (err != hipSuccess) return err;
-    return gate_rows<true>(q, T, D, wq, rope_base, B, Hq, Hkv, nqb, dg, scale, ws, scores, mode,
+    return gate_rows<true>(q, T, D, qsplit, wq, rope_base, B, Hq, Hkv, nqb, dg, scale, ws, scores, mode,
                            threshold, density, keep_sink, idx, cnt, max_k, stream);
   }
   // Without a scores buffer the logits live past the gate's own workspace, at
