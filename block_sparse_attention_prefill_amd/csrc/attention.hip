@@ -34,12 +34,13 @@
 //   free.  K fragments are plain 16-byte LDS reads; V^T fragments come from
 //   ds_read_b64_tr_b16, which transposes 4x16 bf16 blocks on the fly into the
 //   key order of P^T's registers.
-// * K and V of a tile are separate pipeline stages.  The sparse pass keeps one
-//   LDS slot per workgroup (K(j), then V(j), then K(j+1)): V(j) streams in during
-//   the softmax, and the small footprint lets a CU hold 6 workgroups whose
-//   copies cover each other's waits.  The pooled pass keeps a ring of two K
-//   slots and one V slot per (two-item) workgroup, so K(j+1) streams in during
-//   tile j and V(j+1) during QK of tile j+1.
+// * K and V of a tile are separate pipeline stages.  The sparse pass streams
+//   them in parts of 64 keys x 64 head-dims through a ring of three part slots
+//   per workgroup (two parts in flight while one is computed on), and the small
+//   footprint (26 KB) lets a CU hold 6 workgroups whose copies cover each
+//   other's waits.  The pooled pass keeps a ring of two K slots and one V slot
+//   per (two-item) workgroup, so K(j+1) streams in during tile j and V(j+1)
+//   during QK of tile j+1.
 // * exp2 with log2(e) folded into the softmax scale; fp32 row statistics; the
 //   reference max is raised lazily (only when a tile exceeds it by 2^8), which
 //   leaves O = acc / l unchanged and skips most accumulator rescales.
