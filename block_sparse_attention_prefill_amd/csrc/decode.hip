@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = blockIdx.x % nsplit;
   const int bg = blockIdx.x / nsplit;
-  const int b = bg / Hkv, g = bg % Hkv;
+  const int b = bg / Hkv;
   const int e0 = s * chunk;
   const int32_t* lrow = list + (size_t)bg * lstride;
   // The list count, the chunk's entries, the sequence length and the queries are
