@@ -161,6 +161,11 @@ def _stream(stream) -> Optional[int]:
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ...]) -> None:
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    # The calls launch on a stream of the current device (and the no-allocation
+    # entry point takes its scratch from the current device).
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, not on the current device "
+                         f"cuda:{torch.cuda.current_device()} (use torch.cuda.device(...))")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
