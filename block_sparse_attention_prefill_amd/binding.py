@@ -267,6 +267,18 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=device)
 
 
+def _caller_workspace(ws: torch.Tensor) -> torch.Tensor:
+    """A workspace the caller passed: device memory of the current device, one
+    contiguous block (the library checks its size and alignment itself)."""
+    if not ws.is_cuda:
+        raise ValueError("workspace must be a GPU tensor")
+    if ws.device.index != torch.cuda.current_device():
+        raise ValueError(f"workspace is on {ws.device}, not on the current device")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return ws
+
+
 def _qkv_dims(q, k, v):
     b, hq, t, d = q.shape
     hkv = k.shape[1]
@@ -289,6 +301,8 @@ def _sparse_args(q, k, v, kv_idx, kv_cnt, block, sm_scale, out, workspace):
     need = lib.seer_sparse_prefill_workspace_size(b, hq, hkv, t)
     if workspace is None:
         workspace = _workspace(need, q.device)
+    else:
+        _caller_workspace(workspace)
     scale = (1.0 / d ** 0.5) if sm_scale is None else float(sm_scale)
     return lib, (b, hq, hkv, t, d, scale), int(max_k), out, workspace
 
@@ -357,6 +371,8 @@ def seer_pooled_attn_map(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     need = lib.seer_pooled_attn_map_workspace_size(b, hq, t)
     if workspace is None:
         workspace = _workspace(need, q.device)
+    else:
+        _caller_workspace(workspace)
     scale = (1.0 / d ** 0.5) if sm_scale is None else float(sm_scale)
     _check("seer_pooled_attn_map", lib.seer_pooled_attn_map(
         _ptr(q), _ptr(k), _ptr(v), b, hq, hkv, t, d, scale, _ptr(out), _ptr(amap),
@@ -411,6 +427,8 @@ def seer_attn_gate_scores(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor, wk
     need = lib.seer_attn_gate_workspace_size(b, hq, hkv, t, dg)
     if workspace is None:
         workspace = _workspace(need, q.device)
+    else:
+        _caller_workspace(workspace)
     sc = (1.0 / dg ** 0.5) if scale is None else float(scale)
     _check("seer_attn_gate_scores", lib.seer_attn_gate_scores(
         _ptr(q), _ptr(k), b, hq, hkv, t, d, _ptr(wq), _ptr(wk), int(dg), sc, float(rope_base),
@@ -464,6 +482,8 @@ def seer_attn_gate_mask(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor, wk: 
         need = lib.seer_attn_gate_mask_workspace_size(b, hq, hkv, t, dg, int(scores is not None))
     if workspace is None:
         workspace = _workspace(need, q.device)
+    else:
+        _caller_workspace(workspace)
     sc = (1.0 / dg ** 0.5) if scale is None else float(scale)
     _check("seer_attn_gate_mask", lib.seer_attn_gate_mask(
         _ptr(q), _ptr(k), b, hq, hkv, t, d, _ptr(wq), _ptr(wk), int(dg), sc, float(rope_base),
@@ -504,6 +524,8 @@ def seer_attn_gate_decode_keys(k_cache: torch.Tensor, kv_len: torch.Tensor, wk: 
     if workspace is None and not last_block_only:
         workspace = _workspace(lib.seer_attn_gate_decode_keys_workspace_size(
             b, hkv, tmax, d, int(block)), k_cache.device)
+    elif workspace is not None:
+        _caller_workspace(workspace)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("seer_attn_gate_decode_keys", lib.seer_attn_gate_decode_keys(
         _ptr(k_cache), _ptr(kv_len), b, hkv, tmax, d, _ptr(wk), int(dg), float(rope_base),
@@ -635,6 +657,8 @@ def seer_sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
     if workspace is None:
         workspace = _workspace(sparse_decode_workspace_size(b, hq, hkv, tmax, d, lh, max_k,
                                                             int(block)), q.device)
+    else:
+        _caller_workspace(workspace)
     scale = (1.0 / d ** 0.5) if sm_scale is None else float(sm_scale)
     _check("seer_sparse_decode", lib.seer_sparse_decode(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), b, hq, hkv, tmax, d, scale,
