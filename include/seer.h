@@ -26,8 +26,11 @@
  * - Attention is causal with Tq = Tk = T: query position r sees key c iff c <= r.
  * - GQA: query head h reads KV head h / (Hq / Hkv).
  * - Every pointer argument named "device" is device memory owned by the caller.
- *   The library never allocates, frees or keeps any buffer, holds no global
- *   mutable state and may be called from several host threads at once.
+ *   The library never allocates or frees memory and may be called from several
+ *   host threads at once.  It keeps no buffer and no global mutable state,
+ *   with one exception: seer_sparse_prefill_noalloc's static scratch array and
+ *   the per-device address of it that the library caches (calls of that entry
+ *   point that overlap on one GPU race on the array).
  * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *   Every call only enqueues work on it and returns without synchronising.
  * - Errors: argument errors are detected on the host before anything is
