@@ -1015,18 +1015,10 @@ constexpr int kSchedThreads = 1024;
 constexpr int kCostBins = 1024;
 constexpr double kActiveKvBytes = 64.0 * 1024 * 1024;
 
-// Counting sort of the n candidates `keep` accepts by descending cost: the
-// candidate of rank r is handed to put(r, it), and put(r, -1) fills the ranks
-// total .. cap - 1 past the last candidate.  Called by the whole workgroup.
-template <typename Keep, typename Cost, typename Put>
-__device__ void lpt_column(int n, Keep keep, Cost cost, Put put, int cap, int* hist, int* wsum) {
+// Turns the histogram hist[kCostBins] into exclusive offsets (the first rank of
+// each bin) in place and returns the total.  Called by the whole workgroup.
+__device__ int bin_offsets(int* hist, int* wsum) {
   const int tid = threadIdx.x;
-  auto bin_of = [&](int it) { return kCostBins - 1 - min(cost(it), kCostBins - 1); };
-  hist[tid] = 0;
-  __syncthreads();
-  for (int it = tid; it < n; it += kSchedThreads)
-    if (keep(it)) atomicAdd(&hist[bin_of(it)], 1);
-  __syncthreads();
   const int lane = tid & 63, wv = tid >> 6;
   const int v = hist[tid];
   int incl = v;
@@ -1042,23 +1034,26 @@ __device__ void lpt_column(int n, Keep keep, Cost cost, Put put, int cap, int* h
     if (w < wv) before += wsum[w];
     total += wsum[w];
   }
-  hist[tid] = before + incl - v;  // exclusive offset of this bin
+  hist[tid] = before + incl - v;
   __syncthreads();
-  for (int it = tid; it < n; it += kSchedThreads)
-    if (keep(it)) put(atomicAdd(&hist[bin_of(it)], 1), it);
-  for (int r = total + tid; r < cap; r += kSchedThreads) put(r, -1);
-  __syncthreads();  // hist and wsum are reused by the next call
+  return total;
 }
+
+// Items a schedule thread holds in registers: groups of up to 8192 items are
+// sorted from one round of loads.
+constexpr int kSchedIpt = 8;
 
 // Each work entry is {item, first usable list position, its tile, list length}
 // (an int4), so that the prefill workgroup can request its first K tile, its Q
 // rows and its list window at once, with no chain of dependent loads.  An item
-// without a usable position gets position = BS * length and tile -1.
+// without a usable position gets position = BS * length and tile -1.  The
+// group's items are counting-sorted by descending cost (BS * length) in LDS.
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ idx, int Hq, int Hkv, int nqb,
     int bs, int max_k, int phases, int4* __restrict__ work) {
   __shared__ int hist[kCostBins];
   __shared__ int wsum[kSchedThreads / 64];
+  const int tid = threadIdx.x;
   const int G = Hq / Hkv;
   const int grp = blockIdx.x;
   const int ng = gridDim.x;
@@ -1068,31 +1063,62 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
   const int gp = ng / phases;                          // groups per phase
   const int ql = grp % gp;                             // the group's column in its phase
   const size_t pbase = (size_t)(grp / gp) * gp * G * nqb;  // first position of its phase
+  const int N = G * nqb;
   auto row_of = [&](int it) { return (size_t)(bh0 + it / nqb) * rows + (it % nqb) / bs; };
-  auto len_of = [&](int it) { return min(max(cnt[row_of(it)], 0), max_k); };
-  lpt_column(
-      G * nqb, [](int) { return true; }, [&](int it) { return bs * len_of(it); },
-      [&](int r, int it) {
-        int4 e = {-1, 0, -1, 0};
-        if (it >= 0) {
-          const int32_t* lst = idx + row_of(it) * (size_t)max_k;
-          const int j0 = lst[0];  // requested with the count (max_k >= 1)
-          const int n = len_of(it);
-          const int i = it % nqb, ib = i / bs;
-          int x = 0, tile = -1;
-          for (; x < bs * n; ++x) {  // first usable position (normally x = 0)
-            const int j = x < bs ? j0 : lst[x / bs];
-            const int t = bs * j + x % bs;
-            if (j >= 0 && j <= ib && t <= i) {
-              tile = t;
-              break;
-            }
-          }
-          e = {base + it, x, tile, n};
-        }
-        work[pbase + (size_t)r * gp + ql] = e;
-      },
-      G * nqb, hist, wsum);
+  auto clamp_len = [&](int c) { return min(max(c, 0), max_k); };
+  auto bin_of = [&](int n) { return kCostBins - 1 - min(bs * n, kCostBins - 1); };
+  // The entry of item `it`, whose list holds n blocks and starts with j0 (the
+  // first position is normally usable; otherwise the list is read on).
+  auto entry = [&](int it, int n, int j0) -> int4 {
+    const int32_t* lst = idx + row_of(it) * (size_t)max_k;
+    const int i = it % nqb, ib = i / bs;
+    int x = 0, tile = -1;
+    for (; x < bs * n; ++x) {
+      const int j = x < bs ? j0 : lst[x / bs];
+      const int t = bs * j + x % bs;
+      if (j >= 0 && j <= ib && t <= i) {
+        tile = t;
+        break;
+      }
+    }
+    return {base + it, x, tile, n};
+  };
+  auto put = [&](int r, int4 e) { work[pbase + (size_t)r * gp + ql] = e; };
+  hist[tid] = 0;
+  __syncthreads();
+  if (N <= kSchedIpt * kSchedThreads) {
+    // Every count and first list entry of this thread's items requested at once
+    // (indices clamped into the group, so no load sits behind a branch).
+    int len[kSchedIpt], first[kSchedIpt];
+#pragma unroll
+    for (int u = 0; u < kSchedIpt; ++u) {
+      const size_t row = row_of(min(tid + u * kSchedThreads, N - 1));
+      len[u] = cnt[row];
+      first[u] = idx[row * max_k];  // max_k >= 1
+    }
+#pragma unroll
+    for (int u = 0; u < kSchedIpt; ++u) {
+      len[u] = clamp_len(len[u]);
+      if (tid + u * kSchedThreads < N) atomicAdd(&hist[bin_of(len[u])], 1);
+    }
+    __syncthreads();
+    (void)bin_offsets(hist, wsum);
+#pragma unroll
+    for (int u = 0; u < kSchedIpt; ++u) {
+      const int it = tid + u * kSchedThreads;
+      if (it < N) put(atomicAdd(&hist[bin_of(len[u])], 1), entry(it, len[u], first[u]));
+    }
+  } else {
+    for (int it = tid; it < N; it += kSchedThreads)
+      atomicAdd(&hist[bin_of(clamp_len(cnt[row_of(it)]))], 1);
+    __syncthreads();
+    (void)bin_offsets(hist, wsum);
+    for (int it = tid; it < N; it += kSchedThreads) {
+      const size_t row = row_of(it);
+      const int n = clamp_len(cnt[row]);
+      put(atomicAdd(&hist[bin_of(n)], 1), entry(it, n, idx[row * max_k]));
+    }
+  }
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -389,7 +389,10 @@ def _schedule_phases(ng, kv_bytes, active=64 * 1024 * 1024):
                                                   (4, 2, 900, "invalid", 1),
                                                   (3, 3, 1000, "invalid", 1),
                                                   (16, 8, 40000, "sorted", 2),
-                                                  (8, 8, 140000, "invalid", 8)])
+                                                  (8, 8, 140000, "invalid", 8),
+                                                  # 9600 items in one group: the path that
+                                                  # reads the lists again per pass
+                                                  (16, 1, 38400, "invalid", 1)])
 def test_sparse_schedule_work_list(hq, hkv, t, mode, phases):
     """The work list the schedule leaves in the workspace: KV group q = b * Hkv + g
     runs in phase q / GP (GP = NG / P groups per phase), and its rank-r item sits
