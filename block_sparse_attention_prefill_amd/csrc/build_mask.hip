@@ -37,32 +37,15 @@ using rowsel::wave_sum;
 constexpr int kWavesPerGroup = 4;
 
 // NPL = key slots per lane (row length <= 64 * NPL).
+// One row by one wave, with NPL candidate slots per lane (rows of up to 64 NPL
+// candidates).
 template <int NPL>
-__global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
-    const float* __restrict__ scores, long long rows, int nqb, int nkb, int mode, float tau,
-    double density, int keep_sink, int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
-    int32_t* __restrict__ need, int max_k, const int32_t* __restrict__ kv_len, int heads,
-    int block, int k_blocks) {
-  __shared__ int hist_all[kWavesPerGroup][256];
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const long long row = (long long)blockIdx.x * kWavesPerGroup + wv;
-  if (row >= rows) return;
-  int* hist = hist_all[wv];
-  int i;  // last candidate block of the row (-1: no candidate)
-  if (kv_len) {
-    const int len = kv_len[row / heads];
-    i = len > 0 ? min((len - 1) / block, nkb - 1) : -1;
-  } else {
-    i = (int)(row % nqb);
-  }
+__device__ __forceinline__ void mask_row(const float* __restrict__ srow, int i, int lane,
+                                         int mode, float tau, double density, int keep_sink,
+                                         int max_k, bool decode, int k_blocks, int* hist,
+                                         int32_t* __restrict__ out, int32_t* __restrict__ cnt_out,
+                                         int32_t* __restrict__ need_out) {
   const int n = i + 1;
-  const float* srow = scores + row * (long long)nkb;
-  int32_t* out = idx + row * (long long)max_k;
-
-  // All of the row's loads are issued before any is used (a load under the
-  // per-candidate branch would be waited for one at a time); slots past the
-  // diagonal re-read entry i, so no entry j > i is ever read.
   float sv[NPL];
   if (n > 0) {
 #pragma unroll
@@ -90,7 +73,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
   int k;
   if (mode == 1) {
     const int forced = (i == 0) ? 1 : (keep_sink ? 2 : 1);
-    const int want = kv_len ? k_blocks : (int)ceil(density * (double)(i + 1));
+    const int want = decode ? k_blocks : (int)ceil(density * (double)(i + 1));
     k = min(i + 1, max(forced, want));
   } else {
     k = min(npos, max_k);
@@ -98,11 +81,53 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
 
   const int count = wave_select_row<NPL>(key, n, k, npos, lane, hist, out, max_k);
   if (lane == 0) {
-    cnt[row] = count;
-    // The row's size before any cut to max_k: the TopK count, or every forced
-    // and passing block in threshold mode (more than max_k: the row was cut).
-    if (need) need[row] = mode == 1 ? min(k, npos) : npos;
+    *cnt_out = count;
+    if (need_out) *need_out = mode == 1 ? min(k, npos) : npos;
   }
+}
+
+// NPL = slots per lane the longest row of the launch needs; each wave takes the
+// smallest slot count that holds its own row (the selection does not depend on
+// it, so the lists are the same), so short rows skip the empty slots' work.
+template <int NPL>
+__global__ __launch_bounds__(64 * kWavesPerGroup) void build_mask_kernel(
+    const float* __restrict__ scores, long long rows, int nqb, int nkb, int mode, float tau,
+    double density, int keep_sink, int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
+    int32_t* __restrict__ need, int max_k, const int32_t* __restrict__ kv_len, int heads,
+    int block, int k_blocks) {
+  __shared__ int hist_all[kWavesPerGroup][256];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * kWavesPerGroup + wv;
+  if (row >= rows) return;
+  int* hist = hist_all[wv];
+  int i;  // last candidate block of the row (-1: no candidate)
+  if (kv_len) {
+    const int len = kv_len[row / heads];
+    i = len > 0 ? min((len - 1) / block, nkb - 1) : -1;
+  } else {
+    i = (int)(row % nqb);
+  }
+  const float* srow = scores + row * (long long)nkb;
+  int32_t* out = idx + row * (long long)max_k;
+  int32_t* need_out = need ? need + row : nullptr;
+  const bool decode = kv_len != nullptr;
+#define SEER_MASK_ROW(P)                                                                   \
+  mask_row<P>(srow, i, lane, mode, tau, density, keep_sink, max_k, decode, k_blocks, hist, \
+              out, cnt + row, need_out)
+  const int n = i + 1;
+  if (NPL > 1 && n <= 64) {
+    SEER_MASK_ROW(1);
+  } else if (NPL > 4 && n <= 256) {
+    SEER_MASK_ROW(4 < NPL ? 4 : NPL);
+  } else if (NPL > 8 && n <= 512) {
+    SEER_MASK_ROW(8 < NPL ? 8 : NPL);
+  } else if (NPL > 16 && n <= 1024) {
+    SEER_MASK_ROW(16 < NPL ? 16 : NPL);
+  } else {
+    SEER_MASK_ROW(NPL);
+  }
+#undef SEER_MASK_ROW
 }
 
 }  // namespace
