@@ -30,6 +30,14 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# Per-source additions.  The attention kernels are scheduled with LLVM's max-ILP
+# machine-scheduler strategy: same instructions, interleaved further apart (sparse
+# prefill at 32k about 1 % faster, the pooled map not slower).
+SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
+def flags_for(src: str) -> list:
+    return FLAGS + SOURCE_FLAGS.get(os.path.basename(src), [])
 
 
 def hipcc() -> str:
@@ -41,7 +49,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *flags_for(src), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")

@@ -59,7 +59,7 @@ def _run(cmd):
 
 def _compile(hipcc, src):
     # The product flags with -O3 lowered so the reports keep their frames.
-    flags = [f for f in libbuild.FLAGS if f != "-O3"] + ["-O1", "-g"]
+    flags = [f for f in libbuild.flags_for(src) if f != "-O3"] + ["-O1", "-g"]
     obj = os.path.join(OUT, os.path.basename(src) + ".o")
     _run([hipcc, *flags, *_host_only(SAN), "-x", "hip", "-c",
           os.path.join(libbuild.CSRC, src), "-o", obj])
